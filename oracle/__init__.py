@@ -1,0 +1,10 @@
+"""CPU oracle of the looped nGPT forward pass (test infrastructure only).
+
+Importable by the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg, nothing else.
+"""
+from .model import (LAST_LOOP, PER_LOOP, OracleModel, attend, bf16_round, greedy, l2_normalize,
+                    ngpt_residual, rope, self_speculative, silu)
+
+__all__ = ["LAST_LOOP", "PER_LOOP", "OracleModel", "attend", "bf16_round", "greedy", "l2_normalize",
+           "ngpt_residual", "rope", "self_speculative", "silu"]
