@@ -1,0 +1,200 @@
+/*
+ * dory.h -- C ABI of the looped normalised-GPT forward pass on MI355X (gfx950).
+ *
+ * The model: an input stack of n_in blocks runs once, a shared recurrent core
+ * of n_rec blocks runs k = 1..4 times with the loop update
+ *     s_0 = x,  u_t = N(s_{t-1} + x),  s_t = N(F(u_t)),
+ * where x is the input stack's output and N is L2 normalisation; the output
+ * stack of n_out blocks and the LM head run once on s_k (onedev.kr summary
+ * "Dory1.0-4B는 반복 횟수로 추론 연산과 정확도를 조절한다", section "어떻게 동작하나";
+ * lucasainews article "NVIDIA, 루프 구조 4B 모델 Dory1.0-4B 4가지 정밀도로 공개",
+ * section "층을 되풀이하는 구조"). Every block is an attention sublayer followed by
+ * an MLP sublayer, each applied as h <- N(h + alpha * (N(sublayer(h)) - h)).
+ * Attention layers alternate sliding-window and full attention 3:1 (physical
+ * block j is full iff j % full_every == full_every - 1).
+ *
+ * Conventions for every call:
+ *  - Pointers named *_dev are device pointers (HBM of the context's GPU);
+ *    pointers named *_host are host pointers. Nothing else is accepted.
+ *  - The caller allocates and owns all device memory: weights, the KV pool,
+ *    the workspace, inputs and outputs. The library borrows it for the life
+ *    of the context and never frees it. The library owns only host metadata.
+ *  - Work is enqueued asynchronously on the context's stream; results are
+ *    valid once the caller synchronises that stream. No call synchronises the
+ *    stream except where stated.
+ *  - Argument and state errors are detected before anything is enqueued; the
+ *    call then returns a negative status, leaves the context unchanged and
+ *    records a message readable with dory_last_error(). A failed HIP launch
+ *    returns DORY_E_HIP.
+ *  - A context is not thread-safe: use one context per host thread / stream.
+ */
+#ifndef DORY_H
+#define DORY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DORY_OK = 0,
+  DORY_E_INVALID = -1, /* bad argument */
+  DORY_E_STATE = -2,   /* call not allowed in the current state */
+  DORY_E_NOMEM = -3,   /* KV pool, workspace or sequence table exhausted */
+  DORY_E_HIP = -4      /* HIP runtime error */
+} dory_status;
+
+/* KV cache modes (trawling.dev digest "NVIDIA, 반복 연산형 4B 언어 모델 Dory 공개",
+ * section "KV 캐시와 실행 환경"; onedev.kr summary, section "전제와 한계"):
+ *  per-loop : every recurrent block keeps one cache per loop, so the cache
+ *             holds n_in + n_out + k*n_rec layer slots;
+ *  last-loop: every loop overwrites the recurrent block's single cache, so the
+ *             cache holds n_in + n_rec + n_out slots for any k, and a query of
+ *             an earlier loop reads keys/values the final loop wrote. */
+typedef enum { DORY_KV_PER_LOOP = 0, DORY_KV_LAST_LOOP = 1 } dory_kv_mode_t;
+
+typedef enum { DORY_F32 = 0, DORY_BF16 = 1 } dory_dtype_t;
+
+/* Context flag: validate and do all host bookkeeping, but never touch the GPU
+ * (no HIP call at all; device pointers may be NULL). For host-side tests. */
+#define DORY_FLAG_DRY_RUN 1u
+
+typedef struct dory_config {
+  int32_t d_model;       /* d */
+  int32_t n_heads;       /* H query heads */
+  int32_t n_kv_heads;    /* H_kv key/value heads; H % H_kv == 0 (query head h reads kv head h / (H/H_kv)) */
+  int32_t head_dim;      /* d_h; 32, 64 or 128 */
+  int32_t d_ff;          /* SwiGLU width */
+  int32_t vocab;         /* V */
+  int32_t n_in, n_rec, n_out; /* blocks in the input, recurrent and output stacks */
+  int32_t full_every;    /* 4: every 4th physical block is full attention, the rest sliding-window */
+  int32_t window;        /* W: a sliding-window query at position p sees keys p-W < j <= p */
+  int32_t dtype;         /* dory_dtype_t: storage of weights, GEMM inputs and KV; accumulation is fp32 */
+  int32_t page_size;     /* tokens per KV page; must be 16 */
+  int32_t max_seqs;      /* sequence ids are 0 .. max_seqs-1 */
+  int32_t max_model_len; /* tokens per sequence, at most 262144 */
+  int32_t max_loops;     /* 1..4; the per-loop cache is laid out for this many loops */
+  int32_t max_tokens;    /* most rows in one call: prefill chunk length or decode batch */
+  uint32_t flags;        /* DORY_FLAG_* */
+  float rope_theta;      /* 10000 */
+  float attn_scale;      /* multiplies q.k of the unit-norm query and key before the softmax */
+} dory_config;
+
+/* Device pointers to the weights, borrowed. Matrices are row-major [out, in]
+ * in the config's dtype (bf16 = raw 16-bit bfloat16). Per physical block j in
+ * 0 .. n_in+n_rec+n_out-1:
+ *   w_qkv[j]  [(H + 2*H_kv)*d_h, d]: query rows, then key rows, then value rows
+ *   w_o[j]    [d, H*d_h]
+ *   w_gu[j]   [2*d_ff, d]: gate rows 0..d_ff-1, up rows d_ff..2*d_ff-1
+ *   w_down[j] [d, d_ff]
+ *   alpha_attn[j], alpha_mlp[j]: fp32 [d], per-dimension residual step sizes
+ * embed and lm_head are [V, d]. The pointer arrays themselves are host memory
+ * and are copied by dory_create. */
+typedef struct dory_weights {
+  const void* embed;
+  const void* lm_head;
+  const void* const* w_qkv;
+  const void* const* w_o;
+  const void* const* w_gu;
+  const void* const* w_down;
+  const float* const* alpha_attn;
+  const float* const* alpha_mlp;
+} dory_weights;
+
+typedef struct dory_ctx dory_ctx;
+
+/* Counters kept by the scheduler (host side, also in dry-run mode). */
+typedef struct dory_stats {
+  int64_t calls;            /* prefill + decode calls that ran */
+  int64_t block_apps;       /* block applications, summed over rows' calls (one per block per call) */
+  int64_t sublayer_apps;    /* 2 per block application */
+  int64_t full_apps;        /* full-attention block applications */
+  int64_t swa_apps;         /* sliding-window block applications */
+  int64_t kernel_launches;  /* kernels enqueued */
+  int32_t n_slots;          /* cache layer slots of the current mode */
+  int32_t pages_total;      /* pages the KV pool holds */
+  int32_t pages_in_use;
+  int32_t live_seqs;
+} dory_stats;
+
+/* Bytes the caller must allocate. kv_tokens: KV capacity in tokens summed over
+ * all live sequences (rounded up to whole pages per sequence by the caller's
+ * choice; each sequence holds ceil(len/16) pages). The KV pool holds, per page,
+ * every layer slot of `kv_mode` laid out for cfg->max_loops loops. */
+dory_status dory_query_sizes(const dory_config* cfg, int32_t kv_mode, int64_t kv_tokens,
+                             size_t* kv_pool_bytes, size_t* workspace_bytes);
+
+/* Create a context on the current HIP device. kv_pool_dev / workspace_dev must
+ * be at least the sizes dory_query_sizes returned (256-byte aligned); the pool
+ * may be larger, then it holds more pages. stream: a hipStream_t, or NULL for
+ * the null stream. Initialises the rotary table in the workspace (enqueued). */
+dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t kv_mode,
+                        void* kv_pool_dev, size_t kv_pool_bytes, void* workspace_dev,
+                        size_t workspace_bytes, void* stream, dory_ctx** out);
+void dory_destroy(dory_ctx* ctx);
+
+/* Loop count k for the following calls: 1..cfg->max_loops (the pages allow
+ * 1..4). In per-loop mode, a live sequence whose cache lacks loops 1..k for
+ * some of its positions makes a later call on it fail with DORY_E_STATE. */
+dory_status dory_set_loops(dory_ctx* ctx, int32_t k);
+dory_status dory_get_loops(const dory_ctx* ctx, int32_t* k);
+
+/* Switch KV mode; allowed only with no live sequence (else DORY_E_STATE). The
+ * page capacity is recomputed for the new slot count. */
+dory_status dory_kv_mode(dory_ctx* ctx, int32_t mode);
+
+/* Append one chunk of n_tokens tokens (device int32 ids) to sequence seq_id,
+ * creating it if it is not live, and run the forward pass on the chunk: in
+ * every block application the chunk's keys/values are written to the block's
+ * cache slot first, then every query of the chunk attends over its masked
+ * range of that slot. Writes fp32 logits of the last `logits_rows` rows
+ * (1 <= logits_rows <= n_tokens) to logits_dev [logits_rows, V] and, if
+ * ids_dev is not NULL, their argmax (lowest id on ties) to ids_dev
+ * [logits_rows]. n_tokens <= cfg->max_tokens; len + n_tokens <= max_model_len. */
+dory_status dory_prefill(dory_ctx* ctx, int32_t seq_id, const int32_t* tokens_dev,
+                         int32_t n_tokens, int32_t logits_rows, float* logits_dev,
+                         int32_t* ids_dev);
+
+/* One decode step for n_seqs distinct live sequences: token tokens_dev[i]
+ * (device) is appended to sequence seq_ids_host[i] (host). Writes logits
+ * [n_seqs, V] to logits_dev (may be NULL: then only ids are produced, using
+ * workspace memory) and the greedy next ids [n_seqs] to next_ids_dev (may be
+ * NULL). next_ids_dev may be passed as the next call's tokens_dev. */
+dory_status dory_decode(dory_ctx* ctx, int32_t n_seqs, const int32_t* seq_ids_host,
+                        const int32_t* tokens_dev, float* logits_dev, int32_t* next_ids_dev);
+
+/* Roll a live sequence back to new_len tokens (0 <= new_len <= len); pages past
+ * the new end return to the pool. Used to drop rejected speculative tokens. */
+dory_status dory_seq_truncate(dory_ctx* ctx, int32_t seq_id, int32_t new_len);
+dory_status dory_seq_release(dory_ctx* ctx, int32_t seq_id);
+dory_status dory_seq_len(const dory_ctx* ctx, int32_t seq_id, int32_t* len);
+
+/* KV bytes held by live sequences: pages in use x slots x bytes per page slot. */
+dory_status dory_kv_bytes_in_use(const dory_ctx* ctx, size_t* bytes);
+dory_status dory_get_stats(const dory_ctx* ctx, dory_stats* out);
+
+/* Copy the final hidden states (output of the output stack, fp32 [rows, d]) of
+ * the previous prefill/decode call's last `rows` rows to dst_dev. Enqueued. */
+dory_status dory_last_hidden(dory_ctx* ctx, float* dst_dev, int32_t rows);
+
+/* Self-speculative greedy decoding on one live sequence (onedev.kr summary,
+ * section "전제와 한계"): draft `gamma` tokens with k_draft loops by decode calls,
+ * roll the cache back, verify [last, d_1..d_gamma] as one chunk with k_verify
+ * loops, keep the longest agreeing prefix plus the verifier's next token and
+ * roll back past the rest. `last_host` is the newest generated id (not yet in
+ * the cache). Produces at least n_new ids into out_ids_host (capacity
+ * n_new + gamma) and returns their count in *n_out. Synchronises the stream once
+ * per verify step (the accepted length decides the next step). */
+dory_status dory_spec_decode(dory_ctx* ctx, int32_t seq_id, int32_t last_host, int32_t n_new,
+                             int32_t gamma, int32_t k_draft, int32_t k_verify,
+                             int32_t* out_ids_host, int32_t* n_out);
+
+const char* dory_last_error(const dory_ctx* ctx);
+const char* dory_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DORY_H */

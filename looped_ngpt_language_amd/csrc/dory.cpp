@@ -1,0 +1,641 @@
+// Host runtime of the looped nGPT forward pass: the C ABI declared in dory.h,
+// argument/state validation, the paged KV manager and the k-aware scheduler.
+//
+// Scheduler (onedev.kr summary "Dory1.0-4B는 반복 횟수로 추론 연산과 정확도를 조절한다",
+// section "어떻게 동작하나"): the input stack runs once and yields x; s_0 = x; for
+// t = 1..k the recurrent core runs on u_t = N(s_{t-1} + x) and s_t = N(F(u_t));
+// the output stack and the LM head run once on s_k. The recurrent core's
+// weights are re-read on every loop.
+// KV slots (trawling.dev digest "NVIDIA, 반복 연산형 4B 언어 모델 Dory 공개", section
+// "KV 캐시와 실행 환경"; lucasainews article, section "층을 되풀이하는 구조"): input and
+// output blocks own one slot each; a recurrent block owns one slot per loop in
+// per-loop mode and one overwritten slot in last-loop mode.
+#include "../../include/dory.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kPage = 16;
+constexpr int kMaxSplits = 64;
+constexpr int kStageSlots = 4;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {  // byte offsets inside the workspace
+  size_t rope, ptab, upload, err, buf[3], y, hb, qkv, q, o, z, part_ml, part_o, logits, spec, total;
+  int max_pages;       // pages per sequence
+  int upload_ints;     // capacity of the upload area in int32
+  int part_rows;       // rows that may use split attention
+  int logit_rows;      // rows of the logits scratch
+};
+
+int qkv_cols(const dory_config& c) { return (c.n_heads + 2 * c.n_kv_heads) * c.head_dim; }
+size_t esize(const dory_config& c) { return c.dtype == DORY_F32 ? 4 : 2; }
+
+Layout make_layout(const dory_config& c) {
+  Layout L{};
+  const size_t M = c.max_tokens, d = c.d_model, es = esize(c);
+  L.max_pages = (c.max_model_len + kPage - 1) / kPage;
+  const int upd_max = c.max_tokens / kPage + 2 + c.max_seqs;
+  L.upload_ints = 2 * c.max_tokens + 2 * upd_max + 16;
+  L.part_rows = std::min(c.max_tokens, std::max(c.max_seqs, 16));
+  L.logit_rows = std::max(c.max_seqs, 8);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L.rope = take((size_t)c.max_model_len * (c.head_dim / 2) * sizeof(float2));
+  L.ptab = take((size_t)c.max_seqs * L.max_pages * 4);
+  L.upload = take((size_t)L.upload_ints * 4);
+  L.err = take(kAlign);
+  for (int i = 0; i < 3; ++i) L.buf[i] = take(M * d * 4);
+  L.y = take(M * d * 4);
+  L.hb = take(M * d * es);
+  L.qkv = take(M * qkv_cols(c) * 4);
+  L.q = take(M * (size_t)c.n_heads * c.head_dim * es);
+  L.o = take(M * (size_t)c.n_heads * c.head_dim * es);
+  L.z = take(M * (size_t)c.d_ff * es);
+  L.part_ml = take((size_t)L.part_rows * c.n_heads * kMaxSplits * 2 * 4);
+  L.part_o = take((size_t)L.part_rows * c.n_heads * kMaxSplits * c.head_dim * 4);
+  L.logits = take((size_t)L.logit_rows * c.vocab * 4);
+  L.spec = take(64 * 4);
+  L.total = off;
+  return L;
+}
+
+int n_slots_for(const dory_config& c, int mode) {
+  return mode == DORY_KV_PER_LOOP ? c.n_in + c.n_out + c.n_rec * c.max_loops : c.n_in + c.n_rec + c.n_out;
+}
+size_t page_elems(const dory_config& c) { return (size_t)2 * c.n_kv_heads * kPage * c.head_dim; }
+
+std::string check_config(const dory_config* c) {
+  if (!c) return "config is NULL";
+  if (c->d_model <= 0 || c->d_model > 4096) return "d_model must be in 1..4096";
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 32, 64 or 128";
+  if (c->n_heads <= 0 || c->n_kv_heads <= 0 || c->n_heads % c->n_kv_heads) return "n_heads must be a multiple of n_kv_heads";
+  if (c->n_heads / c->n_kv_heads > 8) return "at most 8 query heads per KV head";
+  if (c->d_ff <= 0 || c->vocab <= 0) return "d_ff and vocab must be positive";
+  if (c->n_in < 0 || c->n_out < 0 || c->n_rec < 1) return "stack sizes: n_in, n_out >= 0 and n_rec >= 1";
+  if (c->full_every < 1 || c->window < 1) return "full_every and window must be >= 1";
+  if (c->dtype != DORY_F32 && c->dtype != DORY_BF16) return "dtype must be DORY_F32 or DORY_BF16";
+  if (c->page_size != kPage) return "page_size must be 16";
+  if (c->max_seqs < 1 || c->max_tokens < 1) return "max_seqs and max_tokens must be >= 1";
+  if (c->max_model_len < 1 || c->max_model_len > 262144) return "max_model_len must be in 1..262144";
+  if (c->max_loops < 1 || c->max_loops > 4) return "max_loops must be in 1..4";
+  if (c->dtype == DORY_BF16) {
+    const int hd = c->n_heads * c->head_dim;
+    if (c->d_model % 64 || c->d_ff % 64 || hd % 64) return "bf16 model: d_model, d_ff and n_heads*head_dim must be multiples of 64";
+  }
+  if (!(c->rope_theta > 0.f) || !(c->attn_scale > 0.f)) return "rope_theta and attn_scale must be positive";
+  return "";
+}
+
+struct Seq {
+  bool live = false;
+  int len = 0;
+  std::vector<int32_t> pages;
+  std::vector<std::pair<int, int>> runs;  // (end position, loops whose KV is valid) -- per-loop mode
+  int min_loops() const {
+    int m = 4;
+    for (auto& r : runs) m = std::min(m, r.second);
+    return m;
+  }
+  void append_run(int end, int k) {
+    if (!runs.empty() && runs.back().second == k) runs.back().first = end;
+    else runs.emplace_back(end, k);
+  }
+  void trim_runs(int new_len) {
+    while (!runs.empty()) {
+      const int start = runs.size() > 1 ? runs[runs.size() - 2].first : 0;
+      if (start >= new_len) runs.pop_back();
+      else { runs.back().first = std::min(runs.back().first, new_len); break; }
+    }
+  }
+};
+
+}  // namespace
+
+struct dory_ctx {
+  dory_config cfg{};
+  Layout L{};
+  int kv_mode = DORY_KV_PER_LOOP;
+  int k = 1;
+  bool dry = false;
+  hipStream_t stream = nullptr;
+  int n_blocks = 0, n_slots = 0, pages_total = 0;
+  size_t page_el = 0, page_bytes = 0;
+  char* pool = nullptr;
+  size_t pool_bytes = 0;
+  char* ws = nullptr;
+  // weights
+  const void* embed = nullptr;
+  const void* lm = nullptr;
+  std::vector<const void*> wqkv, wo, wgu, wd;
+  std::vector<const float*> aa, am;
+  // KV manager
+  std::vector<int32_t> free_pages;
+  std::vector<Seq> seqs;
+  // host staging (pinned) for the per-call upload
+  char* stage[kStageSlots] = {};
+  hipEvent_t stage_ev[kStageSlots] = {};
+  bool stage_used[kStageSlots] = {};
+  int stage_cur = 0;
+  size_t stage_bytes = 0;
+  std::vector<int32_t> upl;  // host image of the upload
+  // last call
+  int last_rows = 0;
+  float* last_h = nullptr;
+  dory_stats stats{};
+  std::string err;
+  hipError_t herr = hipSuccess;
+
+  template <typename P = char>
+  P* W(size_t off) const { return reinterpret_cast<P*>(ws + off); }
+};
+
+namespace {
+
+dory_status fail(dory_ctx* c, dory_status s, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+  }
+  return s;
+}
+
+// Record a launch; remember the first HIP error.
+bool ok(dory_ctx* c, hipError_t e) {
+  c->stats.kernel_launches++;
+  if (e != hipSuccess && c->herr == hipSuccess) c->herr = e;
+  return e == hipSuccess;
+}
+
+bool is_full(const dory_ctx* c, int j) { return j % c->cfg.full_every == c->cfg.full_every - 1; }
+
+int slot_of(const dory_ctx* c, int j, int t) {
+  const dory_config& g = c->cfg;
+  if (j < g.n_in) return j;
+  if (j < g.n_in + g.n_rec) {
+    if (c->kv_mode == DORY_KV_PER_LOOP) return g.n_in + (t - 1) * g.n_rec + (j - g.n_in);
+    return j;
+  }
+  if (c->kv_mode == DORY_KV_PER_LOOP) return g.n_in + g.max_loops * g.n_rec + (j - g.n_in - g.n_rec);
+  return j;
+}
+
+void recompute_capacity(dory_ctx* c) {
+  c->n_slots = n_slots_for(c->cfg, c->kv_mode);
+  c->page_el = page_elems(c->cfg);
+  c->page_bytes = c->page_el * esize(c->cfg);
+  const size_t per_page = (size_t)c->n_slots * c->page_bytes;
+  const size_t pages = per_page ? c->pool_bytes / per_page : 0;
+  c->pages_total = (int)std::min<size_t>(pages, (size_t)INT32_MAX);
+  c->free_pages.clear();
+  for (int p = c->pages_total - 1; p >= 0; --p) c->free_pages.push_back(p);
+}
+
+// Copy the host upload image to the device upload area (pinned ring, async).
+bool stage_upload(dory_ctx* c, int n_ints) {
+  if (c->dry || n_ints == 0) return true;
+  const size_t bytes = (size_t)n_ints * 4;
+  const int s = c->stage_cur;
+  c->stage_cur = (c->stage_cur + 1) % kStageSlots;
+  if (c->stage_used[s]) {
+    hipError_t e = hipEventSynchronize(c->stage_ev[s]);
+    if (e != hipSuccess) { c->herr = e; return false; }
+  }
+  memcpy(c->stage[s], c->upl.data(), bytes);
+  hipError_t e = hipMemcpyAsync(c->W(c->L.upload), c->stage[s], bytes, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipEventRecord(c->stage_ev[s], c->stream);
+  c->stage_used[s] = true;
+  if (e != hipSuccess) { c->herr = e; return false; }
+  return true;
+}
+
+int choose_splits(const dory_ctx* c, int M, int max_ctx) {
+  if (M > c->L.part_rows) return 1;
+  const int by_work = (1024 + M * c->cfg.n_kv_heads - 1) / (M * c->cfg.n_kv_heads);
+  const int by_keys = (max_ctx + 63) / 64;
+  return std::max(1, std::min(std::min(by_work, by_keys), kMaxSplits));
+}
+
+// One block application on M rows held in h / hb.
+void run_block(dory_ctx* c, int j, int t, int M, float* h, int splits) {
+  using namespace dory;
+  const dory_config& g = c->cfg;
+  const int dt = g.dtype, d = g.d_model, H = g.n_heads, Hk = g.n_kv_heads, dh = g.head_dim;
+  c->stats.block_apps++;
+  c->stats.sublayer_apps += 2;
+  if (is_full(c, j)) c->stats.full_apps++; else c->stats.swa_apps++;
+  if (c->dry) { c->stats.kernel_launches += 7 + (splits > 1); return; }
+  void* hb = c->W(c->L.hb);
+  float* qkv = c->W<float>(c->L.qkv);
+  float* y = c->W<float>(c->L.y);
+  const int32_t* rows = c->W<int32_t>(c->L.upload);
+  const int32_t* ptab = c->W<int32_t>(c->L.ptab);
+  char* kv = c->pool + (size_t)slot_of(c, j, t) * c->pages_total * c->page_bytes;
+  hipStream_t st = c->stream;
+  ok(c, launch_gemm(dt, false, hb, c->wqkv[j], qkv, M, qkv_cols(g), d, st));
+  ok(c, launch_rope_qk_kv(dt, qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), c->W(c->L.q), kv, M, H, Hk,
+                          dh, c->page_el, st));
+  c->stats.kernel_launches += (splits > 1);
+  ok(c, launch_attn_rows(dt, c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, dh,
+                         is_full(c, j) ? 0 : g.window, g.attn_scale, splits, c->W(c->L.o), c->W<float>(c->L.part_ml),
+                         c->W<float>(c->L.part_o), st));
+  ok(c, launch_gemm(dt, false, c->W(c->L.o), c->wo[j], y, M, d, H * dh, st));
+  ok(c, launch_residual(dt, h, y, c->aa[j], hb, M, d, st));
+  ok(c, launch_gemm(dt, true, hb, c->wgu[j], c->W(c->L.z), M, 2 * g.d_ff, d, st));
+  ok(c, launch_gemm(dt, false, c->W(c->L.z), c->wd[j], y, M, d, g.d_ff, st));
+  ok(c, launch_residual(dt, h, y, c->am[j], hb, M, d, st));
+}
+
+// Whole forward pass over M rows whose (seq, pos) pairs are in the upload area.
+// Leaves the final hidden rows in c->last_h and their storage copy in hb.
+void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, int max_ctx) {
+  using namespace dory;
+  const dory_config& g = c->cfg;
+  const int dt = g.dtype, d = g.d_model;
+  float* b[3] = {c->W<float>(c->L.buf[0]), c->W<float>(c->L.buf[1]), c->W<float>(c->L.buf[2])};
+  void* hb = c->W(c->L.hb);
+  const int splits = choose_splits(c, M, max_ctx);
+  if (!c->dry) ok(c, launch_embed(dt, tokens_dev, c->embed, g.vocab, d, M, b[0], hb, c->W<int32_t>(c->L.err), c->stream));
+  else c->stats.kernel_launches++;
+  for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, b[0], splits);
+  float *x = b[0], *h = b[1], *s = b[2];
+  for (int t = 1; t <= c->k; ++t) {
+    // u_t = N(s_{t-1} + x), with s_0 = x
+    if (!c->dry) ok(c, launch_norm_sum(dt, t == 1 ? x : s, x, h, nullptr, hb, M, d, c->stream));
+    else c->stats.kernel_launches++;
+    for (int j = g.n_in; j < g.n_in + g.n_rec; ++j) run_block(c, j, t, M, h, splits);
+    // s_t = N(F(u_t)); h continues as s_t
+    if (!c->dry) ok(c, launch_norm_sum(dt, h, nullptr, h, s, hb, M, d, c->stream));
+    else c->stats.kernel_launches++;
+  }
+  for (int j = g.n_in + g.n_rec; j < c->n_blocks; ++j) run_block(c, j, 1, M, h, splits);
+  c->last_h = h;
+  c->last_rows = M;
+}
+
+void lm_head(dory_ctx* c, int M, int rows, float* logits, int32_t* ids) {
+  using namespace dory;
+  const dory_config& g = c->cfg;
+  if (c->dry) { c->stats.kernel_launches += 1 + (ids != nullptr); return; }
+  const char* hb = c->W(c->L.hb) + (size_t)(M - rows) * g.d_model * esize(g);
+  ok(c, launch_gemm(g.dtype, false, hb, c->lm, logits, rows, g.vocab, g.d_model, c->stream));
+  if (ids) ok(c, launch_argmax(logits, rows, g.vocab, ids, c->stream));
+}
+
+bool valid_seq(const dory_ctx* c, int32_t id) { return id >= 0 && id < c->cfg.max_seqs; }
+
+// Give seq the pages for positions [len, new_len) (the caller checked the free
+// count) and append the page-table updates to the upload image.
+void take_pages(dory_ctx* c, int sid, int new_len) {
+  Seq& s = c->seqs[sid];
+  const int want = (new_len + kPage - 1) / kPage;
+  while ((int)s.pages.size() < want) {
+    const int p = c->free_pages.back();
+    c->free_pages.pop_back();
+    c->upl.push_back(sid * c->L.max_pages + (int)s.pages.size());
+    c->upl.push_back(p);
+    s.pages.push_back(p);
+  }
+}
+
+void release_pages_from(dory_ctx* c, Seq& s, int new_len) {
+  const int keep = (new_len + kPage - 1) / kPage;
+  while ((int)s.pages.size() > keep) {
+    c->free_pages.push_back(s.pages.back());
+    s.pages.pop_back();
+  }
+}
+
+int pages_in_use(const dory_ctx* c) { return c->pages_total - (int)c->free_pages.size(); }
+
+}  // namespace
+
+// ===================================================================== C ABI
+
+extern "C" {
+
+const char* dory_status_string(int32_t s) {
+  switch (s) {
+    case DORY_OK: return "ok";
+    case DORY_E_INVALID: return "invalid argument";
+    case DORY_E_STATE: return "invalid state";
+    case DORY_E_NOMEM: return "out of memory";
+    case DORY_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* dory_last_error(const dory_ctx* c) { return c ? c->err.c_str() : "context is NULL"; }
+
+dory_status dory_query_sizes(const dory_config* cfg, int32_t kv_mode, int64_t kv_tokens, size_t* kv_pool_bytes,
+                             size_t* workspace_bytes) {
+  if (!check_config(cfg).empty()) return DORY_E_INVALID;
+  if (kv_mode != DORY_KV_PER_LOOP && kv_mode != DORY_KV_LAST_LOOP) return DORY_E_INVALID;
+  if (kv_tokens < 0 || !kv_pool_bytes || !workspace_bytes) return DORY_E_INVALID;
+  const size_t pages = (size_t)((kv_tokens + kPage - 1) / kPage);
+  *kv_pool_bytes = pages * n_slots_for(*cfg, kv_mode) * page_elems(*cfg) * esize(*cfg);
+  *workspace_bytes = make_layout(*cfg).total;
+  return DORY_OK;
+}
+
+dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t kv_mode, void* kv_pool,
+                        size_t kv_bytes, void* workspace, size_t ws_bytes, void* stream, dory_ctx** out) {
+  if (!out) return DORY_E_INVALID;
+  *out = nullptr;
+  if (!check_config(cfg).empty()) return DORY_E_INVALID;
+  if (kv_mode != DORY_KV_PER_LOOP && kv_mode != DORY_KV_LAST_LOOP) return DORY_E_INVALID;
+  const bool dry = (cfg->flags & DORY_FLAG_DRY_RUN) != 0;
+  const Layout L = make_layout(*cfg);
+  if (!dry) {
+    if (!w || !kv_pool || !workspace) return DORY_E_INVALID;
+    if (ws_bytes < L.total) return DORY_E_NOMEM;
+    if ((reinterpret_cast<uintptr_t>(kv_pool) | reinterpret_cast<uintptr_t>(workspace)) % kAlign) return DORY_E_INVALID;
+  }
+  const int nb = cfg->n_in + cfg->n_rec + cfg->n_out;
+  if (!dry) {
+    if (!w->embed || !w->lm_head || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_down || !w->alpha_attn || !w->alpha_mlp)
+      return DORY_E_INVALID;
+    for (int j = 0; j < nb; ++j)
+      if (!w->w_qkv[j] || !w->w_o[j] || !w->w_gu[j] || !w->w_down[j] || !w->alpha_attn[j] || !w->alpha_mlp[j])
+        return DORY_E_INVALID;
+  }
+  dory_ctx* c = new dory_ctx();
+  c->cfg = *cfg;
+  c->L = L;
+  c->dry = dry;
+  c->kv_mode = kv_mode;
+  c->n_blocks = nb;
+  c->pool = static_cast<char*>(kv_pool);
+  c->pool_bytes = kv_bytes;
+  c->ws = static_cast<char*>(workspace);
+  c->stream = static_cast<hipStream_t>(stream);
+  c->seqs.resize(cfg->max_seqs);
+  if (w) {
+    c->embed = w->embed;
+    c->lm = w->lm_head;
+    for (int j = 0; j < nb && w->w_qkv; ++j) {
+      c->wqkv.push_back(w->w_qkv[j]);
+      c->wo.push_back(w->w_o[j]);
+      c->wgu.push_back(w->w_gu[j]);
+      c->wd.push_back(w->w_down[j]);
+      c->aa.push_back(w->alpha_attn[j]);
+      c->am.push_back(w->alpha_mlp[j]);
+    }
+  }
+  recompute_capacity(c);
+  c->upl.reserve(L.upload_ints);
+  if (!dry) {
+    c->stage_bytes = (size_t)L.upload_ints * 4;
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < kStageSlots && e == hipSuccess; ++i) {
+      e = hipHostMalloc(reinterpret_cast<void**>(&c->stage[i]), c->stage_bytes, hipHostMallocDefault);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&c->stage_ev[i], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = dory::launch_rope_table(c->W<float2>(L.rope), cfg->max_model_len, cfg->head_dim,
+                                                      (double)cfg->rope_theta, c->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(c->W(L.ptab), 0, (size_t)cfg->max_seqs * L.max_pages * 4, c->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(c->W(L.err), 0, 4, c->stream);
+    if (e != hipSuccess) {
+      dory_destroy(c);
+      return DORY_E_HIP;
+    }
+  }
+  *out = c;
+  return DORY_OK;
+}
+
+void dory_destroy(dory_ctx* c) {
+  if (!c) return;
+  if (!c->dry) {
+    (void)hipStreamSynchronize(c->stream);
+    for (int i = 0; i < kStageSlots; ++i) {
+      if (c->stage[i]) (void)hipHostFree(c->stage[i]);
+      if (c->stage_ev[i]) (void)hipEventDestroy(c->stage_ev[i]);
+    }
+  }
+  delete c;
+}
+
+dory_status dory_set_loops(dory_ctx* c, int32_t k) {
+  if (!c) return DORY_E_INVALID;
+  if (k < 1 || k > c->cfg.max_loops) return fail(c, DORY_E_INVALID, "loop count %d outside 1..%d", k, c->cfg.max_loops);
+  c->k = k;
+  return DORY_OK;
+}
+
+dory_status dory_get_loops(const dory_ctx* c, int32_t* k) {
+  if (!c || !k) return DORY_E_INVALID;
+  *k = c->k;
+  return DORY_OK;
+}
+
+dory_status dory_kv_mode(dory_ctx* c, int32_t mode) {
+  if (!c) return DORY_E_INVALID;
+  if (mode != DORY_KV_PER_LOOP && mode != DORY_KV_LAST_LOOP) return fail(c, DORY_E_INVALID, "unknown KV mode %d", mode);
+  if (mode == c->kv_mode) return DORY_OK;
+  for (auto& s : c->seqs)
+    if (s.live) return fail(c, DORY_E_STATE, "KV mode can only change with no live sequence");
+  c->kv_mode = mode;
+  recompute_capacity(c);
+  return DORY_OK;
+}
+
+dory_status dory_prefill(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, int32_t n, int32_t logits_rows,
+                         float* logits_dev, int32_t* ids_dev) {
+  if (!c) return DORY_E_INVALID;
+  if (!valid_seq(c, sid)) return fail(c, DORY_E_INVALID, "seq_id %d outside 0..%d", sid, c->cfg.max_seqs - 1);
+  if (n < 1 || n > c->cfg.max_tokens) return fail(c, DORY_E_INVALID, "n_tokens %d outside 1..%d", n, c->cfg.max_tokens);
+  if (logits_rows < 1 || logits_rows > n) return fail(c, DORY_E_INVALID, "logits_rows %d outside 1..%d", logits_rows, n);
+  if (!c->dry && (!tokens_dev || !logits_dev)) return fail(c, DORY_E_INVALID, "tokens_dev and logits_dev are required");
+  Seq& s = c->seqs[sid];
+  const int len = s.live ? s.len : 0;
+  if ((int64_t)len + n > c->cfg.max_model_len)
+    return fail(c, DORY_E_INVALID, "length %d + %d exceeds max_model_len %d", len, n, c->cfg.max_model_len);
+  if (c->kv_mode == DORY_KV_PER_LOOP && s.live && len > 0 && s.min_loops() < c->k)
+    return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), c->k);
+  const int need = (len + n + kPage - 1) / kPage - (int)(s.live ? s.pages.size() : 0);
+  if (need > (int)c->free_pages.size())
+    return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
+  // commit host state and build the upload: rows, then page-table updates
+  if (!s.live) { s = Seq(); s.live = true; }
+  c->upl.clear();
+  for (int i = 0; i < n; ++i) { c->upl.push_back(sid); c->upl.push_back(len + i); }
+  const size_t n_rows_ints = c->upl.size();
+  take_pages(c, sid, len + n);
+  const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
+  c->herr = hipSuccess;
+  if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
+  if (!c->dry) ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints,
+                                                n_upd, c->stream));
+  s.len = len + n;
+  s.append_run(s.len, c->k);
+  run_forward(c, tokens_dev, n, std::min(len + n, c->cfg.max_model_len));
+  lm_head(c, n, logits_rows, logits_dev, ids_dev);
+  c->stats.calls++;
+  if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
+  return DORY_OK;
+}
+
+dory_status dory_decode(dory_ctx* c, int32_t n, const int32_t* seq_ids, const int32_t* tokens_dev, float* logits_dev,
+                        int32_t* next_ids_dev) {
+  if (!c) return DORY_E_INVALID;
+  if (n < 1 || n > c->cfg.max_tokens || n > c->cfg.max_seqs)
+    return fail(c, DORY_E_INVALID, "n_seqs %d outside 1..%d", n, std::min(c->cfg.max_tokens, c->cfg.max_seqs));
+  if (!seq_ids) return fail(c, DORY_E_INVALID, "seq_ids_host is NULL");
+  if (!c->dry && !tokens_dev) return fail(c, DORY_E_INVALID, "tokens_dev is NULL");
+  if (!logits_dev && n > c->L.logit_rows) return fail(c, DORY_E_INVALID, "logits scratch holds %d rows", c->L.logit_rows);
+  int need = 0, max_ctx = 0;
+  for (int i = 0; i < n; ++i) {
+    const int sid = seq_ids[i];
+    if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
+    for (int j = 0; j < i; ++j)
+      if (seq_ids[j] == sid) return fail(c, DORY_E_INVALID, "seq %d listed twice", sid);
+    const Seq& s = c->seqs[sid];
+    if (s.len + 1 > c->cfg.max_model_len) return fail(c, DORY_E_INVALID, "seq %d reached max_model_len", sid);
+    if (c->kv_mode == DORY_KV_PER_LOOP && s.len > 0 && s.min_loops() < c->k)
+      return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), c->k);
+    need += (s.len + 1 + kPage - 1) / kPage - (int)s.pages.size();
+    max_ctx = std::max(max_ctx, s.len + 1);
+  }
+  if (need > (int)c->free_pages.size())
+    return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
+  c->upl.clear();
+  for (int i = 0; i < n; ++i) { c->upl.push_back(seq_ids[i]); c->upl.push_back(c->seqs[seq_ids[i]].len); }
+  const size_t n_rows_ints = c->upl.size();
+  for (int i = 0; i < n; ++i) take_pages(c, seq_ids[i], c->seqs[seq_ids[i]].len + 1);
+  const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
+  c->herr = hipSuccess;
+  if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
+  if (!c->dry && n_upd)
+    ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
+                                     c->stream));
+  for (int i = 0; i < n; ++i) {
+    Seq& s = c->seqs[seq_ids[i]];
+    s.len += 1;
+    s.append_run(s.len, c->k);
+  }
+  run_forward(c, tokens_dev, n, max_ctx);
+  float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
+  lm_head(c, n, n, logits, next_ids_dev);
+  c->stats.calls++;
+  if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
+  return DORY_OK;
+}
+
+dory_status dory_seq_truncate(dory_ctx* c, int32_t sid, int32_t new_len) {
+  if (!c) return DORY_E_INVALID;
+  if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
+  Seq& s = c->seqs[sid];
+  if (new_len < 0 || new_len > s.len) return fail(c, DORY_E_INVALID, "truncate to %d outside 0..%d", new_len, s.len);
+  release_pages_from(c, s, new_len);
+  s.trim_runs(new_len);
+  s.len = new_len;
+  return DORY_OK;
+}
+
+dory_status dory_seq_release(dory_ctx* c, int32_t sid) {
+  if (!c) return DORY_E_INVALID;
+  if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
+  Seq& s = c->seqs[sid];
+  release_pages_from(c, s, 0);
+  s = Seq();
+  return DORY_OK;
+}
+
+dory_status dory_seq_len(const dory_ctx* c, int32_t sid, int32_t* len) {
+  if (!c || !len || !valid_seq(c, sid)) return DORY_E_INVALID;
+  *len = c->seqs[sid].live ? c->seqs[sid].len : -1;
+  return DORY_OK;
+}
+
+dory_status dory_kv_bytes_in_use(const dory_ctx* c, size_t* bytes) {
+  if (!c || !bytes) return DORY_E_INVALID;
+  *bytes = (size_t)pages_in_use(c) * c->n_slots * c->page_bytes;
+  return DORY_OK;
+}
+
+dory_status dory_get_stats(const dory_ctx* c, dory_stats* out) {
+  if (!c || !out) return DORY_E_INVALID;
+  *out = c->stats;
+  out->n_slots = c->n_slots;
+  out->pages_total = c->pages_total;
+  out->pages_in_use = pages_in_use(c);
+  int live = 0;
+  for (auto& s : c->seqs) live += s.live;
+  out->live_seqs = live;
+  return DORY_OK;
+}
+
+dory_status dory_last_hidden(dory_ctx* c, float* dst, int32_t rows) {
+  if (!c || !dst) return DORY_E_INVALID;
+  if (rows < 1 || rows > c->last_rows) return fail(c, DORY_E_INVALID, "rows %d outside 1..%d", rows, c->last_rows);
+  if (c->dry) return DORY_OK;
+  const size_t d = c->cfg.d_model;
+  hipError_t e = hipMemcpyAsync(dst, c->last_h + (size_t)(c->last_rows - rows) * d, (size_t)rows * d * 4,
+                                hipMemcpyDeviceToDevice, c->stream);
+  return e == hipSuccess ? DORY_OK : fail(c, DORY_E_HIP, "%s", hipGetErrorString(e));
+}
+
+dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_new, int32_t gamma, int32_t k_draft,
+                             int32_t k_verify, int32_t* out_ids, int32_t* n_out) {
+  if (!c || !out_ids || !n_out) return DORY_E_INVALID;
+  if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
+  if (gamma < 1 || gamma > 16 || n_new < 1) return fail(c, DORY_E_INVALID, "gamma must be 1..16 and n_new >= 1");
+  if (k_draft < 1 || k_draft > c->cfg.max_loops || k_verify < 1 || k_verify > c->cfg.max_loops)
+    return fail(c, DORY_E_INVALID, "loop counts outside 1..%d", c->cfg.max_loops);
+  if (gamma + 1 > c->cfg.max_tokens || gamma + 1 > c->L.logit_rows)
+    return fail(c, DORY_E_INVALID, "gamma + 1 exceeds max_tokens or the logits scratch");
+  if (c->dry) return fail(c, DORY_E_STATE, "self-speculative decoding needs the GPU");
+  const int k_saved = c->k;
+  int32_t* toks = c->W<int32_t>(c->L.spec);   // [last, d1..d_gamma]
+  int32_t* vids = toks + 32;                  // verifier ids [gamma+1]
+  float* logits = c->W<float>(c->L.logits);
+  int count = 0;
+  dory_status st = DORY_OK;
+  std::vector<int32_t> host(2 * (gamma + 1));
+  while (count < n_new) {
+    const int base = c->seqs[sid].len;
+    hipError_t e = hipMemcpyAsync(toks, &last, 4, hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);  // `last` lives on this host stack frame
+    if (e != hipSuccess) { st = fail(c, DORY_E_HIP, "%s", hipGetErrorString(e)); break; }
+    c->k = k_draft;
+    for (int i = 0; i < gamma && st == DORY_OK; ++i) st = dory_decode(c, 1, &sid, toks + i, nullptr, toks + i + 1);
+    if (st != DORY_OK) break;
+    if ((st = dory_seq_truncate(c, sid, base)) != DORY_OK) break;
+    c->k = k_verify;
+    if ((st = dory_prefill(c, sid, toks, gamma + 1, gamma + 1, logits, vids)) != DORY_OK) break;
+    e = hipMemcpyAsync(host.data(), toks, (gamma + 1) * 4, hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(host.data() + gamma + 1, vids, (gamma + 1) * 4, hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) { st = fail(c, DORY_E_HIP, "%s", hipGetErrorString(e)); break; }
+    const int32_t* d = host.data() + 1;          // drafts d1..d_gamma
+    const int32_t* v = host.data() + gamma + 1;  // verifier ids after last, d1, ..., d_gamma
+    int acc = 0;
+    while (acc < gamma && d[acc] == v[acc]) ++acc;
+    for (int i = 0; i < acc; ++i) out_ids[count++] = d[i];
+    out_ids[count++] = v[acc];
+    last = v[acc];
+    if ((st = dory_seq_truncate(c, sid, base + acc + 1)) != DORY_OK) break;
+  }
+  c->k = k_saved;
+  *n_out = count;
+  return st;
+}
+
+}  // extern "C"

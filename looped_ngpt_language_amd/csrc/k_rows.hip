@@ -1,0 +1,208 @@
+// Row-wise kernels of the looped nGPT forward pass: embedding gather, the
+// normalised residual step, the loop injection and state normalisation, the
+// greedy argmax, page-table updates and the rotary table.
+//
+// Normalised residual step of every sublayer (nGPT backbone; onedev.kr summary
+// "Dory1.0-4B는 반복 횟수로 추론 연산과 정확도를 조절한다", section "어떻게 동작하나"):
+//   h <- N(h + alpha * (N(y) - h)),  N(v) = v / ||v||_2.
+// Loop update (same section): u_t = N(s_{t-1} + x), s_t = N(F(u_t)).
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+
+constexpr int ROW_THREADS = 256;
+constexpr int ROW_EPT = 16;  // elements per thread: d <= 4096
+
+// h[m] = E[tok[m]] (fp32), hb[m] = E[tok[m]] (storage type).
+template <typename T>
+__global__ void __launch_bounds__(ROW_THREADS) k_embed(const int32_t* __restrict__ tokens,
+                                                       const T* __restrict__ E, int vocab, int d,
+                                                       float* __restrict__ h, T* __restrict__ hb,
+                                                       int32_t* __restrict__ err) {
+  const int m = blockIdx.x;
+  int tok = tokens[m];
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0) atomicOr(err, 1);
+    tok = tok < 0 ? 0 : vocab - 1;
+  }
+  const T* e = E + (size_t)tok * d;
+  for (int i = threadIdx.x; i < d; i += ROW_THREADS) {
+    const float v = St<T>::ld(e, i);
+    h[(size_t)m * d + i] = v;
+    hb[(size_t)m * d + i] = e[i];
+  }
+}
+
+// h <- N(h + alpha (N(y) - h)); hb <- storage copy of h.
+template <typename T>
+__global__ void __launch_bounds__(ROW_THREADS) k_residual(float* __restrict__ h, const float* __restrict__ y,
+                                                          const float* __restrict__ alpha,
+                                                          T* __restrict__ hb, int d) {
+  __shared__ float red[ROW_THREADS / 64];
+  const size_t base = (size_t)blockIdx.x * d;
+  float yv[ROW_EPT], hv[ROW_EPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    yv[e] = i < d ? y[base + i] : 0.f;
+    hv[e] = i < d ? h[base + i] : 0.f;
+    ss += yv[e] * yv[e];
+  }
+  const float ry = rsqrtf(fmaxf(block_sum(ss, red, ROW_THREADS / 64), DORY_TINY_SS));
+  float st = 0.f;
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    const float a = i < d ? alpha[i] : 0.f;
+    hv[e] = hv[e] + a * (yv[e] * ry - hv[e]);
+    st += hv[e] * hv[e];
+  }
+  const float rh = rsqrtf(fmaxf(block_sum(st, red, ROW_THREADS / 64), DORY_TINY_SS));
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    if (i < d) {
+      const float v = hv[e] * rh;
+      h[base + i] = v;
+      St<T>::st(hb, base + i, v);
+    }
+  }
+}
+
+// out = N(a + b) written to h (fp32) and hb (storage); a and b may alias.
+// With b == nullptr: out = N(a), also written to s when s != nullptr.
+template <typename T>
+__global__ void __launch_bounds__(ROW_THREADS) k_norm_sum(const float* a, const float* b, float* h, float* s,
+                                                          T* __restrict__ hb, int d) {
+  __shared__ float red[ROW_THREADS / 64];
+  const size_t base = (size_t)blockIdx.x * d;
+  float v[ROW_EPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    v[e] = i < d ? a[base + i] + (b ? b[base + i] : 0.f) : 0.f;
+    ss += v[e] * v[e];
+  }
+  const float r = rsqrtf(fmaxf(block_sum(ss, red, ROW_THREADS / 64), DORY_TINY_SS));
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    if (i < d) {
+      const float o = v[e] * r;
+      h[base + i] = o;
+      if (s) s[base + i] = o;
+      St<T>::st(hb, base + i, o);
+    }
+  }
+}
+
+// ids[r] = argmax_j logits[r, j], lowest j on ties.
+constexpr int ARGMAX_THREADS = 1024;
+__global__ void __launch_bounds__(ARGMAX_THREADS) k_argmax(const float* __restrict__ logits, int V,
+                                                           int32_t* __restrict__ ids) {
+  __shared__ float sv[ARGMAX_THREADS / 64];
+  __shared__ int si[ARGMAX_THREADS / 64];
+  const float* row = logits + (size_t)blockIdx.x * V;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int j = threadIdx.x; j < V; j += ARGMAX_THREADS) {
+    const float v = row[j];
+    if (v > best) { best = v; bi = j; }  // j increases: first maximum kept
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) { sv[w] = best; si[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < ARGMAX_THREADS / 64; ++i)
+      if (sv[i] > best || (sv[i] == best && si[i] < bi)) { best = sv[i]; bi = si[i]; }
+    ids[blockIdx.x] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+// Page-table scatter: table[upd[2i]] = upd[2i+1].
+__global__ void k_apply_updates(int32_t* __restrict__ table, const int32_t* __restrict__ upd, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) table[upd[2 * i]] = upd[2 * i + 1];
+}
+
+// Rotary table: tab[p][i] = (cos, sin)(p * theta^(-2i/dh)), angle and cos/sin in fp64.
+__global__ void k_rope_table(float2* __restrict__ tab, int max_len, int half, int dh, double theta) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)max_len * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double inv = pow(theta, -2.0 * (double)i / (double)dh);
+  const double ang = (double)p * inv;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+__global__ void k_copy_f32(float* __restrict__ dst, const float* __restrict__ src, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <typename T>
+static hipError_t embed_t(const int32_t* tokens, const void* E, int V, int d, int M, float* h, void* hb,
+                          int32_t* err, hipStream_t st) {
+  hipLaunchKernelGGL(k_embed<T>, dim3(M), dim3(ROW_THREADS), 0, st, tokens, (const T*)E, V, d, h, (T*)hb, err);
+  return hipGetLastError();
+}
+hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int V, int d, int M, float* h, void* hb,
+                        int32_t* err, hipStream_t st) {
+  return dtype == 0 ? embed_t<float>(tokens, E, V, d, M, h, hb, err, st)
+                    : embed_t<bf16_t>(tokens, E, V, d, M, h, hb, err, st);
+}
+
+hipError_t launch_residual(int dtype, float* h, const float* y, const float* alpha, void* hb, int M, int d,
+                           hipStream_t st) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_residual<float>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (float*)hb, d);
+  else
+    hipLaunchKernelGGL(k_residual<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (bf16_t*)hb, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_sum(int dtype, const float* a, const float* b, float* h, float* s, void* hb, int M, int d,
+                           hipStream_t st) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_norm_sum<float>, dim3(M), dim3(ROW_THREADS), 0, st, a, b, h, s, (float*)hb, d);
+  else
+    hipLaunchKernelGGL(k_norm_sum<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, a, b, h, s, (bf16_t*)hb, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(ARGMAX_THREADS), 0, st, logits, V, ids);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_apply_updates, dim3((n + 255) / 256), dim3(256), 0, st, table, upd, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2* tab, int max_len, int dh, double theta, hipStream_t st) {
+  const size_t n = (size_t)max_len * (dh / 2);
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, max_len, dh / 2, dh,
+                     theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
+  return hipGetLastError();
+}
+
+}  // namespace dory

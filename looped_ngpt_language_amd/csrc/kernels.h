@@ -1,0 +1,32 @@
+// Launchers of the gfx950 kernels (device pointers, stream-ordered, no allocation).
+// dtype: 0 = fp32 model, 1 = bf16 model (storage type of weights, GEMM inputs, KV).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dory {
+
+hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int V, int d, int M, float* h, void* hb,
+                        int32_t* err, hipStream_t st);
+hipError_t launch_residual(int dtype, float* h, const float* y, const float* alpha, void* hb, int M, int d,
+                           hipStream_t st);
+hipError_t launch_norm_sum(int dtype, const float* a, const float* b, float* h, float* s, void* hb, int M, int d,
+                           hipStream_t st);
+hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, hipStream_t st);
+hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, hipStream_t st);
+hipError_t launch_rope_table(float2* tab, int max_len, int dh, double theta, hipStream_t st);
+hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t st);
+
+hipError_t launch_rope_qk_kv(int dtype, const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
+                             const float2* rope, void* q_out, void* kv_slot, int M, int H, int Hkv, int dh,
+                             size_t page_elems, hipStream_t st);
+hipError_t launch_attn_rows(int dtype, const void* q, const int32_t* rows, const int32_t* ptab, int max_pages,
+                            const void* kv, size_t page_elems, int M, int H, int Hkv, int dh, int window,
+                            float scale, int splits, void* out, float* part_ml, float* part_o, hipStream_t st);
+
+bool gemv_supported(int K);
+hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
+                       hipStream_t st);
+
+}  // namespace dory

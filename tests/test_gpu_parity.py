@@ -1,0 +1,152 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars (written in each test):
+  * fp32 model: logits and final hidden states within 1e-4 max-abs; greedy ids bit-exact
+    (free-running: the GPU feeds its own ids).
+  * bf16 model: teacher-forced on the oracle's ids; logits within 5e-2 and final hidden
+    states within 3e-2 max-abs; the GPU's argmax equals the oracle's except at steps whose
+    oracle margin between the two ids is below twice the step's max logit error (near-ties,
+    counted and reported).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from looped_ngpt_language_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from looped_ngpt_language_amd import dory  # noqa: E402
+from oracle import OracleModel, greedy  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = synth.make_weights(synth.TINY, seed=0)
+    gpu = dory.Model(synth.TINY, w, kv_mode="per_loop", max_loops=4, max_seqs=4, max_model_len=256, max_tokens=128)
+    return w, gpu
+
+
+def run_gpu_greedy(m, seq, prompt, n_steps, teacher=None):
+    """Prefill + n_steps decode steps; feeds the GPU's own ids unless teacher ids are given."""
+    lg, ids = m.prefill(seq, prompt, 1)
+    logits = [lg[0].cpu().numpy()]
+    out = [int(ids[0].item())]
+    hidden = [m.last_hidden(1)[0].cpu().numpy()]
+    for i in range(n_steps):
+        tok = out[-1] if teacher is None else int(teacher[i])
+        lg, ids = m.decode([seq], torch.tensor([tok], dtype=torch.int32, device=m.device))
+        logits.append(lg[0].cpu().numpy())
+        out.append(int(ids[0].item()))
+        hidden.append(m.last_hidden(1)[0].cpu().numpy())
+    return np.array(out, dtype=np.int32), np.array(logits), np.array(hidden)
+
+
+def oracle_greedy(shape, w, mode, k, prompt, n_steps):
+    om = OracleModel(shape, w, mode, k)
+    lg, ids = om.prefill(0, prompt, 1)
+    out, logits, hidden = [int(ids[0])], [lg[0]], [om.last_hidden[-1]]
+    for _ in range(n_steps):
+        lg, ids = om.decode([0], [out[-1]])
+        out.append(int(ids[0]))
+        logits.append(lg[0])
+        hidden.append(om.last_hidden[0])
+    return np.array(out, dtype=np.int32), np.array(logits), np.array(hidden)
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_tiny_fp32_end_to_end(tiny, mode, k):
+    w, m = tiny
+    say(f"[tiny fp32] mode={mode} k={k} prompt=64 decode=16")
+    for s in range(4):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    m.set_kv_mode(mode)
+    m.set_loops(k)
+    prompt = synth.prompt_tokens(synth.TINY, 64)
+    g_ids, g_lg, g_h = run_gpu_greedy(m, 0, prompt, 16)
+    o_ids, o_lg, o_h = oracle_greedy(synth.TINY, w, mode, k, prompt, 16)
+    err_l = np.max(np.abs(g_lg - o_lg))
+    err_h = np.max(np.abs(g_h - o_h))
+    say(f"  logits max-abs {err_l:.3e}  hidden max-abs {err_h:.3e}  ids equal {np.array_equal(g_ids, o_ids)}")
+    assert err_l <= 1e-4
+    assert err_h <= 1e-4
+    np.testing.assert_array_equal(g_ids, o_ids)
+
+
+def test_tiny_fp32_all_rows_and_chunks(tiny):
+    """Logits of every prompt row; a prompt in ragged chunks (per-loop: chunking invariant)."""
+    w, m = tiny
+    say("[tiny fp32] all-row logits, chunked per-loop prefill, k=2")
+    for s in range(4):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    m.set_kv_mode("per_loop")
+    m.set_loops(2)
+    prompt = synth.prompt_tokens(synth.TINY, 77)
+    lg, ids = m.prefill(0, prompt, 77)
+    om = OracleModel(synth.TINY, w, "per_loop", 2)
+    olg, oids = om.prefill(0, prompt, 77)
+    assert np.max(np.abs(lg.cpu().numpy() - olg)) <= 1e-4
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    outs = []
+    for a, b in ((0, 1), (1, 18), (18, 50), (50, 77)):
+        l2, _ = m.prefill(1, prompt[a:b], b - a)
+        outs.append(l2.cpu().numpy())
+    assert np.max(np.abs(np.concatenate(outs) - olg)) <= 1e-4
+
+
+@pytest.fixture(scope="module")
+def mid():
+    w = synth.make_weights(synth.MID, seed=0)
+    gpu = dory.Model(synth.MID, w, kv_mode="per_loop", max_loops=4, max_seqs=2, max_model_len=1024, max_tokens=1024)
+    return w, gpu
+
+
+def bf16_check(tag, g_ids, g_lg, g_h, o_ids, o_lg, o_h):
+    err_l = np.max(np.abs(g_lg - o_lg))
+    err_h = np.max(np.abs(g_h - o_h))
+    rel_h = np.linalg.norm(g_h - o_h) / np.linalg.norm(o_h)
+    near, wrong = 0, 0
+    for i in range(len(g_ids)):
+        if g_ids[i] == o_ids[i]:
+            continue
+        step_err = np.max(np.abs(g_lg[i] - o_lg[i]))
+        margin = o_lg[i][o_ids[i]] - o_lg[i][g_ids[i]]
+        if margin < 2 * step_err:
+            near += 1
+        else:
+            wrong += 1
+    say(f"  {tag}: logits max-abs {err_l:.3e}  hidden max-abs {err_h:.3e} rel-L2 {rel_h:.2e}  "
+        f"ids {np.sum(g_ids == o_ids)}/{len(g_ids)} equal, near-ties {near}, wrong {wrong}")
+    assert err_l <= 5e-2
+    assert err_h <= 3e-2
+    assert wrong == 0
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_mid_bf16_end_to_end(mid, mode, k):
+    w, m = mid
+    n_dec = 6
+    say(f"[mid bf16] mode={mode} k={k} prompt=512 decode={n_dec} (teacher-forced)")
+    for s in range(2):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    m.set_kv_mode(mode)
+    m.set_loops(k)
+    prompt = synth.prompt_tokens(synth.MID, 512)
+    o_ids, o_lg, o_h = oracle_greedy(synth.MID, w, mode, k, prompt, n_dec)
+    g_ids, g_lg, g_h = run_gpu_greedy(m, 0, prompt, n_dec, teacher=o_ids)
+    bf16_check(f"mid k={k} {mode}", g_ids, g_lg, g_h, o_ids, o_lg, o_h)
