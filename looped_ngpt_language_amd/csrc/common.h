@@ -14,6 +14,10 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Reinterpret two packed bfloat16 values. The argument is taken by value: a
+// bit_cast applied directly to a vector-element expression reads element 0.
+DORY_DEV bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
 DORY_DEV float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // float -> bfloat16, round to nearest even (inputs are finite).

@@ -210,7 +210,7 @@ __global__ void __launch_bounds__(256) k_gemv_bf16(const bf16_t* __restrict__ X,
       const int n = min(r0 + r, nrows_out - 1) + b * F;
       const bf16_t* wp = W + (size_t)n * K + (size_t)lane * 8;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) wr[b][r][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + c * 512));
+      for (int c = 0; c < KCH; ++c) wr[b][r][c] = *reinterpret_cast<const u32x4_t*>(wp + c * 512);
     }
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -223,10 +223,10 @@ __global__ void __launch_bounds__(256) k_gemv_bf16(const bf16_t* __restrict__ X,
         for (int c = 0; c < KCH; ++c) {
           const u32x4_t w = wr[b][r][c];
           const uint4 x = xr[m][c];
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), s, false);
         }
         acc[b][r][m] = wave_sum(s);
       }
