@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the looped nGPT forward pass on one MI355X, with roofline fractions.
+
+Workload (seeded synthetic weights and prompts, nothing downloaded): the ~4B
+looped nGPT (d=3072, 24/8 heads of 128, SwiGLU 8192, vocab 131072, 8/20/8
+blocks, 3:1 sliding-window(4096):full attention), bf16, last-loop KV cache.
+
+A step is one decode step at batch 1 (every block application of the input
+stack, k passes of the recurrent core, the output stack, LM head and argmax)
+with a 2560-token prompt already in the cache; the headline value is decode
+tok/s at k=2. The breakdown adds decode at k=1/2/4 and the 2048-token prefill at
+k=1/2/4 with their roofline fractions. The roofline entry is the dominant
+decode kernel: its algorithmic bytes per launch over its average launch time,
+from HIP events recorded around every launch on the stream the library uses
+(an instrumented pass of the same decode steps, after the timed region).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--prompt", type=int, default=2560)
+    p.add_argument("--prefill-len", type=int, default=2048)
+    p.add_argument("--k", type=int, default=2, help="loop count of the headline decode value")
+    p.add_argument("--loops", default="1,2,4")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the forward pass shards by sequence with no exchange; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from looped_ngpt_language_amd import dory, synth
+
+    loops = [int(x) for x in args.loops.split(",")]
+    shape = synth.DORY4B
+    t0 = time.time()
+    w = synth.make_weights(shape, seed=0)
+    log(f"[bench] weights drawn in {time.time() - t0:.1f}s")
+    prompt = synth.prompt_tokens(shape, max(args.prompt, args.prefill_len))
+    max_len = args.prompt + args.warmup + args.steps + 32
+    t0 = time.time()
+    m = dory.Model(shape, w, kv_mode="last_loop", max_loops=4, max_seqs=1, max_model_len=max_len,
+                   max_tokens=max(args.prompt, args.prefill_len), device="cuda:0")
+    torch.cuda.synchronize()
+    log(f"[bench] model uploaded in {time.time() - t0:.1f}s; workspace {m.ws_bytes / 2**30:.2f} GiB, "
+        f"KV pool {m.kv_bytes / 2**30:.2f} GiB")
+    st = m.stream
+    res = {"decode": {}, "prefill": {}}
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ---------------------------------------------------------------- prefill
+    if not args.no_prefill:
+        toks = torch.from_numpy(prompt[:args.prefill_len]).to("cuda:0")
+        logits = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda:0")
+        for k in loops:
+            m.set_loops(k)
+            m.prefill(0, toks, 1, logits=logits)
+            m.release(0)
+            torch.cuda.synchronize()
+            m.timing(reset=True)
+            reps = 3
+            e0, e1 = ev(), ev()
+            e0.record(st)
+            for _ in range(reps):
+                m.prefill(0, toks, 1, logits=logits)
+                m.release(0)
+            e1.record(st)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tim = m.timing(reset=True)
+            flops = sum(v["flops"] for v in tim.values()) / reps
+            tfs = flops / (ms * 1e-3) / 1e12
+            res["prefill"][k] = {"tokens": args.prefill_len, "ms": ms, "tok_s": args.prefill_len / (ms * 1e-3),
+                                 "tflop": flops / 1e12, "tflop_s": tfs, "mfma_frac": tfs / BF16_PEAK_TFLOPS}
+            log(f"[bench] prefill T={args.prefill_len} k={k}: {ms:.2f} ms  {args.prefill_len / (ms * 1e-3):,.0f} tok/s  "
+                f"{tfs:.1f} TFLOP/s ({100 * tfs / BF16_PEAK_TFLOPS:.1f}% of MFMA peak)")
+
+    # ---------------------------------------------------------------- decode
+    ptoks = torch.from_numpy(prompt[:args.prompt]).to("cuda:0")
+    ids = [torch.empty(1, dtype=torch.int32, device="cuda:0") for _ in range(2)]
+    first = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    plog = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda:0")
+    for k in loops:
+        m.set_loops(k)
+        _, pid = m.prefill(0, ptoks, 1, logits=plog)
+        first.copy_(pid)
+        cur = first
+        for i in range(args.warmup):
+            m.decode([0], cur, logits=None, out_ids=ids[i % 2])
+            cur = ids[i % 2]
+        torch.cuda.synchronize()
+        m.timing(reset=True)
+        e0, e1 = ev(), ev()
+        e0.record(st)
+        for i in range(args.steps):
+            m.decode([0], cur, logits=None, out_ids=ids[i % 2])
+            cur = ids[i % 2]
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        alg = m.timing(reset=True)
+        step_bytes = sum(v["bytes"] for v in alg.values()) / args.steps
+        # instrumented pass: same decode steps, an event pair around every launch
+        n_inst = min(args.steps, 20)
+        m.set_timing(True)
+        for i in range(n_inst):
+            m.decode([0], cur, logits=None, out_ids=ids[i % 2])
+            cur = ids[i % 2]
+        tim = m.timing(reset=True)
+        m.set_timing(False)
+        m.release(0)
+        roles = {}
+        for name, v in tim.items():
+            if v["timed_launches"]:
+                avg_ms = v["ms"] / v["timed_launches"]
+                per_launch = v["bytes"] / v["launches"]
+                roles[name] = {"launches_per_step": v["launches"] / n_inst, "avg_us": 1e3 * avg_ms,
+                               "ms_per_step": v["ms"] / n_inst, "bytes_per_launch": per_launch,
+                               "GBs": per_launch / (avg_ms * 1e-3) / 1e9}
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        res["decode"][k] = {"ms_per_step": ms, "tok_s": 1e3 / ms, "bytes_per_step": step_bytes, "GBs": gbs,
+                            "hbm_frac": gbs / HBM_PEAK_GBS, "kernels": roles}
+        log(f"[bench] decode bs1 k={k} ctx {args.prompt}: {ms:.3f} ms/step  {1e3 / ms:.1f} tok/s  "
+            f"{step_bytes / 1e9:.2f} GB/step -> {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+        for name, r in sorted(roles.items(), key=lambda x: -x[1]["ms_per_step"]):
+            log(f"         {name:22s} {r['launches_per_step']:6.1f}/step  avg {r['avg_us']:8.2f} us  "
+                f"{r['ms_per_step']:7.3f} ms/step  {r['GBs']:7.0f} GB/s")
+
+    head = res["decode"].get(args.k) or next(iter(res["decode"].values()))
+    dom_name, dom = max(head["kernels"].items(), key=lambda x: x[1]["ms_per_step"])
+    roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(dom["GBs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dom["GBs"] / HBM_PEAK_GBS, 4), "traffic": None}
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shape, w, prompt, args.k)
+
+    out = {
+        "metric": "decode tok/s (bs1, bs128) + prefill tok/s at k=1/2/4; % of HBM/MFMA roofline",
+        "value": round(head["tok_s"], 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random weights and uniform-random prompt ids)",
+        "config": {"workload": f"looped nGPT ~4B (d=3072, 8/20/8 blocks) decode, batch 1, k={args.k}, "
+                               f"last-loop KV, {args.prompt}-token prompt in cache",
+                   "global_batch": 1, "seq_len": args.prompt, "loops": args.k, "kv_mode": "last_loop"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": {
+            "decode_bs1": {str(k): {"tok_s": round(v["tok_s"], 2), "ms_per_step": round(v["ms_per_step"], 4),
+                                    "GB_per_step": round(v["bytes_per_step"] / 1e9, 3),
+                                    "hbm_frac": round(v["hbm_frac"], 4)} for k, v in res["decode"].items()},
+            "prefill": {str(k): {"tokens": v["tokens"], "tok_s": round(v["tok_s"], 1), "ms": round(v["ms"], 3),
+                                 "tflop_s": round(v["tflop_s"], 1), "mfma_frac": round(v["mfma_frac"], 4)}
+                        for k, v in res["prefill"].items()},
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(shape, w, prompt, k):
+    """The oracle as it stands, on the host cores: a 16-token prompt, then 2 timed decode steps."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import OracleModel
+    t0 = time.time()
+    om = OracleModel(shape, w, "last_loop", k)
+    om.prefill(0, prompt[:16], 1)
+    log(f"[bench] oracle ready in {time.time() - t0:.1f}s")
+    n = 2
+    tok = 1
+    t0 = time.perf_counter()
+    for _ in range(n):
+        _, ids = om.decode([0], [tok])
+        tok = int(ids[0])
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    log(f"[bench] oracle decode: {dt / n:.2f} s/token on {threads} threads")
+    return {"value": round(n / dt, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"2 decode steps at batch 1, k={k}, last-loop KV, after a 16-token prompt "
+                      f"(fp64 numpy oracle, same ~4B weights); cores = BLAS threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -191,6 +191,30 @@ dory_status dory_spec_decode(dory_ctx* ctx, int32_t seq_id, int32_t last_host, i
                              int32_t gamma, int32_t k_draft, int32_t k_verify,
                              int32_t* out_ids_host, int32_t* n_out);
 
+/* Per-kernel accounting, one entry per kernel role of the forward pass
+ * ("qkv_proj", "rope_qknorm_kvwrite", "attention", "o_proj", "ngpt_residual",
+ * "gate_up_swiglu", "down_proj", "loop_norm", "embed", "lm_head", "argmax",
+ * "page_table"). bytes and flops are the algorithmic HBM bytes and flops the
+ * launches must move or compute (weights, activations, the keys/values in each
+ * row's attention range), counted for every launch. timed_launches / total_ms
+ * come from a HIP event pair recorded around each launch while timing is
+ * enabled (dory_set_timing). */
+typedef struct dory_kernel_time {
+  char name[32];
+  int64_t launches;
+  double bytes;
+  double flops;
+  int64_t timed_launches;
+  double total_ms;
+} dory_kernel_time;
+
+/* Enable (1) or disable (0) the event pair around every launch. */
+dory_status dory_set_timing(dory_ctx* ctx, int32_t enable);
+/* Copy up to max entries (roles that launched at least once) to out and their
+ * count to *n; synchronises the stream when timed events are pending. With
+ * reset != 0 the counters restart from zero afterwards. */
+dory_status dory_get_timing(dory_ctx* ctx, dory_kernel_time* out, int32_t max, int32_t* n, int32_t reset);
+
 const char* dory_last_error(const dory_ctx* ctx);
 const char* dory_status_string(int32_t status);
 

@@ -122,6 +122,21 @@ struct Seq {
   }
 };
 
+enum Role { R_EMBED, R_QKV, R_ROPE, R_ATTN, R_OPROJ, R_RESID, R_GU, R_DOWN, R_LOOPN, R_LM, R_ARGMAX, R_PTAB, R_COUNT };
+const char* const kRoleName[R_COUNT] = {"embed", "qkv_proj", "rope_qknorm_kvwrite", "attention", "o_proj",
+                                        "ngpt_residual", "gate_up_swiglu", "down_proj", "loop_norm", "lm_head",
+                                        "argmax", "page_table"};
+
+struct RoleAcc {
+  int64_t launches = 0, timed = 0;
+  double bytes = 0, flops = 0, ms = 0;
+};
+
+struct TimedRec {
+  int role;
+  hipEvent_t a, b;
+};
+
 }  // namespace
 
 struct dory_ctx {
@@ -155,6 +170,12 @@ struct dory_ctx {
   int last_rows = 0;
   float* last_h = nullptr;
   dory_stats stats{};
+  // per-role accounting and optional event timing
+  RoleAcc acc[R_COUNT];
+  bool timing = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<TimedRec> recs;
   std::string err;
   hipError_t herr = hipSuccess;
 
@@ -182,6 +203,39 @@ bool ok(dory_ctx* c, hipError_t e) {
   if (e != hipSuccess && c->herr == hipSuccess) c->herr = e;
   return e == hipSuccess;
 }
+
+hipEvent_t next_event(dory_ctx* c) {
+  if (c->ev_used == c->ev_pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->ev_pool.push_back(e);
+  }
+  return c->ev_pool[c->ev_used++];
+}
+
+// Accounts one launch of `role` (algorithmic bytes / flops) and, while timing
+// is enabled, brackets it with a HIP event pair on the context's stream.
+struct Span {
+  dory_ctx* c;
+  int role;
+  hipEvent_t a = nullptr;
+  Span(dory_ctx* cc, int r, double bytes, double flops) : c(cc), role(r) {
+    c->acc[r].launches++;
+    c->acc[r].bytes += bytes;
+    c->acc[r].flops += flops;
+    if (c->timing && !c->dry) {
+      a = next_event(c);
+      if (a) (void)hipEventRecord(a, c->stream);
+    }
+  }
+  ~Span() {
+    if (!a) return;
+    hipEvent_t b = next_event(c);
+    if (!b) return;
+    (void)hipEventRecord(b, c->stream);
+    c->recs.push_back({role, a, b});
+  }
+};
 
 bool is_full(const dory_ctx* c, int j) { return j % c->cfg.full_every == c->cfg.full_every - 1; }
 
@@ -232,15 +286,40 @@ int choose_splits(const dory_ctx* c, int M, int max_ctx) {
   return std::max(1, std::min(std::min(by_work, by_keys), kMaxSplits));
 }
 
+// Attention geometry of one call: per KV head, the query-key pairs and the
+// distinct keys the rows read, for full and for sliding-window layers.
+struct Geom {
+  double pairs_full = 0, pairs_swa = 0, keys_full = 0, keys_swa = 0;
+  int max_ctx = 0;
+  void add_chunk(int p0, int n, int W) {  // positions p0 .. p0+n-1 of one sequence
+    for (int p = p0; p < p0 + n; ++p) {
+      pairs_full += p + 1;
+      pairs_swa += std::min(p + 1, W);
+    }
+    keys_full += p0 + n;
+    keys_swa += p0 + n - std::max(0, p0 - W + 1);
+    max_ctx = std::max(max_ctx, p0 + n);
+  }
+};
+
 // One block application on M rows held in h / hb.
-void run_block(dory_ctx* c, int j, int t, int M, float* h, int splits) {
+void run_block(dory_ctx* c, int j, int t, int M, float* h, int splits, const Geom& geo) {
   using namespace dory;
   const dory_config& g = c->cfg;
   const int dt = g.dtype, d = g.d_model, H = g.n_heads, Hk = g.n_kv_heads, dh = g.head_dim;
+  const double es = (double)esize(g), Md = (double)M;
+  const int nq = qkv_cols(g), hd = H * dh, F = g.d_ff;
+  const bool full = is_full(c, j);
   c->stats.block_apps++;
   c->stats.sublayer_apps += 2;
-  if (is_full(c, j)) c->stats.full_apps++; else c->stats.swa_apps++;
-  if (c->dry) { c->stats.kernel_launches += 7 + (splits > 1); return; }
+  if (full) c->stats.full_apps++; else c->stats.swa_apps++;
+  const double pairs = full ? geo.pairs_full : geo.pairs_swa;
+  const double keys = full ? geo.keys_full : geo.keys_swa;
+  const double resid_bytes = Md * d * (12 + es) + 4.0 * d;
+  if (c->dry) {
+    c->stats.kernel_launches += 7 + (splits > 1);
+    return;
+  }
   void* hb = c->W(c->L.hb);
   float* qkv = c->W<float>(c->L.qkv);
   float* y = c->W<float>(c->L.y);
@@ -248,43 +327,80 @@ void run_block(dory_ctx* c, int j, int t, int M, float* h, int splits) {
   const int32_t* ptab = c->W<int32_t>(c->L.ptab);
   char* kv = c->pool + (size_t)slot_of(c, j, t) * c->pages_total * c->page_bytes;
   hipStream_t st = c->stream;
-  ok(c, launch_gemm(dt, false, hb, c->wqkv[j], qkv, M, qkv_cols(g), d, st));
-  ok(c, launch_rope_qk_kv(dt, qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), c->W(c->L.q), kv, M, H, Hk,
-                          dh, c->page_el, st));
-  c->stats.kernel_launches += (splits > 1);
-  ok(c, launch_attn_rows(dt, c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, dh,
-                         is_full(c, j) ? 0 : g.window, g.attn_scale, splits, c->W(c->L.o), c->W<float>(c->L.part_ml),
-                         c->W<float>(c->L.part_o), st));
-  ok(c, launch_gemm(dt, false, c->W(c->L.o), c->wo[j], y, M, d, H * dh, st));
-  ok(c, launch_residual(dt, h, y, c->aa[j], hb, M, d, st));
-  ok(c, launch_gemm(dt, true, hb, c->wgu[j], c->W(c->L.z), M, 2 * g.d_ff, d, st));
-  ok(c, launch_gemm(dt, false, c->W(c->L.z), c->wd[j], y, M, d, g.d_ff, st));
-  ok(c, launch_residual(dt, h, y, c->am[j], hb, M, d, st));
+  {
+    Span sp(c, R_QKV, (double)nq * d * es + Md * d * es + Md * nq * 4, 2.0 * Md * nq * d);
+    ok(c, launch_gemm(dt, false, hb, c->wqkv[j], qkv, M, nq, d, st));
+  }
+  {
+    Span sp(c, R_ROPE, Md * nq * 4 + Md * (hd + 2.0 * Hk * dh) * es, 0);
+    ok(c, launch_rope_qk_kv(dt, qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), c->W(c->L.q), kv, M, H,
+                            Hk, dh, c->page_el, st));
+  }
+  {
+    Span sp(c, R_ATTN, keys * 2.0 * Hk * dh * es + 2.0 * Md * hd * es, 4.0 * dh * H * pairs);
+    if (splits > 1) c->stats.kernel_launches++;
+    ok(c, launch_attn_rows(dt, c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, dh,
+                           full ? 0 : g.window, g.attn_scale, splits, c->W(c->L.o), c->W<float>(c->L.part_ml),
+                           c->W<float>(c->L.part_o), st));
+  }
+  {
+    Span sp(c, R_OPROJ, (double)d * hd * es + Md * hd * es + Md * d * 4, 2.0 * Md * d * hd);
+    ok(c, launch_gemm(dt, false, c->W(c->L.o), c->wo[j], y, M, d, hd, st));
+  }
+  {
+    Span sp(c, R_RESID, resid_bytes, 0);
+    ok(c, launch_residual(dt, h, y, c->aa[j], hb, M, d, st));
+  }
+  {
+    Span sp(c, R_GU, 2.0 * F * d * es + Md * d * es + Md * F * es, 2.0 * Md * 2 * F * d);
+    ok(c, launch_gemm(dt, true, hb, c->wgu[j], c->W(c->L.z), M, 2 * F, d, st));
+  }
+  {
+    Span sp(c, R_DOWN, (double)d * F * es + Md * F * es + Md * d * 4, 2.0 * Md * d * F);
+    ok(c, launch_gemm(dt, false, c->W(c->L.z), c->wd[j], y, M, d, F, st));
+  }
+  {
+    Span sp(c, R_RESID, resid_bytes, 0);
+    ok(c, launch_residual(dt, h, y, c->am[j], hb, M, d, st));
+  }
 }
 
 // Whole forward pass over M rows whose (seq, pos) pairs are in the upload area.
 // Leaves the final hidden rows in c->last_h and their storage copy in hb.
-void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, int max_ctx) {
+void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, const Geom& geo) {
   using namespace dory;
   const dory_config& g = c->cfg;
   const int dt = g.dtype, d = g.d_model;
+  const double es = (double)esize(g), Md = (double)M;
   float* b[3] = {c->W<float>(c->L.buf[0]), c->W<float>(c->L.buf[1]), c->W<float>(c->L.buf[2])};
   void* hb = c->W(c->L.hb);
-  const int splits = choose_splits(c, M, max_ctx);
-  if (!c->dry) ok(c, launch_embed(dt, tokens_dev, c->embed, g.vocab, d, M, b[0], hb, c->W<int32_t>(c->L.err), c->stream));
-  else c->stats.kernel_launches++;
-  for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, b[0], splits);
+  const int splits = choose_splits(c, M, geo.max_ctx);
+  if (!c->dry) {
+    Span sp(c, R_EMBED, Md * d * (2 * es + 4) + Md * 4, 0);
+    ok(c, launch_embed(dt, tokens_dev, c->embed, g.vocab, d, M, b[0], hb, c->W<int32_t>(c->L.err), c->stream));
+  } else {
+    c->stats.kernel_launches++;
+  }
+  for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, b[0], splits, geo);
   float *x = b[0], *h = b[1], *s = b[2];
   for (int t = 1; t <= c->k; ++t) {
     // u_t = N(s_{t-1} + x), with s_0 = x
-    if (!c->dry) ok(c, launch_norm_sum(dt, t == 1 ? x : s, x, h, nullptr, hb, M, d, c->stream));
-    else c->stats.kernel_launches++;
-    for (int j = g.n_in; j < g.n_in + g.n_rec; ++j) run_block(c, j, t, M, h, splits);
+    if (!c->dry) {
+      Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
+      ok(c, launch_norm_sum(dt, t == 1 ? x : s, x, h, nullptr, hb, M, d, c->stream));
+    } else {
+      c->stats.kernel_launches++;
+    }
+    for (int j = g.n_in; j < g.n_in + g.n_rec; ++j) run_block(c, j, t, M, h, splits, geo);
     // s_t = N(F(u_t)); h continues as s_t
-    if (!c->dry) ok(c, launch_norm_sum(dt, h, nullptr, h, s, hb, M, d, c->stream));
-    else c->stats.kernel_launches++;
+    if (!c->dry) {
+      Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
+      ok(c, launch_norm_sum(dt, h, nullptr, h, s, hb, M, d, c->stream));
+    } else {
+      c->stats.kernel_launches++;
+    }
   }
-  for (int j = g.n_in + g.n_rec; j < c->n_blocks; ++j) run_block(c, j, 1, M, h, splits);
+  for (int j = g.n_in + g.n_rec; j < c->n_blocks; ++j) run_block(c, j, 1, M, h, splits, geo);
   c->last_h = h;
   c->last_rows = M;
 }
@@ -292,10 +408,20 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, int max_ctx) {
 void lm_head(dory_ctx* c, int M, int rows, float* logits, int32_t* ids) {
   using namespace dory;
   const dory_config& g = c->cfg;
-  if (c->dry) { c->stats.kernel_launches += 1 + (ids != nullptr); return; }
+  if (c->dry) {
+    c->stats.kernel_launches += 1 + (ids != nullptr);
+    return;
+  }
+  const double es = (double)esize(g), V = g.vocab, d = g.d_model;
   const char* hb = c->W(c->L.hb) + (size_t)(M - rows) * g.d_model * esize(g);
-  ok(c, launch_gemm(g.dtype, false, hb, c->lm, logits, rows, g.vocab, g.d_model, c->stream));
-  if (ids) ok(c, launch_argmax(logits, rows, g.vocab, ids, c->stream));
+  {
+    Span sp(c, R_LM, V * d * es + rows * d * es + rows * V * 4, 2.0 * rows * V * d);
+    ok(c, launch_gemm(g.dtype, false, hb, c->lm, logits, rows, g.vocab, g.d_model, c->stream));
+  }
+  if (ids) {
+    Span sp(c, R_ARGMAX, rows * V * 4 + rows * 4.0, 0);
+    ok(c, launch_argmax(logits, rows, g.vocab, ids, c->stream));
+  }
 }
 
 bool valid_seq(const dory_ctx* c, int32_t id) { return id >= 0 && id < c->cfg.max_seqs; }
@@ -424,6 +550,7 @@ void dory_destroy(dory_ctx* c) {
   if (!c) return;
   if (!c->dry) {
     (void)hipStreamSynchronize(c->stream);
+    for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
     for (int i = 0; i < kStageSlots; ++i) {
       if (c->stage[i]) (void)hipHostFree(c->stage[i]);
       if (c->stage_ev[i]) (void)hipEventDestroy(c->stage_ev[i]);
@@ -481,11 +608,16 @@ dory_status dory_prefill(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, in
   const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
   c->herr = hipSuccess;
   if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
-  if (!c->dry) ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints,
-                                                n_upd, c->stream));
+  if (!c->dry && n_upd) {
+    Span sp(c, R_PTAB, 12.0 * n_upd, 0);
+    ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
+                                     c->stream));
+  }
   s.len = len + n;
   s.append_run(s.len, c->k);
-  run_forward(c, tokens_dev, n, std::min(len + n, c->cfg.max_model_len));
+  Geom geo;
+  geo.add_chunk(len, n, c->cfg.window);
+  run_forward(c, tokens_dev, n, geo);
   lm_head(c, n, logits_rows, logits_dev, ids_dev);
   c->stats.calls++;
   if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
@@ -500,7 +632,7 @@ dory_status dory_decode(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
   if (!seq_ids) return fail(c, DORY_E_INVALID, "seq_ids_host is NULL");
   if (!c->dry && !tokens_dev) return fail(c, DORY_E_INVALID, "tokens_dev is NULL");
   if (!logits_dev && n > c->L.logit_rows) return fail(c, DORY_E_INVALID, "logits scratch holds %d rows", c->L.logit_rows);
-  int need = 0, max_ctx = 0;
+  int need = 0;
   for (int i = 0; i < n; ++i) {
     const int sid = seq_ids[i];
     if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
@@ -511,7 +643,6 @@ dory_status dory_decode(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
     if (c->kv_mode == DORY_KV_PER_LOOP && s.len > 0 && s.min_loops() < c->k)
       return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), c->k);
     need += (s.len + 1 + kPage - 1) / kPage - (int)s.pages.size();
-    max_ctx = std::max(max_ctx, s.len + 1);
   }
   if (need > (int)c->free_pages.size())
     return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
@@ -522,15 +653,19 @@ dory_status dory_decode(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
   const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
   c->herr = hipSuccess;
   if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
-  if (!c->dry && n_upd)
+  if (!c->dry && n_upd) {
+    Span sp(c, R_PTAB, 12.0 * n_upd, 0);
     ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
                                      c->stream));
+  }
+  Geom geo;
   for (int i = 0; i < n; ++i) {
     Seq& s = c->seqs[seq_ids[i]];
+    geo.add_chunk(s.len, 1, c->cfg.window);
     s.len += 1;
     s.append_run(s.len, c->k);
   }
-  run_forward(c, tokens_dev, n, max_ctx);
+  run_forward(c, tokens_dev, n, geo);
   float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
   lm_head(c, n, n, logits, next_ids_dev);
   c->stats.calls++;
@@ -590,6 +725,48 @@ dory_status dory_last_hidden(dory_ctx* c, float* dst, int32_t rows) {
   hipError_t e = hipMemcpyAsync(dst, c->last_h + (size_t)(c->last_rows - rows) * d, (size_t)rows * d * 4,
                                 hipMemcpyDeviceToDevice, c->stream);
   return e == hipSuccess ? DORY_OK : fail(c, DORY_E_HIP, "%s", hipGetErrorString(e));
+}
+
+dory_status dory_set_timing(dory_ctx* c, int32_t enable) {
+  if (!c) return DORY_E_INVALID;
+  c->timing = enable != 0;
+  return DORY_OK;
+}
+
+dory_status dory_get_timing(dory_ctx* c, dory_kernel_time* out, int32_t max, int32_t* n, int32_t reset) {
+  if (!c || !n || (max > 0 && !out)) return DORY_E_INVALID;
+  if (!c->recs.empty()) {
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return fail(c, DORY_E_HIP, "%s", hipGetErrorString(e));
+    for (const TimedRec& r : c->recs) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+        c->acc[r.role].ms += ms;
+        c->acc[r.role].timed++;
+      }
+    }
+    c->recs.clear();
+    c->ev_used = 0;
+  }
+  int cnt = 0;
+  for (int r = 0; r < R_COUNT; ++r) {
+    if (c->acc[r].launches == 0) continue;
+    if (cnt < max) {
+      dory_kernel_time& o = out[cnt];
+      memset(&o, 0, sizeof o);
+      snprintf(o.name, sizeof o.name, "%s", kRoleName[r]);
+      o.launches = c->acc[r].launches;
+      o.bytes = c->acc[r].bytes;
+      o.flops = c->acc[r].flops;
+      o.timed_launches = c->acc[r].timed;
+      o.total_ms = c->acc[r].ms;
+    }
+    ++cnt;
+  }
+  *n = cnt;
+  if (reset)
+    for (auto& a : c->acc) a = RoleAcc();
+  return DORY_OK;
 }
 
 dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_new, int32_t gamma, int32_t k_draft,

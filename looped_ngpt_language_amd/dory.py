@@ -51,6 +51,11 @@ class Stats(C.Structure):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
 
+class KernelTime(C.Structure):
+    _fields_ = [("name", C.c_char * 32), ("launches", C.c_int64), ("bytes", C.c_double), ("flops", C.c_double),
+                ("timed_launches", C.c_int64), ("total_ms", C.c_double)]
+
+
 EXPORTS = {
     "dory_query_sizes": (C.c_int, [C.POINTER(Config), C.c_int32, C.c_int64, C.POINTER(C.c_size_t),
                                    C.POINTER(C.c_size_t)]),
@@ -70,6 +75,8 @@ EXPORTS = {
     "dory_last_hidden": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
     "dory_spec_decode": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+    "dory_set_timing": (C.c_int, [C.c_void_p, C.c_int32]),
+    "dory_get_timing": (C.c_int, [C.c_void_p, C.POINTER(KernelTime), C.c_int32, C.POINTER(C.c_int32), C.c_int32]),
     "dory_last_error": (C.c_char_p, [C.c_void_p]),
     "dory_status_string": (C.c_char_p, [C.c_int32]),
 }
@@ -276,6 +283,21 @@ class Model:
         import torch
         out = torch.empty((rows, self.shape.d_model), dtype=torch.float32, device=self.device)
         self._check(lib().dory_last_hidden(self.ctx, _ptr(out), int(rows)), "dory_last_hidden")
+        return out
+
+    def set_timing(self, enable: bool):
+        self._check(lib().dory_set_timing(self.ctx, 1 if enable else 0), "dory_set_timing")
+
+    def timing(self, reset: bool = False) -> dict:
+        """Per kernel role: launches, algorithmic bytes/flops, timed launches and milliseconds."""
+        buf = (KernelTime * 32)()
+        n = C.c_int32()
+        self._check(lib().dory_get_timing(self.ctx, buf, 32, C.byref(n), 1 if reset else 0), "dory_get_timing")
+        out = {}
+        for i in range(min(n.value, 32)):
+            e = buf[i]
+            out[e.name.decode()] = {"launches": e.launches, "bytes": e.bytes, "flops": e.flops,
+                                    "timed_launches": e.timed_launches, "ms": e.total_ms}
         return out
 
     def spec_decode(self, seq_id: int, last: int, n_new: int, gamma=4, k_draft=1, k_verify=4):
