@@ -105,6 +105,19 @@ def main():
                                  "tflop": flops / 1e12, "tflop_s": tfs, "mfma_frac": tfs / BF16_PEAK_TFLOPS}
             log(f"[bench] prefill T={args.prefill_len} k={k}: {ms:.2f} ms  {args.prefill_len / (ms * 1e-3):,.0f} tok/s  "
                 f"{tfs:.1f} TFLOP/s ({100 * tfs / BF16_PEAK_TFLOPS:.1f}% of MFMA peak)")
+            # instrumented pass: one prefill with an event pair around every launch
+            m.set_timing(True)
+            m.prefill(0, toks, 1, logits=logits)
+            m.release(0)
+            tim = m.timing(reset=True)
+            m.set_timing(False)
+            kern = {}
+            for name, v in sorted(tim.items(), key=lambda x: -x[1]["ms"]):
+                if v["timed_launches"]:
+                    tf = v["flops"] / (v["ms"] * 1e-3) / 1e12 if v["ms"] else 0.0
+                    kern[name] = {"ms": v["ms"], "tflop_s": tf, "launches": v["launches"]}
+                    log(f"         {name:22s} {v['launches']:5d} launches  {v['ms']:8.2f} ms  {tf:7.1f} TFLOP/s")
+            res["prefill"][k]["kernels"] = kern
 
     # ---------------------------------------------------------------- decode
     ptoks = torch.from_numpy(prompt[:args.prompt]).to("cuda:0")

@@ -279,10 +279,13 @@ bool stage_upload(dory_ctx* c, int n_ints) {
   return true;
 }
 
-int choose_splits(const dory_ctx* c, int M, int max_ctx) {
+// Key splits per (row, KV head) for split attention: enough workgroups to fill
+// the chip, at least two 16-key pages per wave of the bf16 decode kernel (one
+// key batch per wave for the generic kernel), at most kMaxSplits.
+int choose_splits(const dory_ctx* c, int M, int keys, bool paged_kernel) {
   if (M > c->L.part_rows) return 1;
-  const int by_work = (1024 + M * c->cfg.n_kv_heads - 1) / (M * c->cfg.n_kv_heads);
-  const int by_keys = (max_ctx + 63) / 64;
+  const int by_work = (2048 + M * c->cfg.n_kv_heads - 1) / (M * c->cfg.n_kv_heads);
+  const int by_keys = paged_kernel ? (keys + 127) / 128 : (keys + 63) / 64;
   return std::max(1, std::min(std::min(by_work, by_keys), kMaxSplits));
 }
 
@@ -303,7 +306,7 @@ struct Geom {
 };
 
 // One block application on M rows held in h / hb.
-void run_block(dory_ctx* c, int j, int t, int M, float* h, int splits, const Geom& geo) {
+void run_block(dory_ctx* c, int j, int t, int M, float* h, bool decode, const Geom& geo) {
   using namespace dory;
   const dory_config& g = c->cfg;
   const int dt = g.dtype, d = g.d_model, H = g.n_heads, Hk = g.n_kv_heads, dh = g.head_dim;
@@ -316,8 +319,13 @@ void run_block(dory_ctx* c, int j, int t, int M, float* h, int splits, const Geo
   const double pairs = full ? geo.pairs_full : geo.pairs_swa;
   const double keys = full ? geo.keys_full : geo.keys_swa;
   const double resid_bytes = Md * d * (12 + es) + 4.0 * d;
+  const int keys_max = full ? geo.max_ctx : std::min(geo.max_ctx, g.window);
+  const bool paged = attn_decode_supported(dt, H, Hk, dh);
+  const bool fused_decode = decode && paged;
+  const bool flash = !decode && dt == DORY_BF16 && dh == 128 && M > c->L.part_rows;
+  const int splits = flash ? 1 : choose_splits(c, M, keys_max, paged);
   if (c->dry) {
-    c->stats.kernel_launches += 7 + (splits > 1);
+    c->stats.kernel_launches += 6 + (fused_decode ? 1 : 2) + (!paged && !flash && splits > 1);
     return;
   }
   void* hb = c->W(c->L.hb);
@@ -331,17 +339,29 @@ void run_block(dory_ctx* c, int j, int t, int M, float* h, int splits, const Geo
     Span sp(c, R_QKV, (double)nq * d * es + Md * d * es + Md * nq * 4, 2.0 * Md * nq * d);
     ok(c, launch_gemm(dt, false, hb, c->wqkv[j], qkv, M, nq, d, st));
   }
-  {
+  if (!fused_decode) {
     Span sp(c, R_ROPE, Md * nq * 4 + Md * (hd + 2.0 * Hk * dh) * es, 0);
     ok(c, launch_rope_qk_kv(dt, qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), c->W(c->L.q), kv, M, H,
                             Hk, dh, c->page_el, st));
   }
   {
-    Span sp(c, R_ATTN, keys * 2.0 * Hk * dh * es + 2.0 * Md * hd * es, 4.0 * dh * H * pairs);
-    if (splits > 1) c->stats.kernel_launches++;
-    ok(c, launch_attn_rows(dt, c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, dh,
-                           full ? 0 : g.window, g.attn_scale, splits, c->W(c->L.o), c->W<float>(c->L.part_ml),
-                           c->W<float>(c->L.part_o), st));
+    // fused decode reads q/k/v from the projection output and writes the new key/value itself
+    const double io = fused_decode ? Md * nq * 4 + Md * hd * es + Md * 2.0 * Hk * dh * es : 2.0 * Md * hd * es;
+    Span sp(c, R_ATTN, keys * 2.0 * Hk * dh * es + io, 4.0 * dh * H * pairs);
+    const int win = full ? 0 : g.window;
+    if (paged && (decode || !flash)) {
+      ok(c, launch_attn_decode(qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), kv, c->page_el, M, H, Hk,
+                               win, g.attn_scale, splits, fused_decode ? 1 : 0, c->W(c->L.o), c->W<float>(c->L.part_ml),
+                               c->W<float>(c->L.part_o), st));
+    } else if (flash) {
+      ok(c, launch_attn_prefill(c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, win,
+                                g.attn_scale, c->W(c->L.o), st));
+    } else {
+      if (splits > 1) c->stats.kernel_launches++;
+      ok(c, launch_attn_rows(dt, c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, dh, win,
+                             g.attn_scale, splits, c->W(c->L.o), c->W<float>(c->L.part_ml), c->W<float>(c->L.part_o),
+                             st));
+    }
   }
   {
     Span sp(c, R_OPROJ, (double)d * hd * es + Md * hd * es + Md * d * 4, 2.0 * Md * d * hd);
@@ -367,21 +387,20 @@ void run_block(dory_ctx* c, int j, int t, int M, float* h, int splits, const Geo
 
 // Whole forward pass over M rows whose (seq, pos) pairs are in the upload area.
 // Leaves the final hidden rows in c->last_h and their storage copy in hb.
-void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, const Geom& geo) {
+void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, const Geom& geo) {
   using namespace dory;
   const dory_config& g = c->cfg;
   const int dt = g.dtype, d = g.d_model;
   const double es = (double)esize(g), Md = (double)M;
   float* b[3] = {c->W<float>(c->L.buf[0]), c->W<float>(c->L.buf[1]), c->W<float>(c->L.buf[2])};
   void* hb = c->W(c->L.hb);
-  const int splits = choose_splits(c, M, geo.max_ctx);
   if (!c->dry) {
     Span sp(c, R_EMBED, Md * d * (2 * es + 4) + Md * 4, 0);
     ok(c, launch_embed(dt, tokens_dev, c->embed, g.vocab, d, M, b[0], hb, c->W<int32_t>(c->L.err), c->stream));
   } else {
     c->stats.kernel_launches++;
   }
-  for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, b[0], splits, geo);
+  for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, b[0], decode, geo);
   float *x = b[0], *h = b[1], *s = b[2];
   for (int t = 1; t <= c->k; ++t) {
     // u_t = N(s_{t-1} + x), with s_0 = x
@@ -391,7 +410,7 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, const Geom& geo)
     } else {
       c->stats.kernel_launches++;
     }
-    for (int j = g.n_in; j < g.n_in + g.n_rec; ++j) run_block(c, j, t, M, h, splits, geo);
+    for (int j = g.n_in; j < g.n_in + g.n_rec; ++j) run_block(c, j, t, M, h, decode, geo);
     // s_t = N(F(u_t)); h continues as s_t
     if (!c->dry) {
       Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
@@ -400,7 +419,7 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, const Geom& geo)
       c->stats.kernel_launches++;
     }
   }
-  for (int j = g.n_in + g.n_rec; j < c->n_blocks; ++j) run_block(c, j, 1, M, h, splits, geo);
+  for (int j = g.n_in + g.n_rec; j < c->n_blocks; ++j) run_block(c, j, 1, M, h, decode, geo);
   c->last_h = h;
   c->last_rows = M;
 }
@@ -537,6 +556,8 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t k
                                                       (double)cfg->rope_theta, c->stream);
     if (e == hipSuccess) e = hipMemsetAsync(c->W(L.ptab), 0, (size_t)cfg->max_seqs * L.max_pages * 4, c->stream);
     if (e == hipSuccess) e = hipMemsetAsync(c->W(L.err), 0, 4, c->stream);
+    // unwritten cache slots hold zeros, never NaN bit patterns, so masked keys contribute 0 * v = 0
+    if (e == hipSuccess) e = hipMemsetAsync(c->pool, 0, c->pool_bytes, c->stream);
     if (e != hipSuccess) {
       dory_destroy(c);
       return DORY_E_HIP;
@@ -617,7 +638,7 @@ dory_status dory_prefill(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, in
   s.append_run(s.len, c->k);
   Geom geo;
   geo.add_chunk(len, n, c->cfg.window);
-  run_forward(c, tokens_dev, n, geo);
+  run_forward(c, tokens_dev, n, false, geo);
   lm_head(c, n, logits_rows, logits_dev, ids_dev);
   c->stats.calls++;
   if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
@@ -665,7 +686,7 @@ dory_status dory_decode(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
     s.len += 1;
     s.append_run(s.len, c->k);
   }
-  run_forward(c, tokens_dev, n, geo);
+  run_forward(c, tokens_dev, n, true, geo);
   float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
   lm_head(c, n, n, logits, next_ids_dev);
   c->stats.calls++;

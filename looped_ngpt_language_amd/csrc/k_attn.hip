@@ -1,6 +1,8 @@
 // Attention sublayer kernels: rotary embedding + per-head L2 norm of q and k with
-// the paged KV write, row attention (split over keys for decode) and the merge
-// of split partials.
+// the paged KV write, the split-key decode attention (with the rotary/norm/KV
+// write of the new token fused in and the split merge done by the last
+// workgroup), an MFMA flash-attention kernel for prefill chunks, and a generic
+// row kernel for the fp32 model.
 //
 // Attention of a row at position p, query head h, KV head g = h / (H/H_kv):
 //   o = sum_j softmax_j(scale * q^.k^_j) v_j over keys p-W < j <= p (sliding
@@ -11,12 +13,18 @@
 // query reads it; in last-loop mode every loop writes the recurrent block's
 // single slot (onedev.kr, section "전제와 한계").
 //
-// KV pool layout: slot-major; a page slot holds 16 tokens of one layer slot:
-//   [K|V][H_kv][16 tokens][d_h] in the storage type.
+// KV pool layout: slot-major; a page slot holds 16 tokens of one layer slot,
+// keys row-major and values transposed so both attention products load
+// contiguous 16-byte operands:
+//   K: [H_kv][16 tokens][d_h]     V^T: [H_kv][d_h][16 tokens]
 #include "common.h"
 #include "kernels.h"
 
 namespace dory {
+
+DORY_DEV float safe_scale(float m_old, float m_new) { return m_old == -INFINITY ? 0.f : __expf(m_old - m_new); }
+
+// ---------------------------------------------------------------- rotary + norm + KV write
 
 // One wave per (row, head). Heads 0..H-1 are queries: q^ = N(RoPE(q)) -> q_out.
 // Heads H..H+H_kv-1 are keys: k^ = N(RoPE(k)) and v go to the cache page of the
@@ -49,24 +57,24 @@ __global__ void __launch_bounds__(64) k_rope_qk_kv(const float* __restrict__ qkv
     }
     return;
   }
-  const int g = hd - H;
+  const int g = hd - H, tok = pos & 15;
   const int page = ptab[(size_t)seq * max_pages + (pos >> 4)];
-  T* kp = kv_slot + (size_t)page * page_elems + ((size_t)g * 16 + (pos & 15)) * dh;
-  T* vp = kp + (size_t)Hkv * 16 * dh;
+  T* kp = kv_slot + (size_t)page * page_elems + ((size_t)g * 16 + tok) * dh;
+  T* vt = kv_slot + (size_t)page * page_elems + (size_t)Hkv * 16 * dh + (size_t)g * dh * 16 + tok;
   const float* vsrc = src + (size_t)Hkv * dh;
   if (act) {
     St<T>::st(kp, lane, a0 * r);
     St<T>::st(kp, lane + half, a1 * r);
-    St<T>::st(vp, lane, vsrc[lane]);
-    St<T>::st(vp, lane + half, vsrc[lane + half]);
+    St<T>::st(vt, (size_t)lane * 16, vsrc[lane]);
+    St<T>::st(vt, (size_t)(lane + half) * 16, vsrc[lane + half]);
   }
 }
+
+// ---------------------------------------------------------------- generic row attention
 
 constexpr int ATT_THREADS = 256;
 constexpr int ATT_WAVES = ATT_THREADS / 64;
 constexpr int GMAX = 8;  // query heads per KV head
-
-DORY_DEV float safe_scale(float m_old, float m_new) { return m_old == -INFINITY ? 0.f : __expf(m_old - m_new); }
 
 // Row attention: grid (rows, H_kv, splits). Each workgroup handles the query
 // heads of one KV head for one row over one contiguous share of its key range.
@@ -109,13 +117,14 @@ __global__ void __launch_bounds__(ATT_THREADS) k_attn_rows(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
   }
-  const size_t vofs = (size_t)Hkv * 16 * DH;
   for (int j = kbeg + wv * KPW + lane / LPK; j < kend; j += ATT_WAVES * KPW) {
     const int page = ptab[(size_t)seq * max_pages + (j >> 4)];
-    const T* kp = kv_slot + (size_t)page * page_elems + ((size_t)g * 16 + (j & 15)) * DH + e0;
+    const T* pg = kv_slot + (size_t)page * page_elems;
     float kf[8], vf[8];
-    load8(kp, kf);
-    load8(kp + vofs, vf);
+    load8(pg + ((size_t)g * 16 + (j & 15)) * DH + e0, kf);
+    const T* vt = pg + (size_t)Hkv * 16 * DH + ((size_t)g * DH + e0) * 16 + (j & 15);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vf[e] = St<T>::ld(vt, (size_t)e * 16);
 #pragma unroll
     for (int gi = 0; gi < GMAX; ++gi) {
       if (gi < G) {
@@ -162,7 +171,6 @@ __global__ void __launch_bounds__(ATT_THREADS) k_attn_rows(
     }
   }
   __syncthreads();
-  // Merge the waves: thread t handles (head gi, dim e) pairs.
   for (int idx = threadIdx.x; idx < G * DH; idx += ATT_THREADS) {
     const int gi = idx / DH, e = idx % DH;
     float M = -INFINITY;
@@ -184,22 +192,365 @@ __global__ void __launch_bounds__(ATT_THREADS) k_attn_rows(
   }
 }
 
-// Merge split partials: grid rows*H, block DH threads.
+// Merge split partials: grid rows*H, block max(64, dh) threads. The first wave
+// turns the split maxima into weights exp(m_s - M) (LDS) and the total sum;
+// then thread e sums dim e over the splits with independent loads.
 template <typename T>
-__global__ void k_attn_merge(const float* __restrict__ part_ml, const float* __restrict__ part_o, int splits,
-                             int dh, T* __restrict__ out) {
+__global__ void __launch_bounds__(128) k_attn_merge(const float* __restrict__ part_ml,
+                                                    const float* __restrict__ part_o, int splits, int dh,
+                                                    T* __restrict__ out) {
+  __shared__ float sw[64];
+  __shared__ float sL;
   const size_t rh = blockIdx.x;
   const int e = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[2 * (rh * splits + s)]);
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const size_t pi = rh * splits + s;
-    const float c = safe_scale(part_ml[2 * pi], M);
-    L += part_ml[2 * pi + 1] * c;
-    A += part_o[pi * dh + e] * c;
+  if (e < 64) {
+    const float ms = e < splits ? part_ml[2 * (rh * splits + e)] : -INFINITY;
+    const float ls = e < splits ? part_ml[2 * (rh * splits + e) + 1] : 0.f;
+    const float M = wave_max(ms);
+    const float c = safe_scale(ms, M);
+    sw[e] = c;
+    const float L = wave_sum(ls * c);
+    if (e == 0) sL = L;
   }
-  if (e < dh) St<T>::st(out, rh * dh + e, L > 0.f ? A / L : 0.f);
+  __syncthreads();
+  if (e >= dh) return;
+  const float* po = part_o + rh * splits * dh + e;
+  float A4[4] = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = po[(size_t)(s + i) * dh];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A4[i & 3] += sw[s + i] * v[i];
+  }
+  for (; s < splits; ++s) A4[0] += sw[s] * po[(size_t)s * dh];
+  const float A = (A4[0] + A4[1]) + (A4[2] + A4[3]);
+  St<T>::st(out, rh * dh + e, sL > 0.f ? A / sL : 0.f);
+}
+
+// ---------------------------------------------------------------- bf16 split-key attention, d_h = 128
+
+DORY_DEV float bf16r(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+
+// grid (rows, H_kv, splits), 256 threads. Each workgroup attends the G query
+// heads of KV head g for one row over a page-aligned share of the row's keys.
+// Lane l of a wave reads key (l >> 2) of a page, dims 32*(l & 3) .. +32 for the
+// scores and the value rows 2l, 2l+1 (all 16 keys) for the output. With
+// write_kv, the split holding the row's own position first writes that
+// position's k^ and v (decode: each row is the newest token of its sequence).
+// With splits > 1 each workgroup stores a partial (max, sum, unnormalised
+// output) and k_attn_merge combines them.
+template <int G>
+__global__ void __launch_bounds__(256) k_attn_decode(
+    const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
+    const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window,
+    float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
+    float* __restrict__ part_o) {
+  constexpr int DH = 128;
+  __shared__ float qs[G][DH];
+  __shared__ float knew[DH], vnew[DH];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wacc[4][G][DH];
+  const int m = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int seq = rows[2 * m], pos = rows[2 * m + 1];
+  const int lo = window > 0 ? max(0, pos - window + 1) : 0;
+  const int nkeys = pos - lo + 1;
+  const int chunk = (((nkeys + splits - 1) / splits) + 15) & ~15;
+  const int kbeg = lo + sp * chunk;
+  const int kend = min(pos + 1, kbeg + chunk);
+  const float* src = qkv + (size_t)m * (size_t)((H + 2 * Hkv) * DH);
+  const float2 cs = rope[(size_t)pos * 64 + lane];
+
+  // queries of the group: q^ = N(RoPE(q)), rounded to bf16, times the scale
+  for (int gi = wv; gi < G; gi += 4) {
+    const float* x = src + (size_t)(g * G + gi) * DH;
+    const float x1 = x[lane], x2 = x[lane + 64];
+    const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
+    const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    qs[gi][lane] = bf16r(a0 * r) * scale;
+    qs[gi][lane + 64] = bf16r(a1 * r) * scale;
+  }
+  // The split holding the row's own position writes its key/value and keeps
+  // them in LDS: the key loop below takes that key from LDS, not from memory.
+  const bool writer = write_kv && kbeg <= pos && pos < kend;
+  if (writer && wv < 2) {
+    const int page = ptab[(size_t)seq * max_pages + (pos >> 4)];
+    bf16_t* pg = kv_slot + (size_t)page * page_elems;
+    const int tok = pos & 15;
+    if (wv == 0) {
+      const float* x = src + (size_t)(H + g) * DH;
+      const float x1 = x[lane], x2 = x[lane + 64];
+      const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
+      const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+      const bf16_t k0 = f32_to_bf16(a0 * r), k1 = f32_to_bf16(a1 * r);
+      bf16_t* kp = pg + ((size_t)g * 16 + tok) * DH;
+      kp[lane] = k0;
+      kp[lane + 64] = k1;
+      knew[lane] = bf16_to_f32(k0);
+      knew[lane + 64] = bf16_to_f32(k1);
+    } else {
+      const float* v = src + (size_t)(H + Hkv + g) * DH;
+      const bf16_t v0 = f32_to_bf16(v[lane]), v1 = f32_to_bf16(v[lane + 64]);
+      bf16_t* vt = pg + (size_t)Hkv * 16 * DH + (size_t)g * DH * 16 + tok;
+      vt[(size_t)lane * 16] = v0;
+      vt[(size_t)(lane + 64) * 16] = v1;
+      vnew[lane] = bf16_to_f32(v0);
+      vnew[lane + 64] = bf16_to_f32(v1);
+    }
+  }
+  __syncthreads();
+
+  const int r = lane >> 2, db = lane & 3;
+  float qf[G][32];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qf[gi][i] = qs[gi][db * 32 + i];
+  float mrun[G], lrun[G], acc[G][2];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) { mrun[gi] = -INFINITY; lrun[gi] = 0.f; acc[gi][0] = acc[gi][1] = 0.f; }
+
+  if (kbeg < kend) {
+    const int p_first = (kbeg >> 4) + wv, p_last = (kend - 1) >> 4;
+    const int np = p_first <= p_last ? (p_last - p_first) / 4 + 1 : 0;  // pages of this wave
+    const size_t vofs = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16 + (size_t)lane * 32;
+    const size_t kofs = ((size_t)g * 16 + r) * DH + db * 32;
+    const int32_t* prow = ptab + (size_t)seq * max_pages;
+    // page ids of this wave's pages, 64 at a time, one per lane
+    int pid = lane < np ? prow[p_first + 4 * lane] : 0;
+    uint4 kr[4], vr[4];
+    auto fetch = [&](int it) {
+      const int page = __shfl(pid, it & 63, 64);
+      const bf16_t* pg = kv_slot + (size_t)page * page_elems;
+      const uint4* kp = reinterpret_cast<const uint4*>(pg + kofs);
+      const uint4* vp = reinterpret_cast<const uint4*>(pg + vofs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kr[i] = kp[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vr[i] = vp[i];
+    };
+    if (np > 0) fetch(0);
+    for (int it = 0; it < np; ++it) {
+      const int p = p_first + 4 * it;
+      float kf[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kf[8 * i + 2 * j] = __uint_as_float(w4[j] << 16);
+          kf[8 * i + 2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
+        }
+      }
+      // value rows 2*lane (vr[0..1]) and 2*lane+1 (vr[2..3]), 16 keys each
+      float v0[16], v1[16];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t a4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        const uint32_t b4[4] = {vr[i + 2].x, vr[i + 2].y, vr[i + 2].z, vr[i + 2].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v0[8 * i + 2 * j] = __uint_as_float(a4[j] << 16);
+          v0[8 * i + 2 * j + 1] = __uint_as_float(a4[j] & 0xFFFF0000u);
+          v1[8 * i + 2 * j] = __uint_as_float(b4[j] << 16);
+          v1[8 * i + 2 * j + 1] = __uint_as_float(b4[j] & 0xFFFF0000u);
+        }
+      }
+      // next page's loads are in flight while this page is computed
+      if (it + 1 < np) {
+        if (((it + 1) & 63) == 0) pid = lane + it + 1 < np ? prow[p_first + 4 * (it + 1 + lane)] : 0;
+        fetch(it + 1);
+      }
+      const int key = p * 16 + r;
+      const bool valid = key >= kbeg && key < kend;
+      if (writer && p == (pos >> 4)) {
+        const int tok = pos & 15;
+        if (r == tok) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) kf[i] = knew[db * 32 + i];
+        }
+        const float n0 = vnew[2 * lane], n1 = vnew[2 * lane + 1];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          v0[kk] = kk == tok ? n0 : v0[kk];
+          v1[kk] = kk == tok ? n1 : v1[kk];
+        }
+      }
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) s += qf[gi][i] * kf[i];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        s = valid ? s : -INFINITY;
+        float mp = s;
+        mp = fmaxf(mp, __shfl_xor(mp, 4, 64));
+        mp = fmaxf(mp, __shfl_xor(mp, 8, 64));
+        mp = fmaxf(mp, __shfl_xor(mp, 16, 64));
+        mp = fmaxf(mp, __shfl_xor(mp, 32, 64));
+        const float mn = fmaxf(mrun[gi], mp);
+        const float c = safe_scale(mrun[gi], mn);
+        const float pr = valid ? __expf(s - mn) : 0.f;
+        float ps = db == 0 ? pr : 0.f;
+        ps += __shfl_xor(ps, 4, 64);
+        ps += __shfl_xor(ps, 8, 64);
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        lrun[gi] = lrun[gi] * c + ps;
+        float a0 = acc[gi][0] * c, a1 = acc[gi][1] * c;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float pk = __shfl(pr, 4 * kk, 64);
+          a0 += pk * v0[kk];
+          a1 += pk * v1[kk];
+        }
+        acc[gi][0] = a0;
+        acc[gi][1] = a1;
+        mrun[gi] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    if (lane == 0) { wm[wv][gi] = mrun[gi]; wl[wv][gi] = lrun[gi]; }
+    wacc[wv][gi][2 * lane] = acc[gi][0];
+    wacc[wv][gi][2 * lane + 1] = acc[gi][1];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * DH; idx += 256) {
+    const int gi = idx / DH, e = idx % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][gi]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float c = safe_scale(wm[w][gi], M);
+      L += wl[w][gi] * c;
+      A += wacc[w][gi][e] * c;
+    }
+    const int hq = g * G + gi;
+    if (splits == 1) {
+      out[((size_t)m * H + hq) * DH + e] = f32_to_bf16(L > 0.f ? A / L : 0.f);
+    } else {
+      const size_t pi = ((size_t)m * H + hq) * splits + sp;
+      part_o[pi * DH + e] = A;
+      if (e == 0) { part_ml[2 * pi] = M; part_ml[2 * pi + 1] = L; }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bf16 flash attention for prefill, d_h = 128
+
+// grid (ceil(M/64), H), 256 threads; wave w owns query rows q0+16w .. +16 of head
+// blockIdx.y. Scores are computed transposed, S^T = K . Q^T, with
+// v_mfma_f32_16x16x32_bf16 (lane l holds S^T[keys 4*(l/16)+v][query l%16]),
+// so the probabilities of query l%16 for the 8 keys {4*(l/16)+v} of two
+// adjacent 16-key pages already sit in lane l in the B-operand layout of
+// O^T = V^T . P^T; the value operand pairs with the same key order, read as
+// 8-byte runs from the transposed value pages. Online softmax per query.
+__global__ void __launch_bounds__(256) k_attn_prefill(const bf16_t* __restrict__ q, const int32_t* __restrict__ rows,
+                                                      const int32_t* __restrict__ ptab, int max_pages,
+                                                      const bf16_t* __restrict__ kv_slot, size_t page_elems, int M,
+                                                      int H, int Hkv, int window, float scale,
+                                                      bf16_t* __restrict__ out) {
+  constexpr int DH = 128;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int hq = blockIdx.y, g = hq / (H / Hkv);
+  const int row0 = blockIdx.x * 64 + wv * 16;
+  if (row0 >= M) return;
+  const int nrow = min(16, M - row0);
+  const int seq = rows[0];
+  const int qi = lane & 15, grp = lane >> 4;
+  const int my_row = row0 + min(qi, nrow - 1);
+  const int qpos = rows[2 * my_row + 1];
+  const int pos_first = rows[2 * row0 + 1];
+  const int pos_last = rows[2 * (row0 + nrow - 1) + 1];
+
+  // Q as the B operand: lane holds Q[query qi][dims 32*ks + 8*grp .. +8]
+  bf16x8_t qb[4];
+  const bf16_t* qrow = q + ((size_t)my_row * H + hq) * DH;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32 + grp * 8);
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  const int klo = window > 0 ? max(0, pos_first - window + 1) : 0;
+  const size_t vofs = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16;
+  for (int kb = klo & ~31; kb <= pos_last; kb += 32) {
+    const bool has1 = kb + 16 <= pos_last;
+    const bf16_t* pg0 = kv_slot + (size_t)ptab[(size_t)seq * max_pages + (kb >> 4)] * page_elems;
+    const bf16_t* pg1 = has1 ? kv_slot + (size_t)ptab[(size_t)seq * max_pages + (kb >> 4) + 1] * page_elems : pg0;
+    // scores S^T for the two pages
+    f32x4_t st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const bf16_t* kr = (t == 0 ? pg0 : pg1) + ((size_t)g * 16 + qi) * DH + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
+        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], st[t], 0, 0, 0);
+      }
+    }
+    // mask + online softmax for query qi (this lane's column)
+    float s[8];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int kp = kb + 16 * t + 4 * grp + v;
+        const bool ok = kp <= qpos && (window <= 0 || kp > qpos - window) && (t == 0 || has1);
+        const float x = ok ? st[t][v] * scale : -INFINITY;
+        s[4 * t + v] = x;
+        mb = fmaxf(mb, x);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(mrun, mb);
+    const float c = safe_scale(mrun, mn);
+    float psum = 0.f;
+    bf16x8_t pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = s[i] == -INFINITY ? 0.f : __expf(s[i] - mn);
+      psum += p;
+      pb[i] = (__bf16)p;
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    lrun = lrun * c + psum;
+    mrun = mn;
+    // O^T += V^T . P^T over 8 dim tiles of 16
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int dim = dt * 16 + qi;
+      const uint2 va = *reinterpret_cast<const uint2*>(pg0 + vofs + (size_t)dim * 16 + 4 * grp);
+      const uint2 vb = has1 ? *reinterpret_cast<const uint2*>(pg1 + vofs + (size_t)dim * 16 + 4 * grp)
+                            : make_uint2(0u, 0u);
+      const uint4 vv = make_uint4(va.x, va.y, vb.x, vb.y);
+      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, vv);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[dt][v] *= c;
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb, acc[dt], 0, 0, 0);
+    }
+  }
+  if (qi >= nrow) return;
+  const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+  bf16_t* orow = out + ((size_t)(row0 + qi) * H + hq) * DH;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(acc[dt][0] * inv) | ((uint32_t)f32_to_bf16(acc[dt][1] * inv) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(acc[dt][2] * inv) | ((uint32_t)f32_to_bf16(acc[dt][3] * inv) << 16);
+    *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * grp) = make_uint2(lo, hi);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -234,7 +585,8 @@ static hipError_t attn_t(const void* q, const int32_t* rows, const int32_t* ptab
 #undef DORY_ATT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge<T>, dim3(M * H), dim3(dh), 0, st, part_ml, part_o, splits, dh, (T*)out);
+  hipLaunchKernelGGL(k_attn_merge<T>, dim3(M * H), dim3(dh < 64 ? 64 : dh), 0, st, part_ml, part_o, splits, dh,
+                     (T*)out);
   return hipGetLastError();
 }
 
@@ -246,6 +598,42 @@ hipError_t launch_attn_rows(int dtype, const void* q, const int32_t* rows, const
                                     out, part_ml, part_o, st)
                     : attn_t<bf16_t>(q, rows, ptab, max_pages, kv, page_elems, M, H, Hkv, dh, window, scale, splits,
                                      out, part_ml, part_o, st);
+}
+
+bool attn_decode_supported(int dtype, int H, int Hkv, int dh) {
+  return dtype == 1 && dh == 128 && H % Hkv == 0 && H / Hkv >= 1 && H / Hkv <= 4;
+}
+
+hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
+                              const float2* rope, void* kv, size_t page_elems, int M, int H, int Hkv, int window,
+                              float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
+                              hipStream_t st) {
+  dim3 grid(M, Hkv, splits);
+#define DORY_DEC(GV)                                                                                                  \
+  hipLaunchKernelGGL(k_attn_decode<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv,      \
+                     page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o)
+  switch (H / Hkv) {
+    case 1: DORY_DEC(1); break;
+    case 2: DORY_DEC(2); break;
+    case 3: DORY_DEC(3); break;
+    case 4: DORY_DEC(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DORY_DEC
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(k_attn_merge<bf16_t>, dim3(M * H), dim3(128), 0, st, part_ml, part_o, splits, 128,
+                     (bf16_t*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
+                               size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
+                               hipStream_t st) {
+  dim3 grid((M + 63) / 64, H);
+  hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
+                     (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out);
+  return hipGetLastError();
 }
 
 }  // namespace dory

@@ -75,105 +75,152 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, c
 
 // ------------------------------------------------------------------ bf16 MFMA
 
-constexpr int MF_BM = 128, MF_BN = 128, MF_BK = 64;
-constexpr int MF_LDA = MF_BK + 8;  // padded LDS row (elements): 144 B rows keep ds_read_b128 conflict-free
+constexpr int MF_BK = 64;
 
 // 32x32x16 bf16 MFMA operand layouts (checked on gfx950):
 //  A: lane l holds A[l%32][8*(l/32) .. +8);  B: lane l holds B^T[l%32][8*(l/32) .. +8)
 //  D: element v of lane l is D[8*(v/4) + 4*(l/32) + v%4][l%32].
-template <bool DUAL>
-__global__ void __launch_bounds__(256) k_gemm_mfma(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
-                                                   void* __restrict__ Cv, int M, int N, int K, int F) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][MF_BM * MF_LDA];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][MF_BN * MF_LDA];
+//
+// Tile BM x BN x 64, 256 threads as 2x2 waves of (BM/2) x (BN/2), TM x TN MFMA
+// tiles of 32x32 per wave. Operands go straight from global memory into LDS
+// (global_load_lds_dwordx4: lane l of a wave instruction fills bytes
+// 16l..16l+15 of a 1 KB LDS block = 8 tile rows of 64 bf16), double-buffered:
+// the next k-tile's loads are in flight while the current one is multiplied.
+// Within a row the eight 16-byte chunks are XOR-swizzled by (row & 7), so the
+// MFMA operand reads (32 rows, one chunk) hit distinct banks.
+// The grid is 1-D; workgroup b runs on XCD b % 8, and tiles are dealt so each
+// XCD walks a contiguous run of weight-column tiles over all row tiles, which
+// keeps every weight tile's re-reads inside one XCD's L2.
+// Dual: the tile's B rows are BN/2 gate rows then the BN/2 matching up rows;
+// gate tile j pairs with up tile j + TN/2 in the same lanes for the epilogue.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory into LDS at lds_block + 16 * lane.
+DORY_DEV void load_lds16(const bf16_t* src, bf16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_block, 16, 0, 0);
+}
+
+template <int BM, int BN, bool DUAL>
+__global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+                                                   void* __restrict__ Cv, int M, int N, int K, int F, int m_tiles,
+                                                   int n_tiles) {
+  constexpr int TM = BM / 64, TN = BN / 64;
+  constexpr int IA = BM / 32, IB = BN / 32;  // 1 KB load instructions per wave per k-tile
+  __shared__ __attribute__((aligned(1024))) bf16_t As[2][BM * MF_BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t Bs[2][BN * MF_BK];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  const int m0 = blockIdx.y * MF_BM;
-  // Plain: tile columns n0..n0+127 of C. Dual: z columns c0..c0+63, B rows
-  // c0.. (gate) in tile rows 0..63 and F+c0.. (up) in tile rows 64..127.
-  const int n0 = DUAL ? blockIdx.x * (MF_BN / 2) : blockIdx.x * MF_BN;
 
-  // global -> register staging: 4 chunks of 16 B per thread for A and for B
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      const int gm = min(m0 + r, M - 1);
-      ra[i] = *reinterpret_cast<const uint4*>(A + (size_t)gm * K + k0 + kc);
-      int gn;
-      if (DUAL) gn = (r < 64) ? min(n0 + r, F - 1) : F + min(n0 + r - 64, F - 1);
-      else gn = min(n0 + r, N - 1);
-      rb[i] = *reinterpret_cast<const uint4*>(B + (size_t)gn * K + k0 + kc);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(&As[buf][r * MF_LDA + kc]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[buf][r * MF_LDA + kc]) = rb[i];
-    }
-  };
+  const int ntiles = m_tiles * n_tiles;
+  const int b = blockIdx.x;
+  int t = b;
+  if ((ntiles & 7) == 0) t = (b & 7) * (ntiles >> 3) + (b >> 3);
+  const int tm = t % m_tiles, tn = t / m_tiles;
+  const int m0 = tm * BM;
+  const int n0 = DUAL ? tn * (BN / 2) : tn * BN;  // first C column (plain) or z column (dual)
 
-  f32x16_t acc[2][2];
+  // this lane's global source rows and swizzled chunk for each load instruction
+  const int lrow = lane >> 3;                  // row within the 8-row block
+  const int lchunk = (lane & 7) ^ lrow;        // logical k-chunk stored at physical slot lane & 7
+  const bf16_t* asrc[IA];
+  const bf16_t* bsrc[IB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IA; ++i) {
+    const int r = (wid * IA + i) * 8 + lrow;
+    asrc[i] = A + (size_t)min(m0 + r, M - 1) * K + lchunk * 8;
+  }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < IB; ++i) {
+    const int r = (wid * IB + i) * 8 + lrow;
+    int gn;
+    if (DUAL) gn = (r < BN / 2) ? min(n0 + r, F - 1) : F + min(n0 + r - BN / 2, F - 1);
+    else gn = min(n0 + r, N - 1);
+    bsrc[i] = B + (size_t)gn * K + lchunk * 8;
+  }
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int arow = wm * 64 + (lane & 31);
-  const int bcol0 = DUAL ? wn * 32 : wn * 64;
-  const int bcol1 = DUAL ? 64 + wn * 32 : wn * 64 + 32;
-  const int kl = (lane >> 5) * 8;
+  // B-tile row of this wave's column tile j
+  int brow[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    if (DUAL) brow[j] = j < TN / 2 ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - TN / 2) * 32;
+    else brow[j] = wn * (BN / 2) + j * 32;
+  }
+  const int arow0 = wm * (BM / 2) + (lane & 31);
+  const int khalf = lane >> 5;
 
   const int nk = K / MF_BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < IA; ++i)
+    load_lds16(asrc[i], &As[0][(wid * IA + i) * 512]);
+#pragma unroll
+  for (int i = 0; i < IB; ++i)
+    load_lds16(bsrc[i], &Bs[0][(wid * IB + i) * 512]);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * MF_BK);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile kt have landed
+    __syncthreads();                // ... and every wave's; stage cur^1 is free again
+    if (kt + 1 < nk) {
+      const int k1 = (kt + 1) * MF_BK;
+#pragma unroll
+      for (int i = 0; i < IA; ++i)
+        load_lds16(asrc[i] + k1, &As[cur ^ 1][(wid * IA + i) * 512]);
+#pragma unroll
+      for (int i = 0; i < IB; ++i)
+        load_lds16(bsrc[i] + k1, &Bs[cur ^ 1][(wid * IB + i) * 512]);
+    }
+    const bf16_t* as = As[cur];
+    const bf16_t* bs = Bs[cur];
 #pragma unroll
     for (int ks = 0; ks < MF_BK / 16; ++ks) {
-      const int kk = ks * 16 + kl;
-      bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&As[cur][arow * MF_LDA + kk]);
-      bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(&As[cur][(arow + 32) * MF_LDA + kk]);
-      bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&Bs[cur][(bcol0 + (lane & 31)) * MF_LDA + kk]);
-      bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&Bs[cur][(bcol1 + (lane & 31)) * MF_LDA + kk]);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+      const int ch = 2 * ks + khalf;  // logical 16-byte chunk of this lane's 8 k values
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = arow0 + i * 32;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&as[r * 64 + ((ch ^ (r & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = brow[j] + (lane & 31);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&bs[r * 64 + ((ch ^ (r & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      sstore(cur ^ 1);
-    }
-    __syncthreads();
   }
 
   const int col = lane & 31;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int gm = m0 + wm * 64 + rt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int gm = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (gm >= M) continue;
       if (DUAL) {
-        const int gc = n0 + wn * 32 + col;
-        if (gc < F) {
-          const float z = silu(acc[rt][0][v]) * acc[rt][1][v];
-          reinterpret_cast<bf16_t*>(Cv)[(size_t)gm * F + gc] = f32_to_bf16(z);
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int gc = n0 + wn * (BN / 4) + j * 32 + col;
+          if (gc < F) {
+            const float z = silu(acc[i][j][v]) * acc[i][j + TN / 2][v];
+            reinterpret_cast<bf16_t*>(Cv)[(size_t)gm * F + gc] = f32_to_bf16(z);
+          }
         }
       } else {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int gn = n0 + wn * 64 + ct * 32 + col;
-          if (gn < N) reinterpret_cast<float*>(Cv)[(size_t)gm * N + gn] = acc[rt][ct][v];
+        for (int j = 0; j < TN; ++j) {
+          const int gn = n0 + wn * (BN / 2) + j * 32 + col;
+          if (gn < N) reinterpret_cast<float*>(Cv)[(size_t)gm * N + gn] = acc[i][j][v];
         }
       }
     }
@@ -274,6 +321,43 @@ static hipError_t gemv_dispatch(const bf16_t* X, const bf16_t* W, void* Y, int M
   }
 }
 
+template <int BM, int BN>
+static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
+                              hipStream_t st) {
+  const int ncols = dual ? F : N;
+  const int cols_per_tile = dual ? BN / 2 : BN;
+  const int mt = (M + BM - 1) / BM, nt = (ncols + cols_per_tile - 1) / cols_per_tile;
+  const dim3 grid(mt * nt);
+  if (dual)
+    hipLaunchKernelGGL((k_gemm_tile<BM, BN, true>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt);
+  else
+    hipLaunchKernelGGL((k_gemm_tile<BM, BN, false>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt);
+  return hipGetLastError();
+}
+
+// Tile shape: the candidate with the least estimated time, counting whole
+// rounds of 256 CUs and a per-shape throughput factor (larger tiles reuse
+// each loaded operand more).
+static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
+                                   hipStream_t st) {
+  const int ncols = dual ? F : N;
+  struct Cand { int bm, bn; double eff; } cands[] = {{256, 256, 1.0}, {256, 128, 0.8}, {128, 128, 0.55}};
+  int best = 2;
+  double best_t = 1e300;
+  for (int i = 0; i < 3; ++i) {
+    const int cpt = dual ? cands[i].bn / 2 : cands[i].bn;
+    const long tiles = (long)((M + cands[i].bm - 1) / cands[i].bm) * ((ncols + cpt - 1) / cpt);
+    const double rounds = (double)((tiles + 255) / 256);
+    const double t = rounds * cands[i].bm * cands[i].bn / cands[i].eff;
+    if (t < best_t * 0.999) { best_t = t; best = i; }
+  }
+  switch (best) {
+    case 0: return tile_launch<256, 256>(A, B, out, M, N, K, F, dual, st);
+    case 1: return tile_launch<256, 128>(A, B, out, M, N, K, F, dual, st);
+    default: return tile_launch<128, 128>(A, B, out, M, N, K, F, dual, st);
+  }
+}
+
 bool gemv_supported(int K) { return K == 1024 || K == 3072 || K == 4096 || K == 8192; }
 
 // out: fp32 [M,N] (plain) or storage-type z [M,F] (dual, N = 2F).
@@ -297,13 +381,7 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     return dual ? gemv_dispatch<true>((const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F, st)
                 : gemv_dispatch<false>((const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F, st);
   }
-  const int ncols = dual ? F : N;
-  dim3 grid((ncols + (dual ? MF_BN / 2 : MF_BN) - 1) / (dual ? MF_BN / 2 : MF_BN), (M + MF_BM - 1) / MF_BM);
-  if (dual)
-    hipLaunchKernelGGL(k_gemm_mfma<true>, grid, dim3(256), 0, st, (const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F);
-  else
-    hipLaunchKernelGGL(k_gemm_mfma<false>, grid, dim3(256), 0, st, (const bf16_t*)A, (const bf16_t*)B, out, M, N, K, 0);
-  return hipGetLastError();
+  return launch_tile_gemm((const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F, dual, st);
 }
 
 }  // namespace dory

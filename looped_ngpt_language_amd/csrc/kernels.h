@@ -25,6 +25,15 @@ hipError_t launch_attn_rows(int dtype, const void* q, const int32_t* rows, const
                             const void* kv, size_t page_elems, int M, int H, int Hkv, int dh, int window,
                             float scale, int splits, void* out, float* part_ml, float* part_o, hipStream_t st);
 
+bool attn_decode_supported(int dtype, int H, int Hkv, int dh);
+hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
+                              const float2* rope, void* kv, size_t page_elems, int M, int H, int Hkv, int window,
+                              float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
+                              hipStream_t st);
+hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
+                               size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
+                               hipStream_t st);
+
 bool gemv_supported(int K);
 hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
                        hipStream_t st);

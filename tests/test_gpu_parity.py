@@ -110,7 +110,7 @@ def test_tiny_fp32_all_rows_and_chunks(tiny):
 @pytest.fixture(scope="module")
 def mid():
     w = synth.make_weights(synth.MID, seed=0)
-    gpu = dory.Model(synth.MID, w, kv_mode="per_loop", max_loops=4, max_seqs=2, max_model_len=1024, max_tokens=1024)
+    gpu = dory.Model(synth.MID, w, kv_mode="per_loop", max_loops=4, max_seqs=2, max_model_len=1280, max_tokens=1024)
     return w, gpu
 
 
@@ -150,3 +150,26 @@ def test_mid_bf16_end_to_end(mid, mode, k):
     o_ids, o_lg, o_h = oracle_greedy(synth.MID, w, mode, k, prompt, n_dec)
     g_ids, g_lg, g_h = run_gpu_greedy(m, 0, prompt, n_dec, teacher=o_ids)
     bf16_check(f"mid k={k} {mode}", g_ids, g_lg, g_h, o_ids, o_lg, o_h)
+
+
+def test_mid_bf16_sliding_window_and_chunks(mid):
+    """W = 1024 binds (1200-token prompt); per-loop prompt in ragged chunks through the
+    short-chunk attention path (rows <= 16) and the flash path, checked against the oracle."""
+    w, m = mid
+    say("[mid bf16] window binds: 1200-token prompt, k=1, chunks 700 + 1 + 5 + 16 + 17 + 461")
+    for s in range(2):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    m.set_kv_mode("per_loop")
+    m.set_loops(1)
+    prompt = synth.prompt_tokens(synth.MID, 1200)
+    om = OracleModel(synth.MID, w, "per_loop", 1)
+    olg, oids = om.prefill(0, prompt, 1)
+    bounds = [0, 700, 701, 706, 722, 739, 1200]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        l2, i2 = m.prefill(0, prompt[a:b], 1)
+    err = float(np.max(np.abs(l2.cpu().numpy() - olg)))
+    h = m.last_hidden(1)[0].cpu().numpy()
+    err_h = float(np.max(np.abs(h - om.last_hidden[-1])))
+    say(f"  chunked 1200-token prompt: logits max-abs {err:.3e}, hidden {err_h:.3e}, id {int(i2[0])} vs {int(oids[0])}")
+    assert err <= 5e-2 and err_h <= 3e-2
