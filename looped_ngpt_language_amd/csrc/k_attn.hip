@@ -16,11 +16,16 @@
 // KV pool layout: slot-major; a page slot holds 16 tokens of one layer slot,
 // keys row-major and values transposed so both attention products load
 // contiguous 16-byte operands:
-//   K: [H_kv][16 tokens][d_h]     V^T: [H_kv][d_h][16 tokens]
+//   K: [H_kv][16 tokens][d_h]     V^T: [H_kv][d_h][16 tokens, order vperm]
+// Within a value row, token t sits at vperm(t) = t with bits 2 and 3 swapped
+// (0-3, 8-11, 4-7, 12-15): the 8 tokens {4h..4h+3, 8+4h..8+4h+3} that one
+// lane's share of a 32x32 score tile covers are then 16 contiguous bytes.
 #include "common.h"
 #include "kernels.h"
 
 namespace dory {
+
+DORY_DEV constexpr int vperm(int t) { return (t & 3) | ((t >> 3) & 1) << 2 | ((t >> 2) & 1) << 3; }
 
 DORY_DEV float safe_scale(float m_old, float m_new) { return m_old == -INFINITY ? 0.f : __expf(m_old - m_new); }
 
@@ -60,7 +65,7 @@ __global__ void __launch_bounds__(64) k_rope_qk_kv(const float* __restrict__ qkv
   const int g = hd - H, tok = pos & 15;
   const int page = ptab[(size_t)seq * max_pages + (pos >> 4)];
   T* kp = kv_slot + (size_t)page * page_elems + ((size_t)g * 16 + tok) * dh;
-  T* vt = kv_slot + (size_t)page * page_elems + (size_t)Hkv * 16 * dh + (size_t)g * dh * 16 + tok;
+  T* vt = kv_slot + (size_t)page * page_elems + (size_t)Hkv * 16 * dh + (size_t)g * dh * 16 + vperm(tok);
   const float* vsrc = src + (size_t)Hkv * dh;
   if (act) {
     St<T>::st(kp, lane, a0 * r);
@@ -122,7 +127,7 @@ __global__ void __launch_bounds__(ATT_THREADS) k_attn_rows(
     const T* pg = kv_slot + (size_t)page * page_elems;
     float kf[8], vf[8];
     load8(pg + ((size_t)g * 16 + (j & 15)) * DH + e0, kf);
-    const T* vt = pg + (size_t)Hkv * 16 * DH + ((size_t)g * DH + e0) * 16 + (j & 15);
+    const T* vt = pg + (size_t)Hkv * 16 * DH + ((size_t)g * DH + e0) * 16 + vperm(j & 15);
 #pragma unroll
     for (int e = 0; e < 8; ++e) vf[e] = St<T>::ld(vt, (size_t)e * 16);
 #pragma unroll
@@ -293,7 +298,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(
     } else {
       const float* v = src + (size_t)(H + Hkv + g) * DH;
       const bf16_t v0 = f32_to_bf16(v[lane]), v1 = f32_to_bf16(v[lane + 64]);
-      bf16_t* vt = pg + (size_t)Hkv * 16 * DH + (size_t)g * DH * 16 + tok;
+      bf16_t* vt = pg + (size_t)Hkv * 16 * DH + (size_t)g * DH * 16 + vperm(tok);
       vt[(size_t)lane * 16] = v0;
       vt[(size_t)(lane + 64) * 16] = v1;
       vnew[lane] = bf16_to_f32(v0);
@@ -344,7 +349,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(
           kf[8 * i + 2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
         }
       }
-      // value rows 2*lane (vr[0..1]) and 2*lane+1 (vr[2..3]), 16 keys each
+      // value rows 2*lane (vr[0..1]) and 2*lane+1 (vr[2..3]), 16 keys each in vperm order
       float v0[16], v1[16];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -372,10 +377,11 @@ __global__ void __launch_bounds__(256) k_attn_decode(
           for (int i = 0; i < 32; ++i) kf[i] = knew[db * 32 + i];
         }
         const float n0 = vnew[2 * lane], n1 = vnew[2 * lane + 1];
+        const int ptok = vperm(tok);
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          v0[kk] = kk == tok ? n0 : v0[kk];
-          v1[kk] = kk == tok ? n1 : v1[kk];
+          v0[kk] = kk == ptok ? n0 : v0[kk];
+          v1[kk] = kk == ptok ? n1 : v1[kk];
         }
       }
 #pragma unroll
@@ -402,8 +408,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(
         lrun[gi] = lrun[gi] * c + ps;
         float a0 = acc[gi][0] * c, a1 = acc[gi][1] * c;
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const float pk = __shfl(pr, 4 * kk, 64);
+        for (int kk = 0; kk < 16; ++kk) {  // v0/v1[kk] hold token vperm(kk)
+          const float pk = __shfl(pr, 4 * vperm(kk), 64);
           a0 += pk * v0[kk];
           a1 += pk * v1[kk];
         }
@@ -445,112 +451,159 @@ __global__ void __launch_bounds__(256) k_attn_decode(
 
 // ---------------------------------------------------------------- bf16 flash attention for prefill, d_h = 128
 
-// grid (ceil(M/64), H), 256 threads; wave w owns query rows q0+16w .. +16 of head
-// blockIdx.y. Scores are computed transposed, S^T = K . Q^T, with
-// v_mfma_f32_16x16x32_bf16 (lane l holds S^T[keys 4*(l/16)+v][query l%16]),
-// so the probabilities of query l%16 for the 8 keys {4*(l/16)+v} of two
-// adjacent 16-key pages already sit in lane l in the B-operand layout of
-// O^T = V^T . P^T; the value operand pairs with the same key order, read as
-// 8-byte runs from the transposed value pages. Online softmax per query.
+typedef __attribute__((address_space(3))) void lds_void_t;
+DORY_DEV void load_lds16(const bf16_t* src, bf16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_block, 16, 0, 0);
+}
+
+// grid (ceil(M/128), H), 256 threads; wave w owns query rows q0+32w .. +32 of
+// head blockIdx.y (one sequence: a prefill chunk). Keys go through LDS in
+// blocks of 64 (4 pages), double-buffered with direct global->LDS loads and
+// shared by the four waves. Scores are computed transposed with
+// v_mfma_f32_32x32x16_bf16, S^T = K . Q^T: lane l holds, for query l%32, the
+// keys 8j + 4(l/32) + i (v = 4j + i) of a 32-key half-block; its
+// probabilities for one page (j = 0,1 or 2,3) form the P^T operand of
+// O^T = V^T . P^T as they are, and the matching value operand is the
+// contiguous 16 bytes at vperm position 8(l/32) of each value row.
+// LDS: K [64 keys][16 chunks of 8 dims], chunk c of key k stored at c ^ (k & 7);
+// V^T [4 pages][128 dims][2 halves], half h of dim d stored at h ^ ((d >> 2) & 1).
 __global__ void __launch_bounds__(256) k_attn_prefill(const bf16_t* __restrict__ q, const int32_t* __restrict__ rows,
                                                       const int32_t* __restrict__ ptab, int max_pages,
                                                       const bf16_t* __restrict__ kv_slot, size_t page_elems, int M,
                                                       int H, int Hkv, int window, float scale,
                                                       bf16_t* __restrict__ out) {
-  constexpr int DH = 128;
+  constexpr int DH = 128, KB = 64;
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][KB * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs[2][KB * DH];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int hq = blockIdx.y, g = hq / (H / Hkv);
-  const int row0 = blockIdx.x * 64 + wv * 16;
-  if (row0 >= M) return;
-  const int nrow = min(16, M - row0);
+  const int wrow0 = blockIdx.x * 128;
+  const int row0 = wrow0 + wv * 32;
+  const int nrow = max(0, min(32, M - row0));
   const int seq = rows[0];
-  const int qi = lane & 15, grp = lane >> 4;
-  const int my_row = row0 + min(qi, nrow - 1);
+  const int qi = lane & 31, hh = lane >> 5;
+  const int my_row = nrow > 0 ? row0 + min(qi, nrow - 1) : wrow0;
   const int qpos = rows[2 * my_row + 1];
-  const int pos_first = rows[2 * row0 + 1];
-  const int pos_last = rows[2 * (row0 + nrow - 1) + 1];
+  const int wg_first = rows[2 * wrow0 + 1];
+  const int wg_last = rows[2 * (min(wrow0 + 127, M - 1)) + 1];
+  const int pos_first = nrow > 0 ? rows[2 * row0 + 1] : 0;
+  const int pos_last = nrow > 0 ? rows[2 * (row0 + nrow - 1) + 1] : -1;
+  const int32_t* prow = ptab + (size_t)seq * max_pages;
+  const int last_page = wg_last >> 4;
 
-  // Q as the B operand: lane holds Q[query qi][dims 32*ks + 8*grp .. +8]
-  bf16x8_t qb[4];
+  // Q as the B operand of S^T: lane holds Q[query qi][dims 16ks + 8hh .. +8]
+  bf16x8_t qb[8];
   const bf16_t* qrow = q + ((size_t)my_row * H + hq) * DH;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32 + grp * 8);
+  for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16 + hh * 8);
 
-  f32x4_t acc[8];
+  f32x16_t acc[4];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
 
-  const int klo = window > 0 ? max(0, pos_first - window + 1) : 0;
-  const size_t vofs = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16;
-  for (int kb = klo & ~31; kb <= pos_last; kb += 32) {
-    const bool has1 = kb + 16 <= pos_last;
-    const bf16_t* pg0 = kv_slot + (size_t)ptab[(size_t)seq * max_pages + (kb >> 4)] * page_elems;
-    const bf16_t* pg1 = has1 ? kv_slot + (size_t)ptab[(size_t)seq * max_pages + (kb >> 4) + 1] * page_elems : pg0;
-    // scores S^T for the two pages
-    f32x4_t st[2];
+  // per-lane source offsets of this wave's four 1 KB load instructions (K and V^T)
+  const int kkey_lo = lane >> 4;                 // key within a 4-key quarter
+  const int kslot = lane & 15;
+  const int vdim_lo = lane >> 1;                 // dim within a 32-dim quarter
+  const int vslot = lane & 1;
+  auto issue = [&](int kb, int stage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = wv * 4 + i;                 // 0..15: page ci/4, quarter ci%4
+      const int pi = ci >> 2, qt = ci & 3;
+      const int pidx = min((kb >> 4) + pi, last_page);
+      const bf16_t* pg = kv_slot + (size_t)prow[pidx] * page_elems;
+      const int key = qt * 4 + kkey_lo;
+      const int lc = kslot ^ (key & 7);
+      load_lds16(pg + ((size_t)g * 16 + key) * DH + lc * 8, &Ks[stage][(pi * 16 + qt * 4) * DH]);
+      const int dim = qt * 32 + vdim_lo;
+      const int lh = vslot ^ ((dim >> 2) & 1);
+      load_lds16(pg + (size_t)Hkv * 16 * DH + ((size_t)g * DH + dim) * 16 + lh * 8,
+                 &Vs[stage][(pi * DH + qt * 32) * 16]);
+    }
+  };
+
+  const int klo = window > 0 ? max(0, wg_first - window + 1) : 0;
+  const int wlo = window > 0 ? max(0, pos_first - window + 1) : 0;
+  const int kstart = klo & ~(KB - 1);
+  issue(kstart, 0);
+  int stage = 0;
+  for (int kb = kstart; kb <= wg_last; kb += KB, stage ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kb + KB <= wg_last) issue(kb + KB, stage ^ 1);
+    if (nrow == 0 || kb > pos_last || kb + KB <= wlo) continue;
+    const bf16_t* ks_ = Ks[stage];
+    const bf16_t* vs_ = Vs[stage];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const bf16_t* kr = (t == 0 ? pg0 : pg1) + ((size_t)g * 16 + qi) * DH + grp * 8;
+      const int k0 = kb + 32 * t;
+      if (k0 > pos_last || k0 + 32 <= wlo) continue;
+      f32x16_t st;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kr + ks * 32);
-        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], st[t], 0, 0, 0);
+      for (int v = 0; v < 16; ++v) st[v] = 0.f;
+      const int key = 32 * t + qi;               // A operand row: key of the block
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int ch = (2 * ks + hh) ^ (key & 7);
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks_ + key * DH + ch * 8);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], st, 0, 0, 0);
       }
-    }
-    // mask + online softmax for query qi (this lane's column)
-    float s[8];
-    float mb = -INFINITY;
+      float sv[16];
+      float mb = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int kp = kb + 16 * t + 4 * grp + v;
-        const bool ok = kp <= qpos && (window <= 0 || kp > qpos - window) && (t == 0 || has1);
-        const float x = ok ? st[t][v] * scale : -INFINITY;
-        s[4 * t + v] = x;
-        mb = fmaxf(mb, x);
+      for (int v = 0; v < 16; ++v) {
+        const int kp = k0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const bool ok = kp <= qpos && (window <= 0 || kp > qpos - window);
+        sv[v] = ok ? st[v] * scale : -INFINITY;
+        mb = fmaxf(mb, sv[v]);
       }
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float mn = fmaxf(mrun, mb);
-    const float c = safe_scale(mrun, mn);
-    float psum = 0.f;
-    bf16x8_t pb;
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const float mn = fmaxf(mrun, mb);
+      const float c = safe_scale(mrun, mn);
+      float psum = 0.f;
+      bf16x8_t pb[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = s[i] == -INFINITY ? 0.f : __expf(s[i] - mn);
-      psum += p;
-      pb[i] = (__bf16)p;
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    lrun = lrun * c + psum;
-    mrun = mn;
-    // O^T += V^T . P^T over 8 dim tiles of 16
+      for (int v = 0; v < 16; ++v) {
+        const float p = sv[v] == -INFINITY ? 0.f : __expf(sv[v] - mn);
+        psum += p;
+        pb[v >> 3][v & 7] = (__bf16)p;
+      }
+      psum += __shfl_xor(psum, 32, 64);
+      lrun = lrun * c + psum;
+      mrun = mn;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int dim = dt * 16 + qi;
-      const uint2 va = *reinterpret_cast<const uint2*>(pg0 + vofs + (size_t)dim * 16 + 4 * grp);
-      const uint2 vb = has1 ? *reinterpret_cast<const uint2*>(pg1 + vofs + (size_t)dim * 16 + 4 * grp)
-                            : make_uint2(0u, 0u);
-      const uint4 vv = make_uint4(va.x, va.y, vb.x, vb.y);
-      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, vv);
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[dt][v] *= c;
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb, acc[dt], 0, 0, 0);
+        for (int v = 0; v < 16; ++v) acc[dt][v] *= c;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int page = 2 * t + pp;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int dim = dt * 32 + qi;
+          const int half = hh ^ ((dim >> 2) & 1);
+          const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vs_ + (page * DH + dim) * 16 + half * 8);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[pp], acc[dt], 0, 0, 0);
+        }
+      }
     }
   }
   if (qi >= nrow) return;
   const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
   bf16_t* orow = out + ((size_t)(row0 + qi) * H + hq) * DH;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const uint32_t lo = (uint32_t)f32_to_bf16(acc[dt][0] * inv) | ((uint32_t)f32_to_bf16(acc[dt][1] * inv) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(acc[dt][2] * inv) | ((uint32_t)f32_to_bf16(acc[dt][3] * inv) << 16);
-    *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * grp) = make_uint2(lo, hi);
-  }
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = dt * 32 + 8 * j + 4 * hh;
+      const uint32_t lo = (uint32_t)f32_to_bf16(acc[dt][4 * j] * inv) | ((uint32_t)f32_to_bf16(acc[dt][4 * j + 1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(acc[dt][4 * j + 2] * inv) | ((uint32_t)f32_to_bf16(acc[dt][4 * j + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + d0) = make_uint2(lo, hi);
+    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -630,7 +683,7 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
 hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
                                hipStream_t st) {
-  dim3 grid((M + 63) / 64, H);
+  dim3 grid((M + 127) / 128, H);
   hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
                      (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out);
   return hipGetLastError();
