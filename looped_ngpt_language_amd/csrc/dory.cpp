@@ -33,7 +33,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {  // byte offsets inside the workspace
-  size_t rope, ptab, upload, err, buf[3], y, hb, qkv, q, o, z, part_ml, part_o, logits, spec, total;
+  size_t rope, ptab, upload, err, buf[4], y, hb, qkv, q, o, z, part_ml, part_o, logits, spec, total;
   int max_pages;       // pages per sequence
   int upload_ints;     // capacity of the upload area in int32
   int part_rows;       // rows that may use split attention
@@ -57,7 +57,7 @@ Layout make_layout(const dory_config& c) {
   L.ptab = take((size_t)c.max_seqs * L.max_pages * 4);
   L.upload = take((size_t)L.upload_ints * 4);
   L.err = take(kAlign);
-  for (int i = 0; i < 3; ++i) L.buf[i] = take(M * d * 4);
+  for (int i = 0; i < 4; ++i) L.buf[i] = take(M * d * 4);
   L.y = take(M * d * 4);
   L.hb = take(M * d * es);
   L.qkv = take(M * qkv_cols(c) * 4);
@@ -305,8 +305,39 @@ struct Geom {
   }
 };
 
-// One block application on M rows held in h / hb.
-void run_block(dory_ctx* c, int j, int t, int M, float* h, bool decode, const Geom& geo) {
+// Residual-stream bookkeeping of one forward pass. With a pending step
+// (py != nullptr) the hidden rows are N(h + pa * (N(py) - h)), not yet
+// materialised: the next weight-streaming GEMV applies it in its prologue
+// (writing the result to `spare`, which then becomes h) or flush() runs it.
+struct Flow {
+  float* h;
+  float* spare;
+  const float* py = nullptr;
+  const float* pa = nullptr;
+};
+
+void flush(dory_ctx* c, Flow& f, int M) {
+  if (!f.py) return;
+  const dory_config& g = c->cfg;
+  if (!c->dry) {
+    Span sp(c, R_RESID, (double)M * g.d_model * (12 + esize(g)) + 4.0 * g.d_model, 0);
+    ok(c, dory::launch_residual(g.dtype, f.h, f.py, f.pa, c->W(c->L.hb), M, g.d_model, c->stream));
+  } else {
+    c->stats.kernel_launches++;
+  }
+  f.py = f.pa = nullptr;
+}
+
+// Decode rows few enough for the weight-streaming GEMV with the residual step
+// folded into its prologue.
+bool fused_residual_ok(const dory_ctx* c, int M, bool decode) {
+  const dory_config& g = c->cfg;
+  return decode && M <= 2 && g.dtype == DORY_BF16 && dory::gemv_residual_supported(g.d_model) &&
+         dory::gemv_supported(g.n_heads * g.head_dim) && dory::gemv_supported(g.d_ff);
+}
+
+// One block application on M rows (hidden state per Flow; storage copy in hb when materialised).
+void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geom& geo) {
   using namespace dory;
   const dory_config& g = c->cfg;
   const int dt = g.dtype, d = g.d_model, H = g.n_heads, Hk = g.n_kv_heads, dh = g.head_dim;
@@ -324,8 +355,10 @@ void run_block(dory_ctx* c, int j, int t, int M, float* h, bool decode, const Ge
   const bool fused_decode = decode && paged;
   const bool flash = !decode && dt == DORY_BF16 && dh == 128 && M > c->L.part_rows;
   const int splits = flash ? 1 : choose_splits(c, M, keys_max, paged);
+  const bool fres = fused_residual_ok(c, M, decode);
   if (c->dry) {
-    c->stats.kernel_launches += 6 + (fused_decode ? 1 : 2) + (!paged && !flash && splits > 1);
+    c->stats.kernel_launches += (fres ? 4 : 6) + (fused_decode ? 1 : 2) + (splits > 1);
+    if (fres) { f.py = f.pa = nullptr; }
     return;
   }
   void* hb = c->W(c->L.hb);
@@ -335,7 +368,13 @@ void run_block(dory_ctx* c, int j, int t, int M, float* h, bool decode, const Ge
   const int32_t* ptab = c->W<int32_t>(c->L.ptab);
   char* kv = c->pool + (size_t)slot_of(c, j, t) * c->pages_total * c->page_bytes;
   hipStream_t st = c->stream;
-  {
+  if (f.py && fres) {
+    Span sp(c, R_QKV, (double)nq * d * es + Md * d * 12 + 4.0 * d + Md * nq * 4, 2.0 * Md * nq * d);
+    ok(c, launch_gemv_residual(false, c->wqkv[j], qkv, M, nq, d, f.h, f.py, f.pa, f.spare, st));
+    std::swap(f.h, f.spare);
+    f.py = f.pa = nullptr;
+  } else {
+    flush(c, f, M);
     Span sp(c, R_QKV, (double)nq * d * es + Md * d * es + Md * nq * 4, 2.0 * Md * nq * d);
     ok(c, launch_gemm(dt, false, hb, c->wqkv[j], qkv, M, nq, d, st));
   }
@@ -367,11 +406,15 @@ void run_block(dory_ctx* c, int j, int t, int M, float* h, bool decode, const Ge
     Span sp(c, R_OPROJ, (double)d * hd * es + Md * hd * es + Md * d * 4, 2.0 * Md * d * hd);
     ok(c, launch_gemm(dt, false, c->W(c->L.o), c->wo[j], y, M, d, hd, st));
   }
-  {
-    Span sp(c, R_RESID, resid_bytes, 0);
-    ok(c, launch_residual(dt, h, y, c->aa[j], hb, M, d, st));
-  }
-  {
+  if (fres) {
+    Span sp(c, R_GU, 2.0 * F * d * es + Md * d * 12 + 4.0 * d + Md * F * es, 2.0 * Md * 2 * F * d);
+    ok(c, launch_gemv_residual(true, c->wgu[j], c->W(c->L.z), M, 2 * F, d, f.h, y, c->aa[j], f.spare, st));
+    std::swap(f.h, f.spare);
+  } else {
+    {
+      Span sp(c, R_RESID, resid_bytes, 0);
+      ok(c, launch_residual(dt, f.h, y, c->aa[j], hb, M, d, st));
+    }
     Span sp(c, R_GU, 2.0 * F * d * es + Md * d * es + Md * F * es, 2.0 * Md * 2 * F * d);
     ok(c, launch_gemm(dt, true, hb, c->wgu[j], c->W(c->L.z), M, 2 * F, d, st));
   }
@@ -379,9 +422,12 @@ void run_block(dory_ctx* c, int j, int t, int M, float* h, bool decode, const Ge
     Span sp(c, R_DOWN, (double)d * F * es + Md * F * es + Md * d * 4, 2.0 * Md * d * F);
     ok(c, launch_gemm(dt, false, c->W(c->L.z), c->wd[j], y, M, d, F, st));
   }
-  {
+  if (fres) {
+    f.py = y;
+    f.pa = c->am[j];
+  } else {
     Span sp(c, R_RESID, resid_bytes, 0);
-    ok(c, launch_residual(dt, h, y, c->am[j], hb, M, d, st));
+    ok(c, launch_residual(dt, f.h, y, c->am[j], hb, M, d, st));
   }
 }
 
@@ -392,7 +438,8 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, con
   const dory_config& g = c->cfg;
   const int dt = g.dtype, d = g.d_model;
   const double es = (double)esize(g), Md = (double)M;
-  float* b[3] = {c->W<float>(c->L.buf[0]), c->W<float>(c->L.buf[1]), c->W<float>(c->L.buf[2])};
+  float* b[4] = {c->W<float>(c->L.buf[0]), c->W<float>(c->L.buf[1]), c->W<float>(c->L.buf[2]),
+                 c->W<float>(c->L.buf[3])};
   void* hb = c->W(c->L.hb);
   if (!c->dry) {
     Span sp(c, R_EMBED, Md * d * (2 * es + 4) + Md * 4, 0);
@@ -400,27 +447,38 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, con
   } else {
     c->stats.kernel_launches++;
   }
-  for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, b[0], decode, geo);
-  float *x = b[0], *h = b[1], *s = b[2];
+  Flow f{b[0], b[3]};
+  for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, f, decode, geo);
+  flush(c, f, M);
+  // x = input-stack output; the other three buffers hold h, s and the spare
+  float* x = f.h;
+  float* rest[3];
+  int nr = 0;
+  for (float* p : b)
+    if (p != x) rest[nr++] = p;
+  float* s = rest[1];
+  f = Flow{rest[0], rest[2]};
   for (int t = 1; t <= c->k; ++t) {
     // u_t = N(s_{t-1} + x), with s_0 = x
     if (!c->dry) {
       Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
-      ok(c, launch_norm_sum(dt, t == 1 ? x : s, x, h, nullptr, hb, M, d, c->stream));
+      ok(c, launch_norm_sum(dt, t == 1 ? x : s, x, f.h, nullptr, hb, M, d, c->stream));
     } else {
       c->stats.kernel_launches++;
     }
-    for (int j = g.n_in; j < g.n_in + g.n_rec; ++j) run_block(c, j, t, M, h, decode, geo);
+    for (int j = g.n_in; j < g.n_in + g.n_rec; ++j) run_block(c, j, t, M, f, decode, geo);
+    flush(c, f, M);
     // s_t = N(F(u_t)); h continues as s_t
     if (!c->dry) {
       Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
-      ok(c, launch_norm_sum(dt, h, nullptr, h, s, hb, M, d, c->stream));
+      ok(c, launch_norm_sum(dt, f.h, nullptr, f.h, s, hb, M, d, c->stream));
     } else {
       c->stats.kernel_launches++;
     }
   }
-  for (int j = g.n_in + g.n_rec; j < c->n_blocks; ++j) run_block(c, j, 1, M, h, decode, geo);
-  c->last_h = h;
+  for (int j = g.n_in + g.n_rec; j < c->n_blocks; ++j) run_block(c, j, 1, M, f, decode, geo);
+  flush(c, f, M);
+  c->last_h = f.h;
   c->last_rows = M;
 }
 

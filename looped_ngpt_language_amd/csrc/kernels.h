@@ -35,6 +35,11 @@ hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t
                                hipStream_t st);
 
 bool gemv_supported(int K);
+bool gemv_residual_supported(int K);
+// GEMV (M <= 2) whose input rows are N(h + alpha (N(y) - h)), computed in the prologue; the fp32
+// result is also written to hout (which must not alias h or y).
+hipError_t launch_gemv_residual(bool dual, const void* W, void* out, int M, int N, int K, const float* h,
+                                const float* y, const float* alpha, float* hout, hipStream_t st);
 hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
                        hipStream_t st);
 
