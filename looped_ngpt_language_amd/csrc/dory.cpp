@@ -23,6 +23,10 @@
 
 #include "kernels.h"
 
+namespace dory {
+thread_local LaunchEvents g_launch_events = {nullptr, nullptr};
+}
+
 namespace {
 
 constexpr int kPage = 16;
@@ -214,26 +218,25 @@ hipEvent_t next_event(dory_ctx* c) {
 }
 
 // Accounts one launch of `role` (algorithmic bytes / flops) and, while timing
-// is enabled, brackets it with a HIP event pair on the context's stream.
+// is enabled, has the role's kernel dispatches record a HIP event pair at
+// their start and end (hipExtLaunchKernelGGL), so the time excludes launch gaps.
 struct Span {
   dory_ctx* c;
   int role;
-  hipEvent_t a = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
   Span(dory_ctx* cc, int r, double bytes, double flops) : c(cc), role(r) {
     c->acc[r].launches++;
     c->acc[r].bytes += bytes;
     c->acc[r].flops += flops;
     if (c->timing && !c->dry) {
       a = next_event(c);
-      if (a) (void)hipEventRecord(a, c->stream);
+      b = next_event(c);
+      if (a && b) dory::g_launch_events = {a, b};
     }
   }
   ~Span() {
-    if (!a) return;
-    hipEvent_t b = next_event(c);
-    if (!b) return;
-    (void)hipEventRecord(b, c->stream);
-    c->recs.push_back({role, a, b});
+    dory::g_launch_events = {nullptr, nullptr};
+    if (a && b) c->recs.push_back({role, a, b});
   }
 };
 

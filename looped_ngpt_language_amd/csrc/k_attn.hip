@@ -613,10 +613,10 @@ hipError_t launch_rope_qk_kv(int dtype, const float* qkv, const int32_t* rows, c
                              size_t page_elems, hipStream_t st) {
   dim3 grid(M, H + Hkv);
   if (dtype == 0)
-    hipLaunchKernelGGL(k_rope_qk_kv<float>, grid, dim3(64), 0, st, qkv, rows, ptab, max_pages, rope,
+    DORY_LAUNCH(k_rope_qk_kv<float>, grid, dim3(64), 0, st, qkv, rows, ptab, max_pages, rope,
                        (float*)q_out, (float*)kv_slot, H, Hkv, dh, page_elems);
   else
-    hipLaunchKernelGGL(k_rope_qk_kv<bf16_t>, grid, dim3(64), 0, st, qkv, rows, ptab, max_pages, rope,
+    DORY_LAUNCH(k_rope_qk_kv<bf16_t>, grid, dim3(64), 0, st, qkv, rows, ptab, max_pages, rope,
                        (bf16_t*)q_out, (bf16_t*)kv_slot, H, Hkv, dh, page_elems);
   return hipGetLastError();
 }
@@ -627,7 +627,7 @@ static hipError_t attn_t(const void* q, const int32_t* rows, const int32_t* ptab
                          void* out, float* part_ml, float* part_o, hipStream_t st) {
   dim3 grid(M, Hkv, splits);
 #define DORY_ATT(DHV)                                                                                         \
-  hipLaunchKernelGGL((k_attn_rows<T, DHV>), grid, dim3(ATT_THREADS), 0, st, (const T*)q, rows, ptab, max_pages, \
+  DORY_LAUNCH((k_attn_rows<T, DHV>), grid, dim3(ATT_THREADS), 0, st, (const T*)q, rows, ptab, max_pages, \
                      (const T*)kv, page_elems, H, Hkv, window, scale, splits, (T*)out, part_ml, part_o)
   switch (dh) {
     case 32: DORY_ATT(32); break;
@@ -638,7 +638,7 @@ static hipError_t attn_t(const void* q, const int32_t* rows, const int32_t* ptab
 #undef DORY_ATT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge<T>, dim3(M * H), dim3(dh < 64 ? 64 : dh), 0, st, part_ml, part_o, splits, dh,
+  DORY_LAUNCH(k_attn_merge<T>, dim3(M * H), dim3(dh < 64 ? 64 : dh), 0, st, part_ml, part_o, splits, dh,
                      (T*)out);
   return hipGetLastError();
 }
@@ -663,7 +663,7 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
                               hipStream_t st) {
   dim3 grid(M, Hkv, splits);
 #define DORY_DEC(GV)                                                                                                  \
-  hipLaunchKernelGGL(k_attn_decode<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv,      \
+  DORY_LAUNCH(k_attn_decode<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv,      \
                      page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o)
   switch (H / Hkv) {
     case 1: DORY_DEC(1); break;
@@ -675,7 +675,7 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
 #undef DORY_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge<bf16_t>, dim3(M * H), dim3(128), 0, st, part_ml, part_o, splits, 128,
+  DORY_LAUNCH(k_attn_merge<bf16_t>, dim3(M * H), dim3(128), 0, st, part_ml, part_o, splits, 128,
                      (bf16_t*)out);
   return hipGetLastError();
 }
@@ -684,7 +684,7 @@ hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
                                hipStream_t st) {
   dim3 grid((M + 127) / 128, H);
-  hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
+  DORY_LAUNCH(k_attn_prefill, grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
                      (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out);
   return hipGetLastError();
 }

@@ -360,10 +360,10 @@ static hipError_t gemv_k(const bf16_t* X, const bf16_t* W, void* Y, int M, int N
   const int waves = (rows_out + R - 1) / R;
   const dim3 grid((waves + 3) / 4);
   if (M == 1)
-    hipLaunchKernelGGL((k_gemv_bf16<KCH, R, 1, DUAL, RES>), grid, dim3(256), 0, st, X, W, Y, M, N, F, ra.h, ra.y,
+    DORY_LAUNCH((k_gemv_bf16<KCH, R, 1, DUAL, RES>), grid, dim3(256), 0, st, X, W, Y, M, N, F, ra.h, ra.y,
                        ra.alpha, ra.hout);
   else
-    hipLaunchKernelGGL((k_gemv_bf16<KCH, R, 2, DUAL, RES>), grid, dim3(256), 0, st, X, W, Y, M, N, F, ra.h, ra.y,
+    DORY_LAUNCH((k_gemv_bf16<KCH, R, 2, DUAL, RES>), grid, dim3(256), 0, st, X, W, Y, M, N, F, ra.h, ra.y,
                        ra.alpha, ra.hout);
   return hipGetLastError();
 }
@@ -390,9 +390,9 @@ static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M
   const int mt = (M + BM - 1) / BM, nt = (ncols + cols_per_tile - 1) / cols_per_tile;
   const dim3 grid(mt * nt);
   if (dual)
-    hipLaunchKernelGGL((k_gemm_tile<BM, BN, true>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt);
+    DORY_LAUNCH((k_gemm_tile<BM, BN, true>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt);
   else
-    hipLaunchKernelGGL((k_gemm_tile<BM, BN, false>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt);
+    DORY_LAUNCH((k_gemm_tile<BM, BN, false>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt);
   return hipGetLastError();
 }
 
@@ -440,10 +440,10 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     const int ncols = dual ? F : N;
     dim3 grid((ncols + F_BN - 1) / F_BN, (M + F_BM - 1) / F_BM);
     if (dual)
-      hipLaunchKernelGGL(k_gemm_f32<true>, grid, dim3(256), 0, st, (const float*)A, (const float*)B, (float*)out,
+      DORY_LAUNCH(k_gemm_f32<true>, grid, dim3(256), 0, st, (const float*)A, (const float*)B, (float*)out,
                          M, F, K, F);
     else
-      hipLaunchKernelGGL(k_gemm_f32<false>, grid, dim3(256), 0, st, (const float*)A, (const float*)B, (float*)out,
+      DORY_LAUNCH(k_gemm_f32<false>, grid, dim3(256), 0, st, (const float*)A, (const float*)B, (float*)out,
                          M, N, K, 0);
     return hipGetLastError();
   }

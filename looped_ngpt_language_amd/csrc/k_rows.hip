@@ -154,7 +154,7 @@ __global__ void k_copy_f32(float* __restrict__ dst, const float* __restrict__ sr
 template <typename T>
 static hipError_t embed_t(const int32_t* tokens, const void* E, int V, int d, int M, float* h, void* hb,
                           int32_t* err, hipStream_t st) {
-  hipLaunchKernelGGL(k_embed<T>, dim3(M), dim3(ROW_THREADS), 0, st, tokens, (const T*)E, V, d, h, (T*)hb, err);
+  DORY_LAUNCH(k_embed<T>, dim3(M), dim3(ROW_THREADS), 0, st, tokens, (const T*)E, V, d, h, (T*)hb, err);
   return hipGetLastError();
 }
 hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int V, int d, int M, float* h, void* hb,
@@ -166,42 +166,42 @@ hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int V, 
 hipError_t launch_residual(int dtype, float* h, const float* y, const float* alpha, void* hb, int M, int d,
                            hipStream_t st) {
   if (dtype == 0)
-    hipLaunchKernelGGL(k_residual<float>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (float*)hb, d);
+    DORY_LAUNCH(k_residual<float>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (float*)hb, d);
   else
-    hipLaunchKernelGGL(k_residual<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (bf16_t*)hb, d);
+    DORY_LAUNCH(k_residual<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (bf16_t*)hb, d);
   return hipGetLastError();
 }
 
 hipError_t launch_norm_sum(int dtype, const float* a, const float* b, float* h, float* s, void* hb, int M, int d,
                            hipStream_t st) {
   if (dtype == 0)
-    hipLaunchKernelGGL(k_norm_sum<float>, dim3(M), dim3(ROW_THREADS), 0, st, a, b, h, s, (float*)hb, d);
+    DORY_LAUNCH(k_norm_sum<float>, dim3(M), dim3(ROW_THREADS), 0, st, a, b, h, s, (float*)hb, d);
   else
-    hipLaunchKernelGGL(k_norm_sum<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, a, b, h, s, (bf16_t*)hb, d);
+    DORY_LAUNCH(k_norm_sum<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, a, b, h, s, (bf16_t*)hb, d);
   return hipGetLastError();
 }
 
 hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(ARGMAX_THREADS), 0, st, logits, V, ids);
+  DORY_LAUNCH(k_argmax, dim3(rows), dim3(ARGMAX_THREADS), 0, st, logits, V, ids);
   return hipGetLastError();
 }
 
 hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_apply_updates, dim3((n + 255) / 256), dim3(256), 0, st, table, upd, n);
+  DORY_LAUNCH(k_apply_updates, dim3((n + 255) / 256), dim3(256), 0, st, table, upd, n);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_table(float2* tab, int max_len, int dh, double theta, hipStream_t st) {
   const size_t n = (size_t)max_len * (dh / 2);
-  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, max_len, dh / 2, dh,
+  DORY_LAUNCH(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, max_len, dh / 2, dh,
                      theta);
   return hipGetLastError();
 }
 
 hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
+  DORY_LAUNCH(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
   return hipGetLastError();
 }
 

@@ -1,9 +1,34 @@
 // Launchers of the gfx950 kernels (device pointers, stream-ordered, no allocation).
 // dtype: 0 = fp32 model, 1 = bf16 model (storage type of weights, GEMM inputs, KV).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+namespace dory {
+
+// Event pair the launchers attach to their dispatches while `stop` is set
+// (timing mode): `start` is recorded by the first dispatch's start, `stop` by
+// the end of every dispatch, so the pair spans exactly the role's kernels.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+}  // namespace dory
+
+#define DORY_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                                    \
+  do {                                                                                                          \
+    if (::dory::g_launch_events.stop) {                                                                         \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, ::dory::g_launch_events.start,                \
+                            ::dory::g_launch_events.stop, 0, __VA_ARGS__);                                      \
+      ::dory::g_launch_events.start = nullptr;                                                                  \
+    } else {                                                                                                    \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                                     \
+    }                                                                                                           \
+  } while (0)
 
 namespace dory {
 
