@@ -37,7 +37,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {  // byte offsets inside the workspace
-  size_t rope, ptab, upload, err, buf[4], y, hb, qkv, q, o, z, part_ml, part_o, logits, spec, total;
+  size_t rope, ptab, upload, err, buf[4], y, hb, qkv, q, o, z, part_ml, part_o, logits, argmax, splitk, spec, total;
+  size_t splitk_bytes;
   int max_pages;       // pages per sequence
   int upload_ints;     // capacity of the upload area in int32
   int part_rows;       // rows that may use split attention
@@ -71,6 +72,12 @@ Layout make_layout(const dory_config& c) {
   L.part_ml = take((size_t)L.part_rows * c.n_heads * kMaxSplits * 2 * 4);
   L.part_o = take((size_t)L.part_rows * c.n_heads * kMaxSplits * c.head_dim * 4);
   L.logits = take((size_t)L.logit_rows * c.vocab * 4);
+  L.argmax = take((size_t)std::max(c.max_tokens, L.logit_rows) * dory::kArgmaxParts * 8);
+  {
+    const size_t nmax = std::max({(size_t)qkv_cols(c), (size_t)2 * c.d_ff, (size_t)c.d_model});
+    L.splitk_bytes = c.dtype == DORY_BF16 ? 4 * (size_t)std::min(c.max_tokens, 256) * nmax * 4 : 0;
+    L.splitk = take(L.splitk_bytes);
+  }
   L.spec = take(64 * 4);
   L.total = off;
   return L;
@@ -308,6 +315,8 @@ struct Geom {
   }
 };
 
+#define SPLITK c->W<float>(c->L.splitk), c->L.splitk_bytes
+
 // Residual-stream bookkeeping of one forward pass. With a pending step
 // (py != nullptr) the hidden rows are N(h + pa * (N(py) - h)), not yet
 // materialised: the next weight-streaming GEMV applies it in its prologue
@@ -379,7 +388,7 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   } else {
     flush(c, f, M);
     Span sp(c, R_QKV, (double)nq * d * es + Md * d * es + Md * nq * 4, 2.0 * Md * nq * d);
-    ok(c, launch_gemm(dt, false, hb, c->wqkv[j], qkv, M, nq, d, st));
+    ok(c, launch_gemm(dt, false, hb, c->wqkv[j], qkv, M, nq, d, SPLITK, st));
   }
   if (!fused_decode) {
     Span sp(c, R_ROPE, Md * nq * 4 + Md * (hd + 2.0 * Hk * dh) * es, 0);
@@ -407,7 +416,7 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   }
   {
     Span sp(c, R_OPROJ, (double)d * hd * es + Md * hd * es + Md * d * 4, 2.0 * Md * d * hd);
-    ok(c, launch_gemm(dt, false, c->W(c->L.o), c->wo[j], y, M, d, hd, st));
+    ok(c, launch_gemm(dt, false, c->W(c->L.o), c->wo[j], y, M, d, hd, SPLITK, st));
   }
   if (fres) {
     Span sp(c, R_GU, 2.0 * F * d * es + Md * d * 12 + 4.0 * d + Md * F * es, 2.0 * Md * 2 * F * d);
@@ -419,11 +428,11 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
       ok(c, launch_residual(dt, f.h, y, c->aa[j], hb, M, d, st));
     }
     Span sp(c, R_GU, 2.0 * F * d * es + Md * d * es + Md * F * es, 2.0 * Md * 2 * F * d);
-    ok(c, launch_gemm(dt, true, hb, c->wgu[j], c->W(c->L.z), M, 2 * F, d, st));
+    ok(c, launch_gemm(dt, true, hb, c->wgu[j], c->W(c->L.z), M, 2 * F, d, SPLITK, st));
   }
   {
     Span sp(c, R_DOWN, (double)d * F * es + Md * F * es + Md * d * 4, 2.0 * Md * d * F);
-    ok(c, launch_gemm(dt, false, c->W(c->L.z), c->wd[j], y, M, d, F, st));
+    ok(c, launch_gemm(dt, false, c->W(c->L.z), c->wd[j], y, M, d, F, SPLITK, st));
   }
   if (fres) {
     f.py = y;
@@ -496,11 +505,11 @@ void lm_head(dory_ctx* c, int M, int rows, float* logits, int32_t* ids) {
   const char* hb = c->W(c->L.hb) + (size_t)(M - rows) * g.d_model * esize(g);
   {
     Span sp(c, R_LM, V * d * es + rows * d * es + rows * V * 4, 2.0 * rows * V * d);
-    ok(c, launch_gemm(g.dtype, false, hb, c->lm, logits, rows, g.vocab, g.d_model, c->stream));
+    ok(c, launch_gemm(g.dtype, false, hb, c->lm, logits, rows, g.vocab, g.d_model, SPLITK, c->stream));
   }
   if (ids) {
     Span sp(c, R_ARGMAX, rows * V * 4 + rows * 4.0, 0);
-    ok(c, launch_argmax(logits, rows, g.vocab, ids, c->stream));
+    ok(c, launch_argmax(logits, rows, g.vocab, ids, c->W(c->L.argmax), c->stream));
   }
 }
 

@@ -100,10 +100,13 @@ DORY_DEV void load_lds16(const bf16_t* src, bf16_t* lds_block) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_block, 16, 0, 0);
 }
 
+// Split-K: blockIdx.y selects the K range [y * k_len, (y+1) * k_len); with
+// gridDim.y > 1 (plain only) the fp32 tile goes to partial slice y of Cv,
+// [gridDim.y][M][N], summed afterwards by k_splitk_reduce.
 template <int BM, int BN, bool DUAL>
 __global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
                                                    void* __restrict__ Cv, int M, int N, int K, int F, int m_tiles,
-                                                   int n_tiles) {
+                                                   int n_tiles, int k_len) {
   constexpr int TM = BM / 64, TN = BN / 64;
   constexpr int IA = BM / 32, IB = BN / 32;  // 1 KB load instructions per wave per k-tile
   __shared__ __attribute__((aligned(1024))) bf16_t As[2][BM * MF_BK];
@@ -122,12 +125,13 @@ __global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A,
   // this lane's global source rows and swizzled chunk for each load instruction
   const int lrow = lane >> 3;                  // row within the 8-row block
   const int lchunk = (lane & 7) ^ lrow;        // logical k-chunk stored at physical slot lane & 7
+  const int kbase = blockIdx.y * k_len;
   const bf16_t* asrc[IA];
   const bf16_t* bsrc[IB];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
     const int r = (wid * IA + i) * 8 + lrow;
-    asrc[i] = A + (size_t)min(m0 + r, M - 1) * K + lchunk * 8;
+    asrc[i] = A + (size_t)min(m0 + r, M - 1) * K + kbase + lchunk * 8;
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
@@ -135,7 +139,7 @@ __global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A,
     int gn;
     if (DUAL) gn = (r < BN / 2) ? min(n0 + r, F - 1) : F + min(n0 + r - BN / 2, F - 1);
     else gn = min(n0 + r, N - 1);
-    bsrc[i] = B + (size_t)gn * K + lchunk * 8;
+    bsrc[i] = B + (size_t)gn * K + kbase + lchunk * 8;
   }
 
   f32x16_t acc[TM][TN];
@@ -156,7 +160,8 @@ __global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A,
   const int arow0 = wm * (BM / 2) + (lane & 31);
   const int khalf = lane >> 5;
 
-  const int nk = K / MF_BK;
+  const int nk = k_len / MF_BK;
+  float* const Cf = reinterpret_cast<float*>(Cv) + (size_t)blockIdx.y * M * N;
 #pragma unroll
   for (int i = 0; i < IA; ++i)
     load_lds16(asrc[i], &As[0][(wid * IA + i) * 512]);
@@ -220,7 +225,7 @@ __global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A,
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int gn = n0 + wn * (BN / 2) + j * 32 + col;
-          if (gn < N) reinterpret_cast<float*>(Cv)[(size_t)gm * N + gn] = acc[i][j][v];
+          if (gn < N) Cf[(size_t)gm * N + gn] = acc[i][j][v];
         }
       }
     }
@@ -382,6 +387,25 @@ static hipError_t gemv_dispatch(const bf16_t* X, const bf16_t* W, void* Y, int M
   }
 }
 
+// Sum of split-K partials [S][M][N]: plain -> fp32 [M][N]; dual (N = 2F) ->
+// bf16 z[m][c] = silu(gate) * up with gate = column c, up = column F + c.
+template <bool DUAL>
+__global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__ part, int S, int M, int N,
+                                                       void* __restrict__ out) {
+  const int cols = DUAL ? N / 2 : N;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)M * cols) return;
+  const size_t m = idx / cols, c = idx % cols;
+  const size_t slice = (size_t)M * N;
+  float a = 0.f, u = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    a += part[sp * slice + m * N + c];
+    if (DUAL) u += part[sp * slice + m * N + cols + c];
+  }
+  if (DUAL) reinterpret_cast<bf16_t*>(out)[idx] = f32_to_bf16(silu(a) * u);
+  else reinterpret_cast<float*>(out)[idx] = a;
+}
+
 template <int BM, int BN>
 static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
                               hipStream_t st) {
@@ -390,9 +414,9 @@ static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M
   const int mt = (M + BM - 1) / BM, nt = (ncols + cols_per_tile - 1) / cols_per_tile;
   const dim3 grid(mt * nt);
   if (dual)
-    DORY_LAUNCH((k_gemm_tile<BM, BN, true>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt);
+    DORY_LAUNCH((k_gemm_tile<BM, BN, true>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt, K);
   else
-    DORY_LAUNCH((k_gemm_tile<BM, BN, false>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt);
+    DORY_LAUNCH((k_gemm_tile<BM, BN, false>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt, K);
   return hipGetLastError();
 }
 
@@ -432,8 +456,19 @@ hipError_t launch_gemv_residual(bool dual, const void* W, void* out, int M, int 
 }
 
 // out: fp32 [M,N] (plain) or storage-type z [M,F] (dual, N = 2F).
+// Few rows (3..256): 128x128 tiles leave most CUs idle, so K is split until the
+// grid has >= 256 workgroups (partials in `split_ws`, then a reduce kernel).
+static int choose_split(int M, int N, int K, size_t split_ws_bytes) {
+  const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+  int S = 1;
+  while (tiles * S < 256 && S < 16 && (K / MF_BK) % (2 * S) == 0 &&
+         (size_t)(2 * S) * M * N * sizeof(float) <= split_ws_bytes)
+    S *= 2;
+  return S;
+}
+
 hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
-                       hipStream_t st) {
+                       float* split_ws, size_t split_ws_bytes, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const int F = dual ? N / 2 : 0;
   if (dtype == 0) {
@@ -452,6 +487,22 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     const ResArgs none{nullptr, nullptr, nullptr, nullptr};
     return dual ? gemv_dispatch<true, false>((const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F, none, st)
                 : gemv_dispatch<false, false>((const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F, none, st);
+  }
+  if (M <= 256 && split_ws) {
+    const int S = choose_split(M, N, K, split_ws_bytes);
+    if (S > 1) {
+      const int mt = (M + 127) / 128, nt = (N + 127) / 128;
+      DORY_LAUNCH((k_gemm_tile<128, 128, false>), dim3(mt * nt, S), dim3(256), 0, st, (const bf16_t*)A,
+                  (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
+      const size_t outs = (size_t)M * (dual ? F : N);
+      if (dual)
+        DORY_LAUNCH(k_splitk_reduce<true>, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st,
+                    (const float*)split_ws, S, M, N, out);
+      else
+        DORY_LAUNCH(k_splitk_reduce<false>, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st,
+                    (const float*)split_ws, S, M, N, out);
+      return hipGetLastError();
+    }
   }
   return launch_tile_gemm((const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F, dual, st);
 }

@@ -99,33 +99,55 @@ __global__ void __launch_bounds__(ROW_THREADS) k_norm_sum(const float* a, const 
   }
 }
 
-// ids[r] = argmax_j logits[r, j], lowest j on ties.
-constexpr int ARGMAX_THREADS = 1024;
-__global__ void __launch_bounds__(ARGMAX_THREADS) k_argmax(const float* __restrict__ logits, int V,
-                                                           int32_t* __restrict__ ids) {
+// ids[r] = argmax_j logits[r, j], lowest j on ties. Two passes: grid (rows,
+// ARGMAX_PARTS) workgroups each reduce a contiguous slice to (max, index), then
+// one workgroup per row reduces the slices. Ties keep the lower index.
+constexpr int ARGMAX_THREADS = 256;
+constexpr int ARGMAX_PARTS = kArgmaxParts;
+
+DORY_DEV void argmax_combine(float& best, int& bi, float ov, int oi) {
+  if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+}
+
+DORY_DEV void block_argmax(float& best, int& bi) {
   __shared__ float sv[ARGMAX_THREADS / 64];
   __shared__ int si[ARGMAX_THREADS / 64];
-  const float* row = logits + (size_t)blockIdx.x * V;
-  float best = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int j = threadIdx.x; j < V; j += ARGMAX_THREADS) {
-    const float v = row[j];
-    if (v > best) { best = v; bi = j; }  // j increases: first maximum kept
-  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(best, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-  }
+  for (int o = 32; o > 0; o >>= 1) argmax_combine(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) { sv[w] = best; si[w] = bi; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < ARGMAX_THREADS / 64; ++i)
-      if (sv[i] > best || (sv[i] == best && si[i] < bi)) { best = sv[i]; bi = si[i]; }
-    ids[blockIdx.x] = bi == 0x7fffffff ? 0 : bi;
+  if (threadIdx.x == 0)
+    for (int i = 1; i < ARGMAX_THREADS / 64; ++i) argmax_combine(best, bi, sv[i], si[i]);
+}
+
+__global__ void __launch_bounds__(ARGMAX_THREADS) k_argmax_part(const float* __restrict__ logits, int V,
+                                                                float* __restrict__ pv, int* __restrict__ pi) {
+  const int row = blockIdx.x, part = blockIdx.y;
+  const int chunk = (V + ARGMAX_PARTS - 1) / ARGMAX_PARTS;
+  const int j0 = part * chunk, j1 = min(V, j0 + chunk);
+  const float* r = logits + (size_t)row * V;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int j = j0 + threadIdx.x; j < j1; j += ARGMAX_THREADS) {
+    const float v = r[j];
+    if (v > best) { best = v; bi = j; }  // j increases: first maximum kept
   }
+  block_argmax(best, bi);
+  if (threadIdx.x == 0) {
+    pv[row * ARGMAX_PARTS + part] = best;
+    pi[row * ARGMAX_PARTS + part] = bi;
+  }
+}
+
+__global__ void __launch_bounds__(64) k_argmax_final(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                     int32_t* __restrict__ ids) {
+  const int row = blockIdx.x, t = threadIdx.x;
+  float best = pv[row * ARGMAX_PARTS + t];
+  int bi = pi[row * ARGMAX_PARTS + t];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) argmax_combine(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
+  if (t == 0) ids[row] = bi == 0x7fffffff ? 0 : bi;
 }
 
 // Page-table scatter: table[upd[2i]] = upd[2i+1].
@@ -181,8 +203,12 @@ hipError_t launch_norm_sum(int dtype, const float* a, const float* b, float* h, 
   return hipGetLastError();
 }
 
-hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, hipStream_t st) {
-  DORY_LAUNCH(k_argmax, dim3(rows), dim3(ARGMAX_THREADS), 0, st, logits, V, ids);
+// scratch: rows * ARGMAX_PARTS floats + as many ints
+hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, void* scratch, hipStream_t st) {
+  float* pv = static_cast<float*>(scratch);
+  int* pi = reinterpret_cast<int*>(pv + (size_t)rows * ARGMAX_PARTS);
+  DORY_LAUNCH(k_argmax_part, dim3(rows, ARGMAX_PARTS), dim3(ARGMAX_THREADS), 0, st, logits, V, pv, pi);
+  DORY_LAUNCH(k_argmax_final, dim3(rows), dim3(64), 0, st, (const float*)pv, (const int*)pi, ids);
   return hipGetLastError();
 }
 

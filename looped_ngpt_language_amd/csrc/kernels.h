@@ -38,7 +38,8 @@ hipError_t launch_residual(int dtype, float* h, const float* y, const float* alp
                            hipStream_t st);
 hipError_t launch_norm_sum(int dtype, const float* a, const float* b, float* h, float* s, void* hb, int M, int d,
                            hipStream_t st);
-hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, hipStream_t st);
+constexpr int kArgmaxParts = 64;  // partial (max, index) pairs per row in the argmax scratch
+hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, void* scratch, hipStream_t st);
 hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, hipStream_t st);
 hipError_t launch_rope_table(float2* tab, int max_len, int dh, double theta, hipStream_t st);
 hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t st);
@@ -65,7 +66,8 @@ bool gemv_residual_supported(int K);
 // result is also written to hout (which must not alias h or y).
 hipError_t launch_gemv_residual(bool dual, const void* W, void* out, int M, int N, int K, const float* h,
                                 const float* y, const float* alpha, float* hout, hipStream_t st);
+// C = A . B^T (bf16 or fp32 model). split_ws (may be NULL) holds split-K partials for 3..256 rows.
 hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
-                       hipStream_t st);
+                       float* split_ws, size_t split_ws_bytes, hipStream_t st);
 
 }  // namespace dory

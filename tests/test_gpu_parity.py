@@ -173,3 +173,70 @@ def test_mid_bf16_sliding_window_and_chunks(mid):
     err_h = float(np.max(np.abs(h - om.last_hidden[-1])))
     say(f"  chunked 1200-token prompt: logits max-abs {err:.3e}, hidden {err_h:.3e}, id {int(i2[0])} vs {int(oids[0])}")
     assert err <= 5e-2 and err_h <= 3e-2
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_tiny_fp32_self_speculative(tiny, mode):
+    """dory_spec_decode (k=1 draft of 4, k=4 verify) against the oracle's driver, ids bit-exact;
+    in per-loop mode both also equal plain k=4 greedy."""
+    from oracle import self_speculative
+    w, m = tiny
+    say(f"[tiny fp32] self-speculative decoding, {mode}")
+    for s in range(4):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    m.set_kv_mode(mode)
+    m.set_loops(4)
+    prompt = synth.prompt_tokens(synth.TINY, 30)
+    _, ids = m.prefill(0, prompt, 1)
+    first = int(ids[0].item())
+    got = m.spec_decode(0, first, 20, gamma=4, k_draft=1, k_verify=4)
+    om = OracleModel(synth.TINY, w, mode, 4)
+    want = self_speculative(om, 0, prompt, 21, gamma=4, k_draft=1, k_verify=4)
+    say(f"  gpu {list(got[:20])}\n  oracle {list(want[1:21])}")
+    assert first == int(want[0])
+    np.testing.assert_array_equal(got[:20], want[1:21])
+    assert m.loops() == 4
+    if mode == "per_loop":
+        ref = oracle_greedy(synth.TINY, w, mode, 4, prompt, 20)[0]
+        np.testing.assert_array_equal(want[:21], ref[:21])
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_mid_bf16_batched_decode(mode):
+    """Serving-style batched decode: 6 sequences with ragged prompt lengths decode together
+    (one call per step, rows = sequences); every sequence against its own oracle run,
+    teacher-forced. Exercises the split-K small-M GEMM and multi-row split attention."""
+    w = synth.make_weights(synth.MID, seed=0)
+    m = dory.Model(synth.MID, w, kv_mode=mode, max_loops=2, max_seqs=6, max_model_len=512, max_tokens=512)
+    m.set_loops(2)
+    lens = synth.batch_prompt_lengths(6, 17, 300, seed=2)
+    prompts = synth.batch_prompts(synth.MID, lens, seed=1)
+    say(f"[mid bf16] batched decode, {mode}, k=2, prompt lengths {list(lens)}")
+    n_dec = 3
+    o_all = [oracle_greedy(synth.MID, w, mode, 2, p, n_dec) for p in prompts]
+    first = []
+    for s, p in enumerate(prompts):
+        lg, ids = m.prefill(s, p, 1)
+        first.append((lg[0].cpu().numpy(), int(ids[0].item())))
+    g_lg = [[f[0]] for f in first]
+    g_ids = [[f[1]] for f in first]
+    for step in range(n_dec):
+        toks = torch.tensor([int(o_all[s][0][step]) for s in range(6)], dtype=torch.int32, device=m.device)
+        lg, ids = m.decode(list(range(6)), toks)
+        lg = lg.cpu().numpy()
+        ids = ids.cpu().numpy()
+        for s in range(6):
+            g_lg[s].append(lg[s])
+            g_ids[s].append(int(ids[s]))
+    for s in range(6):
+        o_ids, o_lg, _ = o_all[s]
+        err = float(np.max(np.abs(np.array(g_lg[s]) - o_lg)))
+        agree = int(np.sum(np.array(g_ids[s]) == o_ids))
+        say(f"  seq {s} (len {lens[s]}): logits max-abs {err:.2e}, ids {agree}/{len(o_ids)}")
+        assert err <= 5e-2
+        for i in range(len(o_ids)):
+            if g_ids[s][i] != o_ids[i]:
+                margin = o_lg[i][o_ids[i]] - o_lg[i][g_ids[s][i]]
+                assert margin < 2 * np.max(np.abs(g_lg[s][i] - o_lg[i]))
+    m.close()
