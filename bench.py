@@ -47,6 +47,10 @@ def parse():
     p.add_argument("--loops", default="1,2,4")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-batched", action="store_true")
+    p.add_argument("--batched-steps", type=int, default=16)
+    p.add_argument("--long", action="store_true", help="also run the 131072-token prompt at k=4 and "
+                   "self-speculative decoding (adds a few minutes)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one device copy of 256 MiB first (counter calibration under rocprofv3)")
     return p.parse_args()
@@ -179,6 +183,11 @@ def main():
             log(f"         {name:22s} {r['launches_per_step']:6.1f}/step  avg {r['avg_us']:8.2f} us  "
                 f"{r['ms_per_step']:7.3f} ms/step  {r['GBs']:7.0f} GB/s")
 
+    if not args.no_batched:
+        res["batched"] = bench_batched(m, shape, args, ev)
+    if args.long:
+        res["long"] = bench_long(m, shape, args, ev)
+
     head = res["decode"].get(args.k) or next(iter(res["decode"].values()))
     dom_name, dom = max(head["kernels"].items(), key=lambda x: x[1]["ms_per_step"])
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(dom["GBs"], 1), "peak": HBM_PEAK_GBS,
@@ -216,9 +225,127 @@ def main():
             "prefill": {str(k): {"tokens": v["tokens"], "tok_s": round(v["tok_s"], 1), "ms": round(v["ms"], 3),
                                  "tflop_s": round(v["tflop_s"], 1), "mfma_frac": round(v["mfma_frac"], 4)}
                         for k, v in res["prefill"].items()},
+            "decode_bs128_k2": res.get("batched"),
+            "long_context_k4": res.get("long"),
         },
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_batched(m1, shape, args, ev):
+    """Serving-style batched decode: 128 sequences with prompt lengths uniform in [256, 4096]
+    (seeded), k = 2, one decode call per step for all sequences; per-loop vs last-loop KV."""
+    import torch
+
+    from looped_ngpt_language_amd import dory, synth
+    n_seq, k, steps = 128, 2, args.batched_steps
+    lens = synth.batch_prompt_lengths(n_seq, 256, 4096, seed=2)
+    prompts = synth.batch_prompts(shape, lens, seed=1)
+    extra = 2 + steps + 16
+    kv_tokens = int(sum(((int(n) + extra + 15) // 16) * 16 for n in lens))
+    mb = dory.Model(shape, None, kv_mode="per_loop", max_loops=k, max_seqs=n_seq, max_model_len=4096 + extra,
+                    max_tokens=4096, kv_tokens=kv_tokens, device="cuda:0", share_weights_from=m1)
+    out = {"sequences": n_seq, "loops": k, "prompt_tokens": int(sum(lens)), "steps": steps}
+    st = mb.stream
+    for mode in ("per_loop", "last_loop"):
+        mb.set_kv_mode(mode)
+        mb.set_loops(k)
+        t0 = time.time()
+        firsts = []
+        for s_, p in enumerate(prompts):
+            _, ids = mb.prefill(s_, torch.from_numpy(p).to("cuda:0"), 1)
+            firsts.append(ids)
+        cur = torch.cat(firsts)
+        torch.cuda.synchronize()
+        t_pf = time.time() - t0
+        sids = list(range(n_seq))
+        nxt = [torch.empty(n_seq, dtype=torch.int32, device="cuda:0") for _ in range(2)]
+        for i in range(2):
+            mb.decode(sids, cur, logits=None, out_ids=nxt[i % 2])
+            cur = nxt[i % 2]
+        torch.cuda.synchronize()
+        mb.timing(reset=True)
+        e0, e1 = ev(), ev()
+        e0.record(st)
+        for i in range(steps):
+            mb.decode(sids, cur, logits=None, out_ids=nxt[i % 2])
+            cur = nxt[i % 2]
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tim = mb.timing(reset=True)
+        step_bytes = sum(v["bytes"] for v in tim.values()) / steps
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        kvb = mb.kv_bytes_in_use()
+        out[mode] = {"tok_s": round(n_seq * 1e3 / ms, 1), "ms_per_step": round(ms, 3),
+                     "GB_per_step": round(step_bytes / 1e9, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "kv_bytes_in_use": kvb, "prefill_s": round(t_pf, 1)}
+        log(f"[bench] decode bs{n_seq} k={k} {mode}: {ms:.2f} ms/step  {n_seq * 1e3 / ms:,.0f} tok/s  "
+            f"{step_bytes / 1e9:.1f} GB/step -> {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak); "
+            f"KV in use {kvb / 1e9:.1f} GB; prefill of {int(sum(lens))} tokens took {t_pf:.1f} s")
+        for s_ in sids:
+            mb.release(s_)
+    mb.close()
+    return out
+
+
+def bench_long(m1, shape, args, ev):
+    """131072-token uniform-random prompt at k = 4, last-loop KV (full layers attend over the
+    whole prompt, sliding-window layers over 4096), then decode at batch 1 and self-speculative
+    decoding (k = 1 draft of 4 tokens, k = 4 verification) on the same weights."""
+    import torch
+
+    from looped_ngpt_language_amd import dory, synth
+    T, k, n_dec, n_spec = 131072, 4, 16, 64
+    mb = dory.Model(shape, None, kv_mode="last_loop", max_loops=4, max_seqs=1, max_model_len=T + 256,
+                    max_tokens=T, device="cuda:0", share_weights_from=m1)
+    mb.set_loops(k)
+    st = mb.stream
+    prompt = torch.from_numpy(synth.prompt_tokens(shape, T, seed=1)).to("cuda:0")
+    mb.timing(reset=True)
+    e0, e1 = ev(), ev()
+    e0.record(st)
+    _, ids = mb.prefill(0, prompt, 1)
+    e1.record(st)
+    torch.cuda.synchronize()
+    pf_ms = e0.elapsed_time(e1)
+    tim = mb.timing(reset=True)
+    flops = sum(v["flops"] for v in tim.values())
+    tfs = flops / (pf_ms * 1e-3) / 1e12
+    log(f"[bench] long prefill T={T} k={k}: {pf_ms / 1e3:.2f} s  {T / (pf_ms * 1e-3):,.0f} tok/s  "
+        f"{tfs:.1f} TFLOP/s ({100 * tfs / BF16_PEAK_TFLOPS:.1f}% of MFMA peak)")
+    base_len = mb.seq_len(0)
+    cur = ids.clone()
+    nxt = [torch.empty(1, dtype=torch.int32, device="cuda:0") for _ in range(2)]
+    e0.record(st)
+    for i in range(n_dec):
+        mb.decode([0], cur, logits=None, out_ids=nxt[i % 2])
+        cur = nxt[i % 2]
+    e1.record(st)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / n_dec
+    tim = mb.timing(reset=True)
+    step_bytes = sum(v["bytes"] for v in tim.values()) / n_dec
+    gbs = step_bytes / (dec_ms * 1e-3) / 1e9
+    log(f"[bench] long decode ctx {T} k={k}: {dec_ms:.2f} ms/step  {1e3 / dec_ms:.1f} tok/s  "
+        f"{step_bytes / 1e9:.1f} GB/step -> {gbs:.0f} GB/s")
+    mb.truncate(0, base_len)
+    last = int(ids[0].item())
+    t0 = time.perf_counter()
+    got = mb.spec_decode(0, last, n_spec, gamma=4, k_draft=1, k_verify=4)
+    torch.cuda.synchronize()
+    sp_s = time.perf_counter() - t0
+    calls = None
+    spec_tok_s = len(got) / sp_s
+    log(f"[bench] self-speculative (k=1 draft x4, k=4 verify): {len(got)} tokens in {sp_s:.2f} s -> "
+        f"{spec_tok_s:.1f} tok/s ({spec_tok_s * dec_ms / 1e3:.2f}x plain k=4 decode)")
+    mb.close()
+    return {"prompt_tokens": T, "loops": k, "prefill_s": round(pf_ms / 1e3, 3),
+            "prefill_tok_s": round(T / (pf_ms * 1e-3), 1), "prefill_tflop_s": round(tfs, 1),
+            "prefill_mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4), "decode_tok_s": round(1e3 / dec_ms, 2),
+            "decode_GB_per_step": round(step_bytes / 1e9, 2), "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "spec_tok_s": round(spec_tok_s, 2), "spec_speedup": round(spec_tok_s * dec_ms / 1e3, 3),
+            "spec_tokens": int(len(got))}
 
 
 def measured_traffic(role):

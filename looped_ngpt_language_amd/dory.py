@@ -134,7 +134,8 @@ class Model:
     """One looped nGPT context on one GPU (or a host-only dry-run context)."""
 
     def __init__(self, shape: synth.ModelShape, weights=None, *, kv_mode="per_loop", max_loops=4, max_seqs=1,
-                 max_model_len=4096, max_tokens=None, kv_tokens=None, device="cuda:0", dry_run=False, stream=None):
+                 max_model_len=4096, max_tokens=None, kv_tokens=None, device="cuda:0", dry_run=False, stream=None,
+                 share_weights_from=None):
         self.shape = shape
         self.dry = dry_run
         max_tokens = max_tokens or max_model_len
@@ -152,7 +153,7 @@ class Model:
             import torch
             self.device = torch.device(device)
             self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
-            wc = self._upload_weights(weights)
+            wc = self._share_weights(share_weights_from) if share_weights_from else self._upload_weights(weights)
             self.pool = torch.empty(max(kv_bytes, 256), dtype=torch.uint8, device=self.device)
             self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
             st = lib().dory_create(C.byref(self.cfg), C.byref(wc), KV_MODES[kv_mode], _ptr(self.pool), kv_bytes,
@@ -162,6 +163,15 @@ class Model:
         self.ctx = ctx
 
     # -- weights ------------------------------------------------------------
+    def _share_weights(self, other):
+        """Use the device weights another context already holds (same shape)."""
+        assert other.shape == self.shape
+        self.w_embed, self.w_lm, self.w_blocks = other.w_embed, other.w_lm, other.w_blocks
+        arrs = other._keep[0]
+        self._keep.append(arrs)
+        return WeightsC(embed=_ptr(self.w_embed), lm_head=_ptr(self.w_lm), w_qkv=arrs["qkv"], w_o=arrs["o"],
+                        w_gu=arrs["gu"], w_down=arrs["d"], alpha_attn=arrs["aa"], alpha_mlp=arrs["am"])
+
     def _upload_weights(self, w):
         import torch
         s = self.shape
