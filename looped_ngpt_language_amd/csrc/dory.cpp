@@ -290,12 +290,13 @@ bool stage_upload(dory_ctx* c, int n_ints) {
 }
 
 // Key splits per (row, KV head) for split attention: enough workgroups to fill
-// the chip, at least two 16-key pages per wave of the bf16 decode kernel (one
-// key batch per wave for the generic kernel), at most kMaxSplits.
+// the chip with few serial steps per wave, at most kMaxSplits.
 int choose_splits(const dory_ctx* c, int M, int keys, bool paged_kernel) {
   if (M > c->L.part_rows) return 1;
   const int by_work = (2048 + M * c->cfg.n_kv_heads - 1) / (M * c->cfg.n_kv_heads);
-  const int by_keys = paged_kernel ? (keys + 127) / 128 : (keys + 63) / 64;
+  // MFMA decode kernel (few rows): one 32-key block per wave; VALU kernel: 16 pages per workgroup
+  const int by_keys = !paged_kernel ? (keys + 63) / 64 : M <= dory::kDecodeMfmaRows ? (keys + 127) / 128
+                                                                                    : (keys + 255) / 256;
   return std::max(1, std::min(std::min(by_work, by_keys), kMaxSplits));
 }
 

@@ -238,6 +238,190 @@ __global__ void __launch_bounds__(128) k_attn_merge(const float* __restrict__ pa
 
 DORY_DEV float bf16r(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 
+// Operand loads of one 32-key block (pages p0, p0+1) for k_attn_decode: the key
+// rows as the A operand of S^T = K . Q^T (lane l: key l%32, dims 16ks + 8(l/32)),
+// the value rows as the A operand of O^T = V^T . P^T (page pp, dim tile dt:
+// dim 32dt + l%32, tokens vperm 8(l/32) .. +8).
+#define DORY_DEC_FETCH(KF, VF, P0)                                                                            \
+  do {                                                                                                        \
+    const int p0_ = (P0);                                                                                     \
+    const bf16_t* pg0_ = kv_slot + (size_t)prow[p0_] * page_elems;                                            \
+    const bf16_t* pg1_ = p0_ + 1 <= sp_last ? kv_slot + (size_t)prow[p0_ + 1] * page_elems : pg0_;            \
+    const bf16_t* kp_ = (qi < 16 ? pg0_ : pg1_) + ((size_t)g * 16 + (qi & 15)) * DH + 8 * hh;                 \
+    _Pragma("unroll") for (int ks = 0; ks < 8; ++ks) KF[ks] = *reinterpret_cast<const bf16x8_t*>(kp_ + 16 * ks); \
+    _Pragma("unroll") for (int dt = 0; dt < 4; ++dt) {                                                        \
+      const size_t vo_ = vbase + (size_t)(32 * dt + qi) * 16 + 8 * hh;                                        \
+      VF[dt] = *reinterpret_cast<const bf16x8_t*>(pg0_ + vo_);                                                \
+      VF[4 + dt] = *reinterpret_cast<const bf16x8_t*>(pg1_ + vo_);                                            \
+    }                                                                                                         \
+  } while (0)
+
+// grid (rows, H_kv, splits), 256 threads. Each workgroup attends the G <= 4
+// query heads of KV head g for one row over a page-aligned share of the row's
+// keys, on MFMA: the G queries are columns of a 32-wide S^T = K . Q^T tile
+// (v_mfma_f32_32x32x16_bf16; the other columns are zero), and the tile's
+// probabilities feed O^T = V^T . P^T directly (same scheme as the prefill
+// kernel). Each wave takes 32-key blocks round-robin with the next block's
+// operands in flight. With write_kv the split holding the row's own position
+// first writes that position's k^ and v (decode: every row is the newest token
+// of its sequence; splits never share a page). With splits > 1 each workgroup
+// stores a partial (max, sum, unnormalised output) and k_attn_merge combines them.
+template <int G>
+__global__ void __launch_bounds__(256) k_attn_decode(
+    const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
+    const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window,
+    float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
+    float* __restrict__ part_o) {
+  constexpr int DH = 128;
+  __shared__ __attribute__((aligned(16))) bf16_t qs[G][DH];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wacc[4][G][DH];
+  const int m = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int qi = lane & 31, hh = lane >> 5;
+  const int seq = rows[2 * m], pos = rows[2 * m + 1];
+  const int lo = window > 0 ? max(0, pos - window + 1) : 0;
+  const int pf = lo >> 4, pl = pos >> 4;
+  const int pps = (pl - pf + 1 + splits - 1) / splits;
+  const int sp_first = pf + sp * pps;
+  const int sp_last = min(pl, sp_first + pps - 1);
+  const float* src = qkv + (size_t)m * (size_t)((H + 2 * Hkv) * DH);
+  const int32_t* prow = ptab + (size_t)seq * max_pages;
+  const size_t vbase = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16;
+  const float2 cs = rope[(size_t)pos * 64 + lane];
+  const bool writer = write_kv && sp_first <= pl && pl <= sp_last;
+  const int npair = sp_last >= sp_first ? (sp_last - sp_first + 2) / 2 : 0;
+  const int nw = npair > wv ? (npair - wv + 3) / 4 : 0;  // blocks of this wave: pairs wv, wv+4, ...
+  bf16x8_t kA[8], vA[8], kB[8], vB[8];
+  // the first block's operands are requested before the query prologue (the
+  // writer split fetches after writing the new key/value)
+  if (!writer && nw > 0) DORY_DEC_FETCH(kA, vA, sp_first + 2 * wv);
+
+  // queries of the group: q^ = N(RoPE(q)) in bf16
+  for (int gi = wv; gi < G; gi += 4) {
+    const float* x = src + (size_t)(g * G + gi) * DH;
+    const float x1 = x[lane], x2 = x[lane + 64];
+    const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
+    const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    qs[gi][lane] = f32_to_bf16(a0 * r);
+    qs[gi][lane + 64] = f32_to_bf16(a1 * r);
+  }
+  // the split holding the row's own position writes its key/value first
+  if (writer && wv < 2) {
+    bf16_t* pg = kv_slot + (size_t)prow[pl] * page_elems;
+    const int tok = pos & 15;
+    if (wv == 0) {
+      const float* x = src + (size_t)(H + g) * DH;
+      const float x1 = x[lane], x2 = x[lane + 64];
+      const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
+      const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+      bf16_t* kp = pg + ((size_t)g * 16 + tok) * DH;
+      kp[lane] = f32_to_bf16(a0 * r);
+      kp[lane + 64] = f32_to_bf16(a1 * r);
+    } else {
+      const float* v = src + (size_t)(H + Hkv + g) * DH;
+      bf16_t* vt = pg + vbase + vperm(tok);
+      vt[(size_t)lane * 16] = f32_to_bf16(v[lane]);
+      vt[(size_t)(lane + 64) * 16] = f32_to_bf16(v[lane + 64]);
+    }
+  }
+  __syncthreads();
+
+  bf16x8_t qb[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (qi < G) qb[ks] = *reinterpret_cast<const bf16x8_t*>(&qs[qi < G ? qi : 0][16 * ks + 8 * hh]);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[ks][e] = (__bf16)0.f;
+  }
+  f32x16_t acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+
+  if (writer && nw > 0) DORY_DEC_FETCH(kA, vA, sp_first + 2 * wv);
+  for (int it = 0; it < nw; ++it) {
+    const int p0 = sp_first + 2 * (wv + 4 * it);
+    const bool odd = it & 1;
+    if (it + 1 < nw) {
+      if (odd) DORY_DEC_FETCH(kA, vA, p0 + 8);
+      else DORY_DEC_FETCH(kB, vB, p0 + 8);
+    }
+    f32x16_t st;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(odd ? kB[ks] : kA[ks], qb[ks], st, 0, 0, 0);
+    float sv[16];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kp = 16 * p0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+      const bool ok = kp >= lo && kp <= pos && (kp >> 4) <= sp_last;
+      sv[v] = ok ? st[v] * scale : -INFINITY;
+      mb = fmaxf(mb, sv[v]);
+    }
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(mrun, mb);
+    const float c = safe_scale(mrun, mn);
+    float psum = 0.f;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = sv[v] == -INFINITY ? 0.f : __expf(sv[v] - mn);
+      psum += p;
+      pb[v >> 3][v & 7] = (__bf16)p;
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    lrun = lrun * c + psum;
+    mrun = mn;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[dt][v] *= c;
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(odd ? vB[dt] : vA[dt], pb[0], acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(odd ? vB[4 + dt] : vA[4 + dt], pb[1], acc[dt], 0, 0, 0);
+    }
+  }
+  // waves -> LDS: lanes of query qi < G hold O[qi][32dt + 8(v/4) + 4hh + v%4]
+  if (qi < G) {
+    if (hh == 0) { wm[wv][qi] = mrun; wl[wv][qi] = lrun; }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) wacc[wv][qi][32 * dt + 8 * (v >> 2) + 4 * hh + (v & 3)] = acc[dt][v];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * DH; idx += 256) {
+    const int gi = idx / DH, e = idx % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][gi]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float cw = safe_scale(wm[w][gi], M);
+      L += wl[w][gi] * cw;
+      A += wacc[w][gi][e] * cw;
+    }
+    const int hq = g * G + gi;
+    if (splits == 1) {
+      out[((size_t)m * H + hq) * DH + e] = f32_to_bf16(L > 0.f ? A / L : 0.f);
+    } else {
+      const size_t pi = ((size_t)m * H + hq) * splits + sp;
+      part_o[pi * DH + e] = A;
+      if (e == 0) { part_ml[2 * pi] = M; part_ml[2 * pi + 1] = L; }
+    }
+  }
+}
+#undef DORY_DEC_FETCH
+
+// VALU variant, used for many rows (batched decode): its lighter register use keeps
+// more waves, hence more pages, in flight per CU.
 // grid (rows, H_kv, splits), 256 threads. Each workgroup attends the G query
 // heads of KV head g for one row over a page-aligned share of the row's keys.
 // Lane l of a wave reads key (l >> 2) of a page, dims 32*(l & 3) .. +32 for the
@@ -247,7 +431,7 @@ DORY_DEV float bf16r(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 // With splits > 1 each workgroup stores a partial (max, sum, unnormalised
 // output) and k_attn_merge combines them.
 template <int G>
-__global__ void __launch_bounds__(256) k_attn_decode(
+__global__ void __launch_bounds__(256) k_attn_decode_valu(
     const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
     const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window,
     float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
@@ -662,9 +846,13 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
                               hipStream_t st) {
   dim3 grid(M, Hkv, splits);
-#define DORY_DEC(GV)                                                                                                  \
-  DORY_LAUNCH(k_attn_decode<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv,      \
-                     page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o)
+#define DORY_DEC(GV)                                                                                             \
+  if (M > kDecodeMfmaRows)                                                                                     \
+    DORY_LAUNCH(k_attn_decode_valu<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv, \
+                page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o);           \
+  else                                                                                                         \
+    DORY_LAUNCH(k_attn_decode<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv,      \
+                page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o)
   switch (H / Hkv) {
     case 1: DORY_DEC(1); break;
     case 2: DORY_DEC(2); break;
