@@ -103,16 +103,19 @@ DORY_DEV void load_lds16(const bf16_t* src, bf16_t* lds_block) {
 // Split-K: blockIdx.y selects the K range [y * k_len, (y+1) * k_len); with
 // gridDim.y > 1 (plain only) the fp32 tile goes to partial slice y of Cv,
 // [gridDim.y][M][N], summed afterwards by k_splitk_reduce.
-template <int BM, int BN, bool DUAL>
-__global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
-                                                   void* __restrict__ Cv, int M, int N, int K, int F, int m_tiles,
-                                                   int n_tiles, int k_len) {
-  constexpr int TM = BM / 64, TN = BN / 64;
-  constexpr int IA = BM / 32, IB = BN / 32;  // 1 KB load instructions per wave per k-tile
+// WN waves along N (2 or 4) times 2 along M: 4 or 8 waves per workgroup.
+template <int BM, int BN, bool DUAL, int WN = 2>
+__global__ void __launch_bounds__(128 * WN) k_gemm_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+                                                        void* __restrict__ Cv, int M, int N, int K, int F,
+                                                        int m_tiles, int n_tiles, int k_len) {
+  constexpr int WAVES = 2 * WN;
+  constexpr int TM = BM / 64, TN = BN / (32 * WN);
+  constexpr int IA = BM / (8 * WAVES), IB = BN / (8 * WAVES);  // 1 KB load instructions per wave per k-tile
+  static_assert(TN >= 1 && IA >= 1 && IB >= 1 && (!DUAL || TN % 2 == 0), "tile shape");
   __shared__ __attribute__((aligned(1024))) bf16_t As[2][BM * MF_BK];
   __shared__ __attribute__((aligned(1024))) bf16_t Bs[2][BN * MF_BK];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WN, wn = wid % WN;
 
   const int ntiles = m_tiles * n_tiles;
   const int b = blockIdx.x;
@@ -154,8 +157,8 @@ __global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A,
   int brow[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    if (DUAL) brow[j] = j < TN / 2 ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - TN / 2) * 32;
-    else brow[j] = wn * (BN / 2) + j * 32;
+    if (DUAL) brow[j] = j < TN / 2 ? wn * (BN / (2 * WN)) + j * 32 : BN / 2 + wn * (BN / (2 * WN)) + (j - TN / 2) * 32;
+    else brow[j] = wn * (BN / WN) + j * 32;
   }
   const int arow0 = wm * (BM / 2) + (lane & 31);
   const int khalf = lane >> 5;
@@ -215,7 +218,7 @@ __global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A,
       if (DUAL) {
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j) {
-          const int gc = n0 + wn * (BN / 4) + j * 32 + col;
+          const int gc = n0 + wn * (BN / (2 * WN)) + j * 32 + col;
           if (gc < F) {
             const float z = silu(acc[i][j][v]) * acc[i][j + TN / 2][v];
             reinterpret_cast<bf16_t*>(Cv)[(size_t)gm * F + gc] = f32_to_bf16(z);
@@ -224,7 +227,7 @@ __global__ void __launch_bounds__(256) k_gemm_tile(const bf16_t* __restrict__ A,
       } else {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int gn = n0 + wn * (BN / 2) + j * 32 + col;
+          const int gn = n0 + wn * (BN / WN) + j * 32 + col;
           if (gn < N) Cf[(size_t)gm * N + gn] = acc[i][j][v];
         }
       }
@@ -406,40 +409,50 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
   else reinterpret_cast<float*>(out)[idx] = a;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WN = 2>
 static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
                               hipStream_t st) {
   const int ncols = dual ? F : N;
   const int cols_per_tile = dual ? BN / 2 : BN;
   const int mt = (M + BM - 1) / BM, nt = (ncols + cols_per_tile - 1) / cols_per_tile;
   const dim3 grid(mt * nt);
-  if (dual)
-    DORY_LAUNCH((k_gemm_tile<BM, BN, true>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt, K);
-  else
-    DORY_LAUNCH((k_gemm_tile<BM, BN, false>), grid, dim3(256), 0, st, A, B, out, M, N, K, F, mt, nt, K);
+  if (dual) {
+    if constexpr ((BN / (32 * WN)) % 2 == 0)
+      DORY_LAUNCH((k_gemm_tile<BM, BN, true, WN>), grid, dim3(128 * WN), 0, st, A, B, out, M, N, K, F, mt, nt, K);
+    else
+      return hipErrorNotSupported;
+  } else
+    DORY_LAUNCH((k_gemm_tile<BM, BN, false, WN>), grid, dim3(128 * WN), 0, st, A, B, out, M, N, K, F, mt, nt, K);
   return hipGetLastError();
 }
 
-// Tile shape: the candidate with the least estimated time, counting whole
-// rounds of 256 CUs and a per-shape throughput factor (larger tiles reuse
-// each loaded operand more).
+// Tile shape: the candidate with the least estimated time. A round is one
+// workgroup per CU (256x256 tiles need 128 KB of LDS) or two sharing a CU
+// (128x128); a round costs per_cu tiles' area over the shape's measured
+// relative throughput (256x256 / 8 waves = 1).
 static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
                                    hipStream_t st) {
   const int ncols = dual ? F : N;
-  struct Cand { int bm, bn; double eff; } cands[] = {{256, 256, 1.0}, {256, 128, 0.8}, {128, 128, 0.55}};
-  int best = 2;
+  struct Cand { int bm, bn, wn, per_cu; double eff; };
+  static const Cand cands[] = {{256, 256, 4, 1, 1.0}, {256, 128, 4, 1, 0.8}, {256, 128, 2, 1, 0.7},
+                               {128, 128, 4, 2, 0.75}, {128, 128, 2, 2, 0.6}};
+  int best = 0;
   double best_t = 1e300;
-  for (int i = 0; i < 3; ++i) {
-    const int cpt = dual ? cands[i].bn / 2 : cands[i].bn;
-    const long tiles = (long)((M + cands[i].bm - 1) / cands[i].bm) * ((ncols + cpt - 1) / cpt);
-    const double rounds = (double)((tiles + 255) / 256);
-    const double t = rounds * cands[i].bm * cands[i].bn / cands[i].eff;
+  for (int i = 0; i < (int)(sizeof(cands) / sizeof(cands[0])); ++i) {
+    const Cand& c = cands[i];
+    if (dual && (c.bn / (32 * c.wn)) % 2) continue;
+    const int cpt = dual ? c.bn / 2 : c.bn;
+    const long tiles = (long)((M + c.bm - 1) / c.bm) * ((ncols + cpt - 1) / cpt);
+    const long slots = 256L * c.per_cu;
+    const double t = (double)((tiles + slots - 1) / slots) * c.per_cu * c.bm * c.bn / c.eff;
     if (t < best_t * 0.999) { best_t = t; best = i; }
   }
   switch (best) {
-    case 0: return tile_launch<256, 256>(A, B, out, M, N, K, F, dual, st);
-    case 1: return tile_launch<256, 128>(A, B, out, M, N, K, F, dual, st);
-    default: return tile_launch<128, 128>(A, B, out, M, N, K, F, dual, st);
+    case 0: return tile_launch<256, 256, 4>(A, B, out, M, N, K, F, dual, st);
+    case 1: return tile_launch<256, 128, 4>(A, B, out, M, N, K, F, dual, st);
+    case 2: return tile_launch<256, 128, 2>(A, B, out, M, N, K, F, dual, st);
+    case 3: return tile_launch<128, 128, 4>(A, B, out, M, N, K, F, dual, st);
+    default: return tile_launch<128, 128, 2>(A, B, out, M, N, K, F, dual, st);
   }
 }
 
@@ -492,7 +505,7 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {
       const int mt = (M + 127) / 128, nt = (N + 127) / 128;
-      DORY_LAUNCH((k_gemm_tile<128, 128, false>), dim3(mt * nt, S), dim3(256), 0, st, (const bf16_t*)A,
+      DORY_LAUNCH((k_gemm_tile<128, 128, false, 4>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
                   (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
       const size_t outs = (size_t)M * (dual ? F : N);
       if (dual)
