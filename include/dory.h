@@ -175,6 +175,12 @@ dory_status dory_seq_len(const dory_ctx* ctx, int32_t seq_id, int32_t* len);
 dory_status dory_kv_bytes_in_use(const dory_ctx* ctx, size_t* bytes);
 dory_status dory_get_stats(const dory_ctx* ctx, dory_stats* out);
 
+/* Device-side error flags raised since the last reset (synchronises the
+ * stream): bit 0 = a token id outside 0..V-1 reached the embedding (it was
+ * clamped into range, so that call's outputs are not those of the given ids).
+ * With reset != 0 the flags are cleared afterwards. */
+dory_status dory_device_flags(dory_ctx* ctx, int32_t* flags, int32_t reset);
+
 /* Copy the final hidden states (output of the output stack, fp32 [rows, d]) of
  * the previous prefill/decode call's last `rows` rows to dst_dev. Enqueued. */
 dory_status dory_last_hidden(dory_ctx* ctx, float* dst_dev, int32_t rows);

@@ -81,6 +81,15 @@ DORY_DEV float block_sum(float v, float* red, int nwaves) {
   return s;
 }
 
+// Value-row position of token t (0..15) inside a KV page: t with bits 2 and 3
+// swapped, so the 8 tokens one lane covers in a 32x32 score tile are contiguous.
+DORY_DEV constexpr int vperm(int t) { return (t & 3) | ((t >> 3) & 1) << 2 | ((t >> 2) & 1) << 3; }
+
+// Online-softmax rescale factor exp(m_old - m_new), 0 when nothing was accumulated yet.
+DORY_DEV float safe_scale(float m_old, float m_new) { return m_old == -INFINITY ? 0.f : __expf(m_old - m_new); }
+
+DORY_DEV float silu(float z) { return z / (1.f + __expf(-z)); }
+
 // The smallest positive normal float: lower bound of a sum of squares before
 // the reciprocal square root, so a zero vector yields zeros instead of NaN.
 #define DORY_TINY_SS 1.17549435e-38f

@@ -809,6 +809,19 @@ dory_status dory_get_stats(const dory_ctx* c, dory_stats* out) {
   return DORY_OK;
 }
 
+dory_status dory_device_flags(dory_ctx* c, int32_t* flags, int32_t reset) {
+  if (!c || !flags) return DORY_E_INVALID;
+  *flags = 0;
+  if (c->dry) return DORY_OK;
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, c->W(c->L.err), 4, hipMemcpyDeviceToHost, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e == hipSuccess && reset) e = hipMemsetAsync(c->W(c->L.err), 0, 4, c->stream);
+  if (e != hipSuccess) return fail(c, DORY_E_HIP, "reading device flags: %s", hipGetErrorString(e));
+  *flags = v;
+  return DORY_OK;
+}
+
 dory_status dory_last_hidden(dory_ctx* c, float* dst, int32_t rows) {
   if (!c || !dst) return DORY_E_INVALID;
   if (rows < 1 || rows > c->last_rows) return fail(c, DORY_E_INVALID, "rows %d outside 1..%d", rows, c->last_rows);

@@ -25,10 +25,6 @@
 
 namespace dory {
 
-DORY_DEV constexpr int vperm(int t) { return (t & 3) | ((t >> 3) & 1) << 2 | ((t >> 2) & 1) << 3; }
-
-DORY_DEV float safe_scale(float m_old, float m_new) { return m_old == -INFINITY ? 0.f : __expf(m_old - m_new); }
-
 // ---------------------------------------------------------------- rotary + norm + KV write
 
 // One wave per (row, head). Heads 0..H-1 are queries: q^ = N(RoPE(q)) -> q_out.
@@ -197,41 +193,44 @@ __global__ void __launch_bounds__(ATT_THREADS) k_attn_rows(
   }
 }
 
-// Merge split partials: grid rows*H, block max(64, dh) threads. The first wave
-// turns the split maxima into weights exp(m_s - M) (LDS) and the total sum;
-// then thread e sums dim e over the splits with independent loads.
+// Merge split partials: grid rows*H, block max(64, dh) threads; thread e owns
+// output dim e. Splits are combined 16 at a time with a running maximum; the 48
+// loads of a group (maxima and sums are the same for every thread) are issued
+// together, so a merge of <= 16 splits is one memory round trip.
 template <typename T>
 __global__ void __launch_bounds__(128) k_attn_merge(const float* __restrict__ part_ml,
                                                     const float* __restrict__ part_o, int splits, int dh,
                                                     T* __restrict__ out) {
-  __shared__ float sw[64];
-  __shared__ float sL;
   const size_t rh = blockIdx.x;
   const int e = threadIdx.x;
-  if (e < 64) {
-    const float ms = e < splits ? part_ml[2 * (rh * splits + e)] : -INFINITY;
-    const float ls = e < splits ? part_ml[2 * (rh * splits + e) + 1] : 0.f;
-    const float M = wave_max(ms);
-    const float c = safe_scale(ms, M);
-    sw[e] = c;
-    const float L = wave_sum(ls * c);
-    if (e == 0) sL = L;
-  }
-  __syncthreads();
-  if (e >= dh) return;
-  const float* po = part_o + rh * splits * dh + e;
-  float A4[4] = {0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 8 <= splits; s += 8) {
-    float v[8];
+  const bool own = e < dh;
+  const float* ml = part_ml + 2 * rh * splits;
+  const float* po = part_o + rh * splits * dh + (own ? e : 0);
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += 16) {
+    float mv[16], lv[16], ov[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = po[(size_t)(s + i) * dh];
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = s0 + i < splits;
+      mv[i] = ok ? ml[2 * (s0 + i)] : -INFINITY;
+      lv[i] = ok ? ml[2 * (s0 + i) + 1] : 0.f;
+      ov[i] = ok ? po[(size_t)(s0 + i) * dh] : 0.f;
+    }
+    float mc = M;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) A4[i & 3] += sw[s + i] * v[i];
+    for (int i = 0; i < 16; ++i) mc = fmaxf(mc, mv[i]);
+    const float c = safe_scale(M, mc);
+    A *= c;
+    L *= c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float w = safe_scale(mv[i], mc);
+      A += w * ov[i];
+      L += w * lv[i];
+    }
+    M = mc;
   }
-  for (; s < splits; ++s) A4[0] += sw[s] * po[(size_t)s * dh];
-  const float A = (A4[0] + A4[1]) + (A4[2] + A4[3]);
-  St<T>::st(out, rh * dh + e, sL > 0.f ? A / sL : 0.f);
+  if (own) St<T>::st(out, rh * dh + e, L > 0.f ? A / L : 0.f);
 }
 
 // ---------------------------------------------------------------- bf16 split-key attention, d_h = 128

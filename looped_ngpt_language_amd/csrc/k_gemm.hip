@@ -4,17 +4,14 @@
 // fused gate/up weight (z = silu(A.Bg^T) * (A.Bu^T), Bg = rows 0..F-1 and
 // Bu = rows F..2F-1 of B) stored in the model's storage type.
 //
-//  - k_gemm_mfma: bf16 MFMA (v_mfma_f32_32x32x16_bf16), 128x128x64 tiles,
-//    4 waves of 64x64, LDS double-buffered; for the bf16 model at M > 2.
-//  - k_gemv_bf16: weight-streaming kernel for M <= 2 rows (decode); the x rows
-//    stay in registers, every weight byte is read once, dot2 bf16 FMA.
+//  - k_gemm_tile: bf16 MFMA (v_mfma_f32_32x32x16_bf16) tiles of 128..256 rows
+//    and columns, LDS double-buffered, optional split-K; for the bf16 model at
+//    M > 2 (M <= 2 goes to the weight-streaming GEMV of k_gemv.hip).
 //  - k_gemm_f32: plain FMA tiles for the fp32 model.
 #include "common.h"
 #include "kernels.h"
 
 namespace dory {
-
-DORY_DEV float silu(float z) { return z / (1.f + __expf(-z)); }
 
 // ------------------------------------------------------------------ fp32 tiles
 
@@ -235,160 +232,7 @@ __global__ void __launch_bounds__(128 * WN) k_gemm_tile(const bf16_t* __restrict
   }
 }
 
-// ------------------------------------------------------------------ bf16 GEMV (M <= 2)
-
-// One wave per group of R output rows; lane l reads 16-byte chunks l, l+64, ...
-// of each weight row (KCH chunks per lane, K = 512*KCH). The weight loads are
-// issued first. With RES the input rows are not read from X: the workgroup
-// first applies the pending normalised residual step of the previous sublayer,
-//   x = N(h + alpha * (N(y) - h))       (h, y fp32 [M, K]; alpha [K])
-// keeps bf16(x) in LDS as the GEMV input and (workgroup 0 only) writes the fp32
-// x to hout for the next residual step -- while the weights are in flight.
-template <int KCH, int R, int MR, bool DUAL, bool RES>
-__global__ void __launch_bounds__(256) k_gemv_bf16(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
-                                                   void* __restrict__ Y, int M, int N, int F,
-                                                   const float* __restrict__ rh, const float* __restrict__ ry,
-                                                   const float* __restrict__ ralpha, float* __restrict__ hout) {
-  constexpr int K = KCH * 512;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = blockIdx.x * 4 + (tid >> 6);
-  const int nrows_out = DUAL ? F : N;
-  const int r0 = wave * R;
-  const bool active = r0 < nrows_out;
-  constexpr int NB = DUAL ? 2 : 1;
-  u32x4_t wr[NB][R][KCH];
-  if (active) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int n = min(r0 + r, nrows_out - 1) + b * F;
-        const bf16_t* wp = W + (size_t)n * K + (size_t)lane * 8;
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) wr[b][r][c] = *reinterpret_cast<const u32x4_t*>(wp + c * 512);
-      }
-  }
-  uint4 xr[MR][KCH];
-  if constexpr (RES) {
-    constexpr int EPT = K / 256;
-    __shared__ __attribute__((aligned(16))) bf16_t xs[MR][K];
-    __shared__ float red[4];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      if (m >= M) break;
-      float hv[EPT], yv[EPT];
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int i = tid + 256 * e;
-        hv[e] = rh[(size_t)m * K + i];
-        yv[e] = ry[(size_t)m * K + i];
-        ss += yv[e] * yv[e];
-      }
-      const float iy = rsqrtf(fmaxf(block_sum(ss, red, 4), DORY_TINY_SS));
-      float st = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int i = tid + 256 * e;
-        hv[e] += ralpha[i] * (yv[e] * iy - hv[e]);
-        st += hv[e] * hv[e];
-      }
-      const float ih = rsqrtf(fmaxf(block_sum(st, red, 4), DORY_TINY_SS));
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int i = tid + 256 * e;
-        const float v = hv[e] * ih;
-        xs[m][i] = f32_to_bf16(v);
-        if (blockIdx.x == 0) hout[(size_t)m * K + i] = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int c = 0; c < KCH; ++c)
-        xr[m][c] = m < M ? *reinterpret_cast<const uint4*>(&xs[m][(c * 64 + lane) * 8]) : make_uint4(0, 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int c = 0; c < KCH; ++c)
-        xr[m][c] = m < M ? *reinterpret_cast<const uint4*>(X + (size_t)m * K + (size_t)(c * 64 + lane) * 8)
-                         : make_uint4(0, 0, 0, 0);
-  }
-  if (!active) return;
-  float acc[NB][R][MR];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        float s = 0.f;
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-          const u32x4_t w = wr[b][r][c];
-          const uint4 x = xr[m][c];
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), s, false);
-        }
-        acc[b][r][m] = wave_sum(s);
-      }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int n = r0 + r;
-      if (n >= nrows_out) continue;
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        if (m >= M) continue;
-        if (DUAL)
-          reinterpret_cast<bf16_t*>(Y)[(size_t)m * F + n] = f32_to_bf16(silu(acc[0][r][m]) * acc[NB - 1][r][m]);
-        else
-          reinterpret_cast<float*>(Y)[(size_t)m * N + n] = acc[0][r][m];
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ launchers
-
-struct ResArgs {
-  const float *h, *y, *alpha;
-  float* hout;
-};
-
-template <int KCH, bool DUAL, bool RES>
-static hipError_t gemv_k(const bf16_t* X, const bf16_t* W, void* Y, int M, int N, int F, const ResArgs& ra,
-                         hipStream_t st) {
-  const int rows_out = DUAL ? F : N;
-  constexpr int R = KCH >= 16 ? 1 : 2;  // keeps the weight registers of a wave near 128 VGPRs
-  const int waves = (rows_out + R - 1) / R;
-  const dim3 grid((waves + 3) / 4);
-  if (M == 1)
-    DORY_LAUNCH((k_gemv_bf16<KCH, R, 1, DUAL, RES>), grid, dim3(256), 0, st, X, W, Y, M, N, F, ra.h, ra.y,
-                       ra.alpha, ra.hout);
-  else
-    DORY_LAUNCH((k_gemv_bf16<KCH, R, 2, DUAL, RES>), grid, dim3(256), 0, st, X, W, Y, M, N, F, ra.h, ra.y,
-                       ra.alpha, ra.hout);
-  return hipGetLastError();
-}
-
-template <bool DUAL, bool RES>
-static hipError_t gemv_dispatch(const bf16_t* X, const bf16_t* W, void* Y, int M, int N, int K, int F,
-                                const ResArgs& ra, hipStream_t st) {
-  switch (K) {
-    case 1024: return gemv_k<2, DUAL, RES>(X, W, Y, M, N, F, ra, st);
-    case 3072: return gemv_k<6, DUAL, RES>(X, W, Y, M, N, F, ra, st);
-    case 4096: return gemv_k<8, DUAL, RES>(X, W, Y, M, N, F, ra, st);
-    case 8192:
-      if constexpr (!RES) return gemv_k<16, DUAL, false>(X, W, Y, M, N, F, ra, st);
-      return hipErrorNotSupported;
-    default: return hipErrorNotSupported;
-  }
-}
 
 // Sum of split-K partials [S][M][N]: plain -> fp32 [M][N]; dual (N = 2F) ->
 // bf16 z[m][c] = silu(gate) * up with gate = column c, up = column F + c.
@@ -456,18 +300,6 @@ static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, 
   }
 }
 
-bool gemv_supported(int K) { return K == 1024 || K == 3072 || K == 4096 || K == 8192; }
-bool gemv_residual_supported(int K) { return K == 1024 || K == 3072 || K == 4096; }
-
-hipError_t launch_gemv_residual(bool dual, const void* W, void* out, int M, int N, int K, const float* h,
-                                const float* y, const float* alpha, float* hout, hipStream_t st) {
-  if (M < 1 || M > 2 || !gemv_residual_supported(K)) return hipErrorNotSupported;
-  const int F = dual ? N / 2 : 0;
-  const ResArgs ra{h, y, alpha, hout};
-  return dual ? gemv_dispatch<true, true>(nullptr, (const bf16_t*)W, out, M, N, K, F, ra, st)
-              : gemv_dispatch<false, true>(nullptr, (const bf16_t*)W, out, M, N, K, F, ra, st);
-}
-
 // out: fp32 [M,N] (plain) or storage-type z [M,F] (dual, N = 2F).
 // Few rows (3..256): 128x128 tiles leave most CUs idle, so K is split until the
 // grid has >= 256 workgroups (partials in `split_ws`, then a reduce kernel).
@@ -496,11 +328,7 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     return hipGetLastError();
   }
   if (K % MF_BK != 0) return hipErrorNotSupported;
-  if (M <= 2 && gemv_supported(K)) {
-    const ResArgs none{nullptr, nullptr, nullptr, nullptr};
-    return dual ? gemv_dispatch<true, false>((const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F, none, st)
-                : gemv_dispatch<false, false>((const bf16_t*)A, (const bf16_t*)B, out, M, N, K, F, none, st);
-  }
+  if (M <= 2 && gemv_supported(K)) return launch_gemv(dual, A, B, out, M, N, K, st);
   if (M <= 256 && split_ws) {
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {

@@ -63,6 +63,8 @@ hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t
 
 bool gemv_supported(int K);
 bool gemv_residual_supported(int K);
+// GEMV for M <= 2 bf16 rows (k_gemv.hip).
+hipError_t launch_gemv(bool dual, const void* X, const void* W, void* out, int M, int N, int K, hipStream_t st);
 // GEMV (M <= 2) whose input rows are N(h + alpha (N(y) - h)), computed in the prologue; the fp32
 // result is also written to hout (which must not alias h or y).
 hipError_t launch_gemv_residual(bool dual, const void* W, void* out, int M, int N, int K, const float* h,

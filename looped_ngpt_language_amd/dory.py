@@ -73,6 +73,7 @@ EXPORTS = {
     "dory_kv_bytes_in_use": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "dory_get_stats": (C.c_int, [C.c_void_p, C.POINTER(Stats)]),
     "dory_last_hidden": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
+    "dory_device_flags": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
     "dory_spec_decode": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "dory_set_timing": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -294,6 +295,12 @@ class Model:
         out = torch.empty((rows, self.shape.d_model), dtype=torch.float32, device=self.device)
         self._check(lib().dory_last_hidden(self.ctx, _ptr(out), int(rows)), "dory_last_hidden")
         return out
+
+    def device_flags(self, reset=True) -> int:
+        """Device error flags (bit 0: an out-of-range token id was clamped)."""
+        v = C.c_int32()
+        self._check(lib().dory_device_flags(self.ctx, C.byref(v), int(reset)), "dory_device_flags")
+        return v.value
 
     def set_timing(self, enable: bool):
         self._check(lib().dory_set_timing(self.ctx, 1 if enable else 0), "dory_set_timing")

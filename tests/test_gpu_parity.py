@@ -240,3 +240,20 @@ def test_mid_bf16_batched_decode(mode):
                 margin = o_lg[i][o_ids[i]] - o_lg[i][g_ids[s][i]]
                 assert margin < 2 * np.max(np.abs(g_lg[s][i] - o_lg[i]))
     m.close()
+
+
+def test_out_of_range_token_raises_device_flag(tiny):
+    """A token id outside 0..V-1 is clamped by the embedding and reported through dory_device_flags."""
+    _, m = tiny
+    say("[tiny fp32] out-of-range token -> device flag bit 0")
+    for s in range(4):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    assert m.device_flags() == 0
+    m.prefill(0, [3, synth.TINY.vocab + 5, 7], 1)
+    assert m.device_flags() == 1
+    assert m.device_flags() == 0      # the previous call reset it
+    m.prefill(1, [3, 4, 5], 1)
+    assert m.device_flags() == 0
+    m.release(0)
+    m.release(1)
