@@ -78,25 +78,22 @@ constexpr int MF_BK = 64;
 //  A: lane l holds A[l%32][8*(l/32) .. +8);  B: lane l holds B^T[l%32][8*(l/32) .. +8)
 //  D: element v of lane l is D[8*(v/4) + 4*(l/32) + v%4][l%32].
 //
-// Tile BM x BN x 64, 256 threads as 2x2 waves of (BM/2) x (BN/2), TM x TN MFMA
-// tiles of 32x32 per wave. Operands go straight from global memory into LDS
-// (global_load_lds_dwordx4: lane l of a wave instruction fills bytes
-// 16l..16l+15 of a 1 KB LDS block = 8 tile rows of 64 bf16), double-buffered:
-// the next k-tile's loads are in flight while the current one is multiplied.
-// Within a row the eight 16-byte chunks are XOR-swizzled by (row & 7), so the
-// MFMA operand reads (32 rows, one chunk) hit distinct banks.
+// Tile BM x BN x 64, 2 x WN waves of (BM/2) x (BN/WN), TM x TN MFMA tiles of
+// 32x32 per wave. LDS is double-buffered; the operand tiles of k-tile kt+1 are
+// loaded into registers (16 bytes per lane per load: lane l of a wave load
+// covers bytes 16l..16l+15 of a 1 KB block = 8 tile rows of 64 bf16) while
+// k-tile kt is multiplied, and written to the idle LDS buffer afterwards, so the
+// global-load latency overlaps a whole k-tile of MFMA work. (Direct
+// global->LDS loads would save the register round trip, but the compiler then
+// waits for every outstanding load before each LDS read, since it cannot tell
+// the two buffers apart.) Within a row the eight 16-byte chunks are
+// XOR-swizzled by (row & 7), so the MFMA operand reads (32 rows, one chunk)
+// hit distinct banks.
 // The grid is 1-D; workgroup b runs on XCD b % 8, and tiles are dealt so each
 // XCD walks a contiguous run of weight-column tiles over all row tiles, which
 // keeps every weight tile's re-reads inside one XCD's L2.
 // Dual: the tile's B rows are BN/2 gate rows then the BN/2 matching up rows;
 // gate tile j pairs with up tile j + TN/2 in the same lanes for the epilogue.
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// 16 bytes per lane from global memory into LDS at lds_block + 16 * lane.
-DORY_DEV void load_lds16(const bf16_t* src, bf16_t* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_block, 16, 0, 0);
-}
-
 // Split-K: blockIdx.y selects the K range [y * k_len, (y+1) * k_len); with
 // gridDim.y > 1 (plain only) the fp32 tile goes to partial slice y of Cv,
 // [gridDim.y][M][N], summed afterwards by k_splitk_reduce.
@@ -162,25 +159,25 @@ __global__ void __launch_bounds__(128 * WN) k_gemm_tile(const bf16_t* __restrict
 
   const int nk = k_len / MF_BK;
   float* const Cf = reinterpret_cast<float*>(Cv) + (size_t)blockIdx.y * M * N;
-#pragma unroll
-  for (int i = 0; i < IA; ++i)
-    load_lds16(asrc[i], &As[0][(wid * IA + i) * 512]);
-#pragma unroll
-  for (int i = 0; i < IB; ++i)
-    load_lds16(bsrc[i], &Bs[0][(wid * IB + i) * 512]);
+  u32x4_t ra[IA], rb[IB];
+#define DORY_GLOAD(K1)                                                                                           \
+  do {                                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < IA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + (K1));    \
+    _Pragma("unroll") for (int i = 0; i < IB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bsrc[i] + (K1));    \
+  } while (0)
+#define DORY_SWRITE(S)                                                                                           \
+  do {                                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < IA; ++i)                                                               \
+      *reinterpret_cast<u32x4_t*>(&As[S][(wid * IA + i) * 512 + lane * 8]) = ra[i];                              \
+    _Pragma("unroll") for (int i = 0; i < IB; ++i)                                                               \
+      *reinterpret_cast<u32x4_t*>(&Bs[S][(wid * IB + i) * 512 + lane * 8]) = rb[i];                              \
+  } while (0)
+  DORY_GLOAD(0);
+  DORY_SWRITE(0);
+  if (nk > 1) DORY_GLOAD(MF_BK);
+  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile kt have landed
-    __syncthreads();                // ... and every wave's; stage cur^1 is free again
-    if (kt + 1 < nk) {
-      const int k1 = (kt + 1) * MF_BK;
-#pragma unroll
-      for (int i = 0; i < IA; ++i)
-        load_lds16(asrc[i] + k1, &As[cur ^ 1][(wid * IA + i) * 512]);
-#pragma unroll
-      for (int i = 0; i < IB; ++i)
-        load_lds16(bsrc[i] + k1, &Bs[cur ^ 1][(wid * IB + i) * 512]);
-    }
     const bf16_t* as = As[cur];
     const bf16_t* bs = Bs[cur];
 #pragma unroll
@@ -203,7 +200,14 @@ __global__ void __launch_bounds__(128 * WN) k_gemm_tile(const bf16_t* __restrict
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+    if (kt + 1 < nk) {
+      DORY_SWRITE(cur ^ 1);  // every wave finished reading buffer cur^1 before the last barrier
+      if (kt + 2 < nk) DORY_GLOAD((kt + 2) * MF_BK);
+    }
+    __syncthreads();
   }
+#undef DORY_GLOAD
+#undef DORY_SWRITE
 
   const int col = lane & 31;
 #pragma unroll
