@@ -78,7 +78,7 @@ constexpr int MF_BK = 64;
 //  A: lane l holds A[l%32][8*(l/32) .. +8);  B: lane l holds B^T[l%32][8*(l/32) .. +8)
 //  D: element v of lane l is D[8*(v/4) + 4*(l/32) + v%4][l%32].
 //
-// Tile BM x BN x 64, 2 x WN waves of (BM/2) x (BN/WN), TM x TN MFMA tiles of
+// Tile BM x BN x 64, WM x WN waves of (BM/WM) x (BN/WN), TM x TN MFMA tiles of
 // 32x32 per wave. LDS is double-buffered; the operand tiles of k-tile kt+1 are
 // loaded into registers (16 bytes per lane per load: lane l of a wave load
 // covers bytes 16l..16l+15 of a 1 KB block = 8 tile rows of 64 bf16) while
@@ -97,15 +97,15 @@ constexpr int MF_BK = 64;
 // Split-K: blockIdx.y selects the K range [y * k_len, (y+1) * k_len); with
 // gridDim.y > 1 (plain only) the fp32 tile goes to partial slice y of Cv,
 // [gridDim.y][M][N], summed afterwards by k_splitk_reduce.
-// WN waves along N (2 or 4) times 2 along M: 4 or 8 waves per workgroup.
-template <int BM, int BN, bool DUAL, int WN = 2>
-__global__ void __launch_bounds__(128 * WN) k_gemm_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
-                                                        void* __restrict__ Cv, int M, int N, int K, int F,
-                                                        int m_tiles, int n_tiles, int k_len) {
-  constexpr int WAVES = 2 * WN;
-  constexpr int TM = BM / 64, TN = BN / (32 * WN);
+template <int BM, int BN, int WM, int WN, bool DUAL>
+__global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+                                                            void* __restrict__ Cv, int M, int N, int K, int F,
+                                                            int m_tiles, int n_tiles, int k_len) {
+  constexpr int WAVES = WM * WN;
+  constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
   constexpr int IA = BM / (8 * WAVES), IB = BN / (8 * WAVES);  // 1 KB load instructions per wave per k-tile
-  static_assert(TN >= 1 && IA >= 1 && IB >= 1 && (!DUAL || TN % 2 == 0), "tile shape");
+  static_assert(TM >= 1 && TN >= 1 && IA * 8 * WAVES == BM && IB * 8 * WAVES == BN && (!DUAL || TN % 2 == 0),
+                "tile shape");
   __shared__ __attribute__((aligned(1024))) bf16_t As[2][BM * MF_BK];
   __shared__ __attribute__((aligned(1024))) bf16_t Bs[2][BN * MF_BK];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(128 * WN) k_gemm_tile(const bf16_t* __restrict
     if (DUAL) brow[j] = j < TN / 2 ? wn * (BN / (2 * WN)) + j * 32 : BN / 2 + wn * (BN / (2 * WN)) + (j - TN / 2) * 32;
     else brow[j] = wn * (BN / WN) + j * 32;
   }
-  const int arow0 = wm * (BM / 2) + (lane & 31);
+  const int arow0 = wm * (BM / WM) + (lane & 31);
   const int khalf = lane >> 5;
 
   const int nk = k_len / MF_BK;
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(128 * WN) k_gemm_tile(const bf16_t* __restrict
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int gm = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int gm = m0 + wm * (BM / WM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (gm >= M) continue;
       if (DUAL) {
 #pragma unroll
@@ -257,50 +257,53 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
   else reinterpret_cast<float*>(out)[idx] = a;
 }
 
-template <int BM, int BN, int WN = 2>
+template <int BM, int BN, int WM, int WN>
 static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
                               hipStream_t st) {
   const int ncols = dual ? F : N;
   const int cols_per_tile = dual ? BN / 2 : BN;
   const int mt = (M + BM - 1) / BM, nt = (ncols + cols_per_tile - 1) / cols_per_tile;
-  const dim3 grid(mt * nt);
+  const dim3 grid(mt * nt), block(64 * WM * WN);
   if (dual) {
     if constexpr ((BN / (32 * WN)) % 2 == 0)
-      DORY_LAUNCH((k_gemm_tile<BM, BN, true, WN>), grid, dim3(128 * WN), 0, st, A, B, out, M, N, K, F, mt, nt, K);
+      DORY_LAUNCH((k_gemm_tile<BM, BN, WM, WN, true>), grid, block, 0, st, A, B, out, M, N, K, F, mt, nt, K);
     else
       return hipErrorNotSupported;
-  } else
-    DORY_LAUNCH((k_gemm_tile<BM, BN, false, WN>), grid, dim3(128 * WN), 0, st, A, B, out, M, N, K, F, mt, nt, K);
+  } else {
+    DORY_LAUNCH((k_gemm_tile<BM, BN, WM, WN, false>), grid, block, 0, st, A, B, out, M, N, K, F, mt, nt, K);
+  }
   return hipGetLastError();
 }
 
-// Tile shape: the candidate with the least estimated time. A round is one
-// workgroup per CU (256x256 tiles need 128 KB of LDS) or two sharing a CU
-// (128x128); a round costs per_cu tiles' area over the shape's measured
-// relative throughput (256x256 / 8 waves = 1).
+// Tile shape: the candidate with the least estimated time, taken as the tiles
+// of the busiest CU (tiles dealt evenly over 256 CUs) times the tile's area over
+// the shape's measured per-CU rate (TFLOP/s per CU on the ~4B prefill shapes:
+// 256x256 on the gate/up projection, 128x192 on down and o, 256x160 on qkv).
+// Shapes that split N into exactly 256 equal tiles (one per CU) avoid the
+// half-empty last round that 256x256 or 128x128 tiles leave on N = 3072.
 static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
                                    hipStream_t st) {
   const int ncols = dual ? F : N;
-  struct Cand { int bm, bn, wn, per_cu; double eff; };
-  static const Cand cands[] = {{256, 256, 4, 1, 1.0}, {256, 128, 4, 1, 0.8}, {256, 128, 2, 1, 0.7},
-                               {128, 128, 4, 2, 0.75}, {128, 128, 2, 2, 0.6}};
+  struct Cand { int bm, bn, tn; double rate; };  // tn: MFMA column tiles per wave (dual needs an even count)
+  static const Cand cands[] = {{256, 256, 2, 4.0}, {128, 192, 3, 3.5}, {256, 160, 5, 3.45},
+                               {128, 320, 5, 3.3}, {256, 128, 2, 3.6}, {128, 128, 2, 3.6}};
   int best = 0;
   double best_t = 1e300;
   for (int i = 0; i < (int)(sizeof(cands) / sizeof(cands[0])); ++i) {
     const Cand& c = cands[i];
-    if (dual && (c.bn / (32 * c.wn)) % 2) continue;
+    if (dual && c.tn % 2) continue;
     const int cpt = dual ? c.bn / 2 : c.bn;
     const long tiles = (long)((M + c.bm - 1) / c.bm) * ((ncols + cpt - 1) / cpt);
-    const long slots = 256L * c.per_cu;
-    const double t = (double)((tiles + slots - 1) / slots) * c.per_cu * c.bm * c.bn / c.eff;
+    const double t = (double)((tiles + 255) / 256) * c.bm * c.bn / c.rate;
     if (t < best_t * 0.999) { best_t = t; best = i; }
   }
   switch (best) {
-    case 0: return tile_launch<256, 256, 4>(A, B, out, M, N, K, F, dual, st);
-    case 1: return tile_launch<256, 128, 4>(A, B, out, M, N, K, F, dual, st);
-    case 2: return tile_launch<256, 128, 2>(A, B, out, M, N, K, F, dual, st);
-    case 3: return tile_launch<128, 128, 4>(A, B, out, M, N, K, F, dual, st);
-    default: return tile_launch<128, 128, 2>(A, B, out, M, N, K, F, dual, st);
+    case 0: return tile_launch<256, 256, 2, 4>(A, B, out, M, N, K, F, dual, st);
+    case 1: return tile_launch<128, 192, 4, 2>(A, B, out, M, N, K, F, dual, st);
+    case 2: return tile_launch<256, 160, 4, 1>(A, B, out, M, N, K, F, dual, st);
+    case 3: return tile_launch<128, 320, 2, 2>(A, B, out, M, N, K, F, dual, st);
+    case 4: return tile_launch<256, 128, 4, 2>(A, B, out, M, N, K, F, dual, st);
+    default: return tile_launch<128, 128, 2, 2>(A, B, out, M, N, K, F, dual, st);
   }
 }
 
@@ -337,7 +340,7 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {
       const int mt = (M + 127) / 128, nt = (N + 127) / 128;
-      DORY_LAUNCH((k_gemm_tile<128, 128, false, 4>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
+      DORY_LAUNCH((k_gemm_tile<128, 128, 2, 4, false>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
                   (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
       const size_t outs = (size_t)M * (dual ? F : N);
       if (dual)
