@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-batched", action="store_true")
+    p.add_argument("--no-decode", action="store_true",
+                   help="prefill only (for profiling): the JSON value is then the prefill rate at --k")
     p.add_argument("--batched-steps", type=int, default=16)
     p.add_argument("--long", action="store_true", help="also run the 131072-token prompt at k=4 and "
                    "self-speculative decoding (adds a few minutes)")
@@ -131,6 +133,21 @@ def main():
                     kern[name] = {"ms": v["ms"], "tflop_s": tf, "launches": v["launches"]}
                     log(f"         {name:22s} {v['launches']:5d} launches  {v['ms']:8.2f} ms  {tf:7.1f} TFLOP/s")
             res["prefill"][k]["kernels"] = kern
+
+    if args.no_decode:
+        head = res["prefill"].get(args.k) or next(iter(res["prefill"].values()))
+        dom_name, dom = max(head["kernels"].items(), key=lambda x: x[1]["ms"])
+        print(json.dumps({
+            "metric": f"prefill tok/s ({args.prefill_len}-token prompt, k={args.k})", "value": round(head["tok_s"], 1),
+            "unit": "tok/s", "n_gpus": 1, "steps": 3, "warmup": 1, "ms_per_step": round(head["ms"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded random weights and uniform-random prompt ids)",
+            "config": {"workload": f"looped nGPT ~4B prefill, {args.prefill_len} tokens, k={args.k}"},
+            "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": round(dom["tflop_s"], 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(dom["tflop_s"] / BF16_PEAK_TFLOPS, 4), "traffic": None},
+            "cpu_baseline": None}), flush=True)
+        return
 
     # ---------------------------------------------------------------- decode
     ptoks = torch.from_numpy(prompt[:args.prompt]).to("cuda:0")
