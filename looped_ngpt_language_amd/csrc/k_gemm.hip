@@ -86,9 +86,13 @@ constexpr int MF_BK = 64;
 // global-load latency overlaps a whole k-tile of MFMA work. (Direct
 // global->LDS loads would save the register round trip, but the compiler then
 // waits for every outstanding load before each LDS read, since it cannot tell
-// the two buffers apart.) Within a row the eight 16-byte chunks are
-// XOR-swizzled by (row & 7), so the MFMA operand reads (32 rows, one chunk)
-// hit distinct banks.
+// the two buffers apart.) With PF2 two register sets alternate and each k-tile
+// is requested two k-tiles ahead (more latency cover, more registers).
+// LDS banks: gfx950 serves a 16-byte-per-lane read to 64 banks of 4 bytes, so
+// the 16 rows a pass touches (128 bytes each) must land on 16 distinct
+// (row parity, chunk) pairs: the eight 16-byte chunks of row r are XOR-swizzled
+// by (r >> 1) & 7 (rows r, r + 1 share the swizzle but sit in opposite bank
+// halves), which the LDS conflict counter reads as zero.
 // The grid is 1-D; workgroup b runs on XCD b % 8, and tiles are dealt so each
 // XCD walks a contiguous run of weight-column tiles over all row tiles, which
 // keeps every weight tile's re-reads inside one XCD's L2.
@@ -97,7 +101,9 @@ constexpr int MF_BK = 64;
 // Split-K: blockIdx.y selects the K range [y * k_len, (y+1) * k_len); with
 // gridDim.y > 1 (plain only) the fp32 tile goes to partial slice y of Cv,
 // [gridDim.y][M][N], summed afterwards by k_splitk_reduce.
-template <int BM, int BN, int WM, int WN, bool DUAL>
+DORY_DEV int lds_swz(int r) { return (r >> 1) & 7; }
+
+template <int BM, int BN, int WM, int WN, bool DUAL, bool PF2>
 __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
                                                             void* __restrict__ Cv, int M, int N, int K, int F,
                                                             int m_tiles, int n_tiles, int k_len) {
@@ -119,16 +125,16 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
   const int m0 = tm * BM;
   const int n0 = DUAL ? tn * (BN / 2) : tn * BN;  // first C column (plain) or z column (dual)
 
-  // this lane's global source rows and swizzled chunk for each load instruction
+  // this lane's global source row and chunk for each load instruction: lane l
+  // fills physical slot l & 7 of tile row 8i + l/8, i.e. logical chunk (l & 7) ^ swz
   const int lrow = lane >> 3;                  // row within the 8-row block
-  const int lchunk = (lane & 7) ^ lrow;        // logical k-chunk stored at physical slot lane & 7
   const int kbase = blockIdx.y * k_len;
   const bf16_t* asrc[IA];
   const bf16_t* bsrc[IB];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
     const int r = (wid * IA + i) * 8 + lrow;
-    asrc[i] = A + (size_t)min(m0 + r, M - 1) * K + kbase + lchunk * 8;
+    asrc[i] = A + (size_t)min(m0 + r, M - 1) * K + kbase + ((lane & 7) ^ lds_swz(r)) * 8;
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
@@ -136,7 +142,7 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
     int gn;
     if (DUAL) gn = (r < BN / 2) ? min(n0 + r, F - 1) : F + min(n0 + r - BN / 2, F - 1);
     else gn = min(n0 + r, N - 1);
-    bsrc[i] = B + (size_t)gn * K + kbase + lchunk * 8;
+    bsrc[i] = B + (size_t)gn * K + kbase + ((lane & 7) ^ lds_swz(r)) * 8;
   }
 
   f32x16_t acc[TM][TN];
@@ -159,53 +165,76 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
 
   const int nk = k_len / MF_BK;
   float* const Cf = reinterpret_cast<float*>(Cv) + (size_t)blockIdx.y * M * N;
-  u32x4_t ra[IA], rb[IB];
-#define DORY_GLOAD(K1)                                                                                           \
+#define DORY_GLOAD(RA, RB, K1)                                                                                   \
   do {                                                                                                           \
-    _Pragma("unroll") for (int i = 0; i < IA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + (K1));    \
-    _Pragma("unroll") for (int i = 0; i < IB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bsrc[i] + (K1));    \
+    _Pragma("unroll") for (int i = 0; i < IA; ++i) RA[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + (K1));    \
+    _Pragma("unroll") for (int i = 0; i < IB; ++i) RB[i] = *reinterpret_cast<const u32x4_t*>(bsrc[i] + (K1));    \
   } while (0)
-#define DORY_SWRITE(S)                                                                                           \
+#define DORY_SWRITE(RA, RB, S)                                                                                   \
   do {                                                                                                           \
     _Pragma("unroll") for (int i = 0; i < IA; ++i)                                                               \
-      *reinterpret_cast<u32x4_t*>(&As[S][(wid * IA + i) * 512 + lane * 8]) = ra[i];                              \
+      *reinterpret_cast<u32x4_t*>(&As[S][(wid * IA + i) * 512 + lane * 8]) = RA[i];                              \
     _Pragma("unroll") for (int i = 0; i < IB; ++i)                                                               \
-      *reinterpret_cast<u32x4_t*>(&Bs[S][(wid * IB + i) * 512 + lane * 8]) = rb[i];                              \
+      *reinterpret_cast<u32x4_t*>(&Bs[S][(wid * IB + i) * 512 + lane * 8]) = RB[i];                              \
   } while (0)
-  DORY_GLOAD(0);
-  DORY_SWRITE(0);
-  if (nk > 1) DORY_GLOAD(MF_BK);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bf16_t* as = As[cur];
-    const bf16_t* bs = Bs[cur];
-#pragma unroll
-    for (int ks = 0; ks < MF_BK / 16; ++ks) {
-      const int ch = 2 * ks + khalf;  // logical 16-byte chunk of this lane's 8 k values
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = arow0 + i * 32;
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&as[r * 64 + ((ch ^ (r & 7)) << 3)]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = brow[j] + (lane & 31);
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&bs[r * 64 + ((ch ^ (r & 7)) << 3)]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      DORY_SWRITE(cur ^ 1);  // every wave finished reading buffer cur^1 before the last barrier
-      if (kt + 2 < nk) DORY_GLOAD((kt + 2) * MF_BK);
-    }
+#define DORY_COMPUTE(S)                                                                                          \
+  do {                                                                                                           \
+    const bf16_t* as = As[S];                                                                                    \
+    const bf16_t* bs = Bs[S];                                                                                    \
+    _Pragma("unroll") for (int ks = 0; ks < MF_BK / 16; ++ks) {                                                  \
+      const int ch = 2 * ks + khalf; /* logical 16-byte chunk of this lane's 8 k values */                       \
+      bf16x8_t af[TM], bfr[TN];                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                                           \
+        const int r = arow0 + i * 32;                                                                            \
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&as[r * 64 + ((ch ^ lds_swz(r)) << 3)]);                      \
+      }                                                                                                          \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                                           \
+        const int r = brow[j] + (lane & 31);                                                                     \
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&bs[r * 64 + ((ch ^ lds_swz(r)) << 3)]);                     \
+      }                                                                                                          \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                             \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                           \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);                \
+    }                                                                                                            \
+  } while (0)
+  u32x4_t ra[IA], rb[IB];
+  if constexpr (!PF2) {
+    DORY_GLOAD(ra, rb, 0);
+    DORY_SWRITE(ra, rb, 0);
+    if (nk > 1) DORY_GLOAD(ra, rb, MF_BK);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      DORY_COMPUTE(cur);
+      if (kt + 1 < nk) {
+        DORY_SWRITE(ra, rb, cur ^ 1);  // every wave finished reading buffer cur^1 before the last barrier
+        if (kt + 2 < nk) DORY_GLOAD(ra, rb, (kt + 2) * MF_BK);
+      }
+      __syncthreads();
+    }
+  } else {
+    // register set 0 carries the odd k-tiles, set 1 the even ones (from tile 2)
+    u32x4_t ra1[IA], rb1[IB];
+    DORY_GLOAD(ra, rb, 0);
+    DORY_SWRITE(ra, rb, 0);
+    if (nk > 1) DORY_GLOAD(ra, rb, MF_BK);
+    if (nk > 2) DORY_GLOAD(ra1, rb1, 2 * MF_BK);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      DORY_COMPUTE(0);
+      if (kt + 1 >= nk) break;
+      DORY_SWRITE(ra, rb, 1);
+      if (kt + 3 < nk) DORY_GLOAD(ra, rb, (kt + 3) * MF_BK);
+      __syncthreads();
+      DORY_COMPUTE(1);
+      if (kt + 2 < nk) {
+        DORY_SWRITE(ra1, rb1, 0);
+        if (kt + 4 < nk) DORY_GLOAD(ra1, rb1, (kt + 4) * MF_BK);
+      }
+      __syncthreads();
+    }
   }
+#undef DORY_COMPUTE
 #undef DORY_GLOAD
 #undef DORY_SWRITE
 
@@ -257,7 +286,7 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
   else reinterpret_cast<float*>(out)[idx] = a;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool PF2 = false>
 static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
                               hipStream_t st) {
   const int ncols = dual ? F : N;
@@ -266,11 +295,11 @@ static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M
   const dim3 grid(mt * nt), block(64 * WM * WN);
   if (dual) {
     if constexpr ((BN / (32 * WN)) % 2 == 0)
-      DORY_LAUNCH((k_gemm_tile<BM, BN, WM, WN, true>), grid, block, 0, st, A, B, out, M, N, K, F, mt, nt, K);
+      DORY_LAUNCH((k_gemm_tile<BM, BN, WM, WN, true, PF2>), grid, block, 0, st, A, B, out, M, N, K, F, mt, nt, K);
     else
       return hipErrorNotSupported;
   } else {
-    DORY_LAUNCH((k_gemm_tile<BM, BN, WM, WN, false>), grid, block, 0, st, A, B, out, M, N, K, F, mt, nt, K);
+    DORY_LAUNCH((k_gemm_tile<BM, BN, WM, WN, false, PF2>), grid, block, 0, st, A, B, out, M, N, K, F, mt, nt, K);
   }
   return hipGetLastError();
 }
@@ -299,7 +328,7 @@ static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, 
   }
   switch (best) {
     case 0: return tile_launch<256, 256, 2, 4>(A, B, out, M, N, K, F, dual, st);
-    case 1: return tile_launch<128, 192, 4, 2>(A, B, out, M, N, K, F, dual, st);
+    case 1: return tile_launch<128, 192, 4, 2, true>(A, B, out, M, N, K, F, dual, st);
     case 2: return tile_launch<256, 160, 4, 1>(A, B, out, M, N, K, F, dual, st);
     case 3: return tile_launch<128, 320, 2, 2>(A, B, out, M, N, K, F, dual, st);
     case 4: return tile_launch<256, 128, 4, 2>(A, B, out, M, N, K, F, dual, st);
@@ -340,7 +369,7 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {
       const int mt = (M + 127) / 128, nt = (N + 127) / 128;
-      DORY_LAUNCH((k_gemm_tile<128, 128, 2, 4, false>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
+      DORY_LAUNCH((k_gemm_tile<128, 128, 2, 4, false, false>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
                   (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
       const size_t outs = (size_t)M * (dual ? F : N);
       if (dual)

@@ -81,3 +81,27 @@ def test_4b_long_prefill_prefix_property(big):
     assert err <= 1e-3
     assert np.isfinite(full.cpu().numpy()).all()
     m.release(0)
+
+
+def test_4b_width_2048_token_prefill_vs_oracle():
+    """The prefill GEMM tile shapes the benchmark's 2048-token prefill selects (256x160 qkv,
+    128x192 o and down, 256x256 gate/up with the SwiGLU epilogue) and the flash kernel at that
+    length, on a one-block model of the ~4B widths (d=3072, 24/8 heads, FFN 8192) that the
+    oracle computes in under a minute: logits of the last 8 rows and the final hidden row
+    against the oracle (bf16 bars 5e-2 / 3e-2)."""
+    shape = synth.ModelShape(d_model=3072, n_heads=24, n_kv_heads=8, head_dim=128, d_ff=8192, vocab=2048,
+                             n_in=0, n_rec=1, n_out=0, window=4096, dtype=synth.BF16)
+    say("[4B width, 1 block] 2048-token prefill, k=1, vs oracle")
+    w = synth.make_weights(shape, seed=3)
+    m = dory.Model(shape, w, kv_mode="per_loop", max_loops=1, max_seqs=1, max_model_len=2048, max_tokens=2048)
+    prompt = synth.prompt_tokens(shape, 2048)
+    lg, ids = m.prefill(0, prompt, 8)
+    g_h = m.last_hidden(1)[0].cpu().numpy()
+    om = OracleModel(shape, w, "per_loop", 1)
+    olg, oids = om.prefill(0, prompt, 8)
+    err = float(np.max(np.abs(lg.cpu().numpy() - olg)))
+    err_h = float(np.max(np.abs(g_h - om.last_hidden[-1])))
+    agree = int(np.sum(ids.cpu().numpy() == oids))
+    say(f"  logits max-abs {err:.3e}, hidden max-abs {err_h:.3e}, ids {agree}/8")
+    assert err <= 5e-2 and err_h <= 3e-2
+    m.close()
