@@ -634,9 +634,12 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
 
 // ---------------------------------------------------------------- bf16 flash attention for prefill, d_h = 128
 
-// grid (ceil(M/128), H), 256 threads; wave w owns query rows q0+32w .. +32 of
-// head blockIdx.y (one sequence: a prefill chunk); row blocks are dealt last
-// first, so the longest causal ranges start first. Keys go through LDS in
+// grid (row-block slots, H), 256 threads; a workgroup handles 128-query row
+// blocks of head blockIdx.y (one sequence: a prefill chunk), wave w owning
+// queries 32w .. +32 of the block. Causal row block i reads i + 1 key ranges'
+// worth of keys, so with `paired` a workgroup takes row blocks R-1-x and x (the
+// same total for every workgroup: no CU is left with two long blocks while
+// others idle); otherwise workgroup x takes row block R-1-x (longest first). Keys go through LDS in
 // blocks of 64 (4 pages), shared by the four waves and double-buffered: the
 // next block is loaded into registers while the current one is used, then
 // written to the idle buffer. Scores are computed transposed with
@@ -645,8 +648,11 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
 // probabilities for one page (j = 0,1 or 2,3) form the P^T operand of
 // O^T = V^T . P^T as they are, and the matching value operand is the
 // contiguous 16 bytes at vperm position 8(l/32) of each value row.
-// LDS: K [64 keys][16 chunks of 8 dims], chunk c of key k stored at c ^ (k & 7);
-// V^T [4 pages][128 dims][2 halves], half h of dim d stored at h ^ ((d >> 2) & 1).
+// LDS: K [64 keys][16 chunks of 8 dims], chunk c of key k stored at c ^ (k & 15);
+// V^T [4 pages][128 dims][2 halves], half h of dim d stored at h ^ ((d >> 3) & 1).
+// gfx950 serves a 16-byte-per-lane LDS read to 64 banks, 16 lanes at a time: the
+// 16 consecutive keys (256-byte rows) or dims (32-byte rows) such a group reads
+// then fall on 16 distinct 16-byte bank groups.
 // FIXED: q^ and k^ are unit vectors, so a scaled score never exceeds `scale`
 // (up to bf16 rounding); the probabilities are exp(s - scale) with no running
 // maximum and no rescaling of the accumulators (softmax is invariant to the
@@ -655,20 +661,24 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
 // numbers: exp(-2 * 40) ~ 1.8e-35 > 1.2e-38.
 constexpr float kFixedMaxScale = 40.f;
 
-template <bool FIXED>
-__global__ void __launch_bounds__(256) k_attn_prefill(const bf16_t* __restrict__ q, const int32_t* __restrict__ rows,
-                                                      const int32_t* __restrict__ ptab, int max_pages,
-                                                      const bf16_t* __restrict__ kv_slot, size_t page_elems, int M,
-                                                      int H, int Hkv, int window, float scale,
-                                                      bf16_t* __restrict__ out) {
-  constexpr int DH = 128, KB = 64;
+constexpr int PF_KB = 64;  // keys per LDS block of the prefill kernel
+
+// One 128-query row block of head blockIdx.y. KSPLIT = 2: the workgroup has 8
+// waves; waves 4g .. 4g+3 (key group g) take the 64-key blocks 2s + g of each
+// 128-key step for their 32 queries each, and the two groups' partial sums are
+// merged through LDS at the end (two waves per SIMD, half the serial key loop).
+template <bool FIXED, int KSPLIT>
+DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __restrict__ rows,
+                             const int32_t* __restrict__ ptab, int max_pages, const bf16_t* __restrict__ kv_slot,
+                             size_t page_elems, int M, int H, int Hkv, int window, float scale,
+                             bf16_t* __restrict__ out, int wrow0, bf16_t (*Ks)[KSPLIT][PF_KB * 128],
+                             bf16_t (*Vs)[KSPLIT][PF_KB * 128]) {
+  constexpr int DH = 128, KB = PF_KB, STEP = KB * KSPLIT;
   constexpr float LOG2E = 1.4426950408889634f;
-  __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][KB * DH];
-  __shared__ __attribute__((aligned(1024))) bf16_t Vs[2][KB * DH];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wq = wv & 3, kg = wv >> 2;             // query group, key group
   const int hq = blockIdx.y, g = hq / (H / Hkv);
-  const int wrow0 = (gridDim.x - 1 - blockIdx.x) * 128;
-  const int row0 = wrow0 + wv * 32;
+  const int row0 = wrow0 + wq * 32;
   const int nrow = max(0, min(32, M - row0));
   const int seq = rows[0];
   const int qi = lane & 31, hh = lane >> 5;
@@ -696,31 +706,31 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const bf16_t* __restrict__
   // score -> exp2 argument: s * scale * log2(e) - offset * log2(e)
   const float k2 = scale * LOG2E;
 
-  // this wave's share of a 64-key block: four 1 KB pieces of K and of V^T
+  // this wave's share of its key group's 64-key block: four 1 KB pieces of K and of V^T
   const int kkey_lo = lane >> 4;                 // key within a 4-key quarter
   const int kslot = lane & 15;
   const int vdim_lo = lane >> 1;                 // dim within a 32-dim quarter
   const int vslot = lane & 1;
   u32x4_t rk[4], rv[4];
-#define DORY_KV_GLOAD(KB0)                                                                                    \
+#define DORY_KV_GLOAD(STEP0)                                                                                  \
   do {                                                                                                        \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                           \
-      const int ci = wv * 4 + i, pi = ci >> 2, qt = ci & 3;                                                   \
-      const int pidx = min(((KB0) >> 4) + pi, last_page);                                                     \
+      const int ci = wq * 4 + i, pi = ci >> 2, qt = ci & 3;                                                   \
+      const int pidx = min(((STEP0) + kg * KB >> 4) + pi, last_page);                                         \
       const bf16_t* pg = kv_slot + (size_t)prow[pidx] * page_elems;                                           \
       const int key = qt * 4 + kkey_lo;                                                                       \
-      rk[i] = *reinterpret_cast<const u32x4_t*>(pg + ((size_t)g * 16 + key) * DH + (kslot ^ (key & 7)) * 8);  \
+      rk[i] = *reinterpret_cast<const u32x4_t*>(pg + ((size_t)g * 16 + key) * DH + (kslot ^ (key & 15)) * 8); \
       const int dim = qt * 32 + vdim_lo;                                                                      \
       rv[i] = *reinterpret_cast<const u32x4_t*>(pg + (size_t)Hkv * 16 * DH + ((size_t)g * DH + dim) * 16 +    \
-                                                (vslot ^ ((dim >> 2) & 1)) * 8);                              \
+                                                (vslot ^ ((dim >> 3) & 1)) * 8);                              \
     }                                                                                                         \
   } while (0)
 #define DORY_KV_SWRITE(S)                                                                                     \
   do {                                                                                                        \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                           \
-      const int ci = wv * 4 + i, pi = ci >> 2, qt = ci & 3;                                                   \
-      *reinterpret_cast<u32x4_t*>(&Ks[S][(pi * 16 + qt * 4) * DH + lane * 8]) = rk[i];                        \
-      *reinterpret_cast<u32x4_t*>(&Vs[S][(pi * DH + qt * 32) * 16 + lane * 8]) = rv[i];                       \
+      const int ci = wq * 4 + i, pi = ci >> 2, qt = ci & 3;                                                   \
+      *reinterpret_cast<u32x4_t*>(&Ks[S][kg][(pi * 16 + qt * 4) * DH + lane * 8]) = rk[i];                    \
+      *reinterpret_cast<u32x4_t*>(&Vs[S][kg][(pi * DH + qt * 32) * 16 + lane * 8]) = rv[i];                   \
     }                                                                                                         \
   } while (0)
 
@@ -729,13 +739,14 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const bf16_t* __restrict__
   const int kstart = klo & ~(KB - 1);
   DORY_KV_GLOAD(kstart);
   DORY_KV_SWRITE(0);
-  if (kstart + KB <= wg_last) DORY_KV_GLOAD(kstart + KB);
+  if (kstart + STEP <= wg_last) DORY_KV_GLOAD(kstart + STEP);
   __syncthreads();
   int stage = 0;
-  for (int kb = kstart; kb <= wg_last; kb += KB, stage ^= 1) {
+  for (int kstep = kstart; kstep <= wg_last; kstep += STEP, stage ^= 1) {
+    const int kb = kstep + kg * KB;              // this key group's 64-key block
     if (nrow > 0 && kb <= pos_last && kb + KB > wlo) {
-      const bf16_t* ks_ = Ks[stage];
-      const bf16_t* vs_ = Vs[stage];
+      const bf16_t* ks_ = Ks[stage][kg];
+      const bf16_t* vs_ = Vs[stage][kg];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int k0 = kb + 32 * t;
@@ -746,7 +757,7 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const bf16_t* __restrict__
         const int key = 32 * t + qi;             // A operand row: key of the block
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          const int ch = (2 * ks + hh) ^ (key & 7);
+          const int ch = (2 * ks + hh) ^ (key & 15);
           const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks_ + key * DH + ch * 8);
           st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], st, 0, 0, 0);
         }
@@ -791,21 +802,47 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const bf16_t* __restrict__
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
             const int dim = dt * 32 + qi;
-            const int half = hh ^ ((dim >> 2) & 1);
+            const int half = hh ^ ((dim >> 3) & 1);
             const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vs_ + (page * DH + dim) * 16 + half * 8);
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[pp], acc[dt], 0, 0, 0);
           }
         }
       }
     }
-    if (kb + KB <= wg_last) {
+    if (kstep + STEP <= wg_last) {
       DORY_KV_SWRITE(stage ^ 1);  // every wave finished reading that buffer before the last barrier
-      if (kb + 2 * KB <= wg_last) DORY_KV_GLOAD(kb + 2 * KB);
+      if (kstep + 2 * STEP <= wg_last) DORY_KV_GLOAD(kstep + 2 * STEP);
     }
     __syncthreads();
   }
 #undef DORY_KV_GLOAD
 #undef DORY_KV_SWRITE
+  if constexpr (KSPLIT == 2) {
+    // key group 1 hands (max, sum, output) to key group 0 through the (now idle) LDS:
+    // the 64 output floats per lane fill the K buffers exactly (4 waves x 64 lanes,
+    // lane-contiguous), max and sum go to the V buffers
+    float* xs = reinterpret_cast<float*>(&Ks[0][0][0]) + (size_t)wq * 64 * 64 + lane;
+    float* xm = reinterpret_cast<float*>(&Vs[0][0][0]) + (size_t)wq * 2 * 64 + lane;
+    static_assert(sizeof(Ks[0]) * 2 >= 4 * 64 * 64 * sizeof(float), "merge buffer");
+    if (kg == 1) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xs[(dt * 16 + v) * 64] = acc[dt][v];
+      xm[0] = mrun;
+      xm[64] = lrun;
+    }
+    __syncthreads();
+    if (kg == 1) return;
+    const float m1 = xm[0], l1 = xm[64];
+    const float mn = fmaxf(mrun, m1);
+    const float c0 = FIXED ? 1.f : safe_scale(mrun, mn), c1 = FIXED ? 1.f : safe_scale(m1, mn);
+    lrun = lrun * c0 + l1 * c1;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[dt][v] = acc[dt][v] * c0 + xs[(dt * 16 + v) * 64] * c1;
+  }
   if (qi >= nrow) return;
   const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
   bf16_t* orow = out + ((size_t)(row0 + qi) * H + hq) * DH;
@@ -818,6 +855,26 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const bf16_t* __restrict__
       const uint32_t hi = (uint32_t)f32_to_bf16(acc[dt][4 * j + 2] * inv) | ((uint32_t)f32_to_bf16(acc[dt][4 * j + 3] * inv) << 16);
       *reinterpret_cast<uint2*>(orow + d0) = make_uint2(lo, hi);
     }
+}
+
+template <bool FIXED, int KSPLIT>
+__global__ void __launch_bounds__(256 * KSPLIT) k_attn_prefill(const bf16_t* __restrict__ q,
+                                                               const int32_t* __restrict__ rows,
+                                                               const int32_t* __restrict__ ptab, int max_pages,
+                                                               const bf16_t* __restrict__ kv_slot, size_t page_elems,
+                                                               int M, int H, int Hkv, int window, float scale,
+                                                               bf16_t* __restrict__ out, int paired) {
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][KSPLIT][PF_KB * 128];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs[2][KSPLIT][PF_KB * 128];
+  const int nrb = (M + 127) / 128;
+  const int hi = nrb - 1 - (int)blockIdx.x, lo = (int)blockIdx.x;
+  attn_row_block<FIXED, KSPLIT>(q, rows, ptab, max_pages, kv_slot, page_elems, M, H, Hkv, window, scale, out,
+                                hi * 128, Ks, Vs);
+  if (paired && lo < hi) {
+    __syncthreads();  // the first block's merge read the LDS
+    attn_row_block<FIXED, KSPLIT>(q, rows, ptab, max_pages, kv_slot, page_elems, M, H, Hkv, window, scale, out,
+                                  lo * 128, Ks, Vs);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -901,13 +958,16 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
 hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
                                hipStream_t st) {
-  dim3 grid((M + 127) / 128, H);
+  // pair row blocks when that still leaves at least 128 workgroups
+  const int nrb = (M + 127) / 128;
+  const int paired = ((nrb + 1) / 2) * H >= 128 ? 1 : 0;
+  dim3 grid(paired ? (nrb + 1) / 2 : nrb, H);
   if (scale <= kFixedMaxScale)
-    DORY_LAUNCH(k_attn_prefill<true>, grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
-                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out);
+    DORY_LAUNCH((k_attn_prefill<true, 2>), grid, dim3(512), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
+                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, paired);
   else
-    DORY_LAUNCH(k_attn_prefill<false>, grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
-                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out);
+    DORY_LAUNCH((k_attn_prefill<false, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
+                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, paired);
   return hipGetLastError();
 }
 
