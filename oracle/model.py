@@ -168,7 +168,10 @@ class OracleModel:
     last-loop mode [lucas-struct; trawl-kv; onedev-limits].
     """
 
-    def __init__(self, shape, weights, kv_mode: str = PER_LOOP, loops: int = 1):
+    def __init__(self, shape, weights, kv_mode: str = PER_LOOP, loops: int = 1, gemv_weights: str = "bf16"):
+        """gemv_weights = "mxfp8": calls that process at most 2 rows (decode of one or two
+        sequences, prefill chunks of one or two tokens) use the projection and LM-head weights
+        quantised to MXFP8 and dequantised (oracle.mx); other calls use the weights as given."""
         self.s = shape
         self.bf16 = shape.dtype == "bf16"
         self.E = np.asarray(weights.embed, dtype=np.float64)
@@ -176,6 +179,16 @@ class OracleModel:
         self.blocks = []
         for blk in weights.blocks:
             self.blocks.append({k: np.asarray(v, dtype=np.float64) for k, v in blk.items()})
+        if gemv_weights not in ("bf16", "mxfp8"):
+            raise ValueError(gemv_weights)
+        self.mx = gemv_weights == "mxfp8"
+        self.blocks_mx, self.Wlm_mx = [], None
+        if self.mx:
+            from .mx import dequantize_mxfp8, quantize_mxfp8
+            dq = lambda w: dequantize_mxfp8(*quantize_mxfp8(w))  # noqa: E731
+            for blk in self.blocks:
+                self.blocks_mx.append({k: (dq(v) if k.startswith("w") else v) for k, v in blk.items()})
+            self.Wlm_mx = dq(self.Wlm)
         if kv_mode not in (PER_LOOP, LAST_LOOP):
             raise ValueError(kv_mode)
         self.kv_mode = kv_mode
@@ -214,9 +227,9 @@ class OracleModel:
     def _act(self, a):
         return bf16_round(a) if self.bf16 else np.asarray(a, dtype=np.float64)
 
-    def _block(self, h, j, t, seq: _Seq, pos):
+    def _block(self, h, j, t, seq: _Seq, pos, mx=False):
         s = self.s
-        W = self.blocks[j]
+        W = self.blocks_mx[j] if mx else self.blocks[j]
         T = h.shape[0]
         H, Hk, dh = s.n_heads, s.n_kv_heads, s.head_dim
         # attention sublayer
@@ -250,14 +263,14 @@ class OracleModel:
         self.counts["full" if self.is_full(j) else "swa"] += 1
         return h
 
-    def forward_chunk(self, seq: _Seq, tokens, pos0: int, trace=None):
+    def forward_chunk(self, seq: _Seq, tokens, pos0: int, trace=None, mx=False):
         """Hidden states after the output stack for one chunk [onedev-how]."""
         s = self.s
         tokens = np.asarray(tokens, dtype=np.int64)
         pos = pos0 + np.arange(len(tokens))
         h = self.E[tokens]
         for j in range(s.n_in):
-            h = self._block(h, j, 1, seq, pos)
+            h = self._block(h, j, 1, seq, pos, mx)
         x = h
         st = x                                   # s_0 = x
         if trace is not None:
@@ -266,20 +279,20 @@ class OracleModel:
             u = l2_normalize(st + x)             # u_t = N(s_{t-1} + x)
             h = u
             for j in range(s.n_in, s.n_in + s.n_rec):
-                h = self._block(h, j, t, seq, pos)
+                h = self._block(h, j, t, seq, pos, mx)
             st = l2_normalize(h)                 # s_t = N(F(u_t))
             if trace is not None:
                 trace.setdefault("u", []).append(u)
                 trace.setdefault("s", []).append(st)
         h = st
         for j in range(s.n_in + s.n_rec, s.n_blocks):
-            h = self._block(h, j, 1, seq, pos)
+            h = self._block(h, j, 1, seq, pos, mx)
         return h
 
-    def lm_head(self, h):
+    def lm_head(self, h, mx=False):
         """fp64 logits of the final hidden rows; ids = argmax over the float32-rounded logits,
         lowest id on ties (the kernel decides in float32)."""
-        logits = self._act(h) @ self.Wlm.T
+        logits = self._act(h) @ (self.Wlm_mx if mx else self.Wlm).T
         ids = np.argmax(logits.astype(np.float32), axis=-1).astype(np.int32)
         return logits, ids
 
@@ -297,20 +310,22 @@ class OracleModel:
         if seq is None:
             seq = self.seqs[seq_id] = _Seq(self.s.n_kv_heads, self.s.head_dim)
         self._check_loops_for(seq)
-        h = self.forward_chunk(seq, tokens, seq.len, trace)
+        mx = self.mx and len(tokens) <= 2
+        h = self.forward_chunk(seq, tokens, seq.len, trace, mx)
         seq.len += len(tokens)
         self.last_hidden = h
-        logits, ids = self.lm_head(h[len(tokens) - logits_rows:])
+        logits, ids = self.lm_head(h[len(tokens) - logits_rows:], mx)
         return logits, ids
 
     def decode(self, seq_ids, tokens):
         logits, ids, hid = [], [], []
+        mx = self.mx and len(seq_ids) <= 2
         for sid, tok in zip(seq_ids, tokens):
             seq = self.seqs[int(sid)]
             self._check_loops_for(seq)
-            h = self.forward_chunk(seq, [int(tok)], seq.len)
+            h = self.forward_chunk(seq, [int(tok)], seq.len, mx=mx)
             seq.len += 1
-            lg, i = self.lm_head(h)
+            lg, i = self.lm_head(h, mx)
             logits.append(lg[0])
             ids.append(i[0])
             hid.append(h[0])
