@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-batched", action="store_true")
+    p.add_argument("--no-mx", action="store_true", help="skip the MXFP8-weight decode measurement")
     p.add_argument("--no-decode", action="store_true",
                    help="prefill only (for profiling): the JSON value is then the prefill rate at --k")
     p.add_argument("--batched-steps", type=int, default=16)
@@ -156,7 +157,7 @@ def main():
     ids = [torch.empty(1, dtype=torch.int32, device="cuda:0") for _ in range(2)]
     first = torch.empty(1, dtype=torch.int32, device="cuda:0")
     plog = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda:0")
-    def decode_run(k, mode):
+    def decode_run(k, mode, m=m):
         m.set_kv_mode(mode)
         m.set_loops(k)
         _, pid = m.prefill(0, ptoks, 1, logits=plog)
@@ -206,6 +207,15 @@ def main():
     for k in loops:
         res["decode"][k] = decode_run(k, "last_loop")
     res["decode_per_loop"] = {args.k: decode_run(args.k, "per_loop")}
+    if not args.no_mx:
+        # the same steps streaming MXFP8 copies of the weights (OCP MX, E4M3 + E8M0 per 32)
+        mm = dory.Model(shape, None, kv_mode="last_loop", max_loops=4, max_seqs=1, max_model_len=max_len,
+                        max_tokens=max(args.prompt, args.prefill_len), device="cuda:0", share_weights_from=m,
+                        gemv_weights="mxfp8")
+        log(f"[bench] MXFP8 context: workspace {mm.ws_bytes / 2**30:.2f} GiB")
+        res["decode_mx"] = {k: decode_run(k, "last_loop", mm) for k in loops}
+        mm.close()
+        del mm
 
     if not args.no_batched:
         res["batched"] = bench_batched(m, shape, args, ev)
@@ -246,6 +256,10 @@ def main():
             "decode_bs1": {str(k): {"tok_s": round(v["tok_s"], 2), "ms_per_step": round(v["ms_per_step"], 4),
                                     "GB_per_step": round(v["bytes_per_step"] / 1e9, 3),
                                     "hbm_frac": round(v["hbm_frac"], 4)} for k, v in res["decode"].items()},
+            "decode_bs1_mxfp8": {str(k): {"tok_s": round(v["tok_s"], 2), "ms_per_step": round(v["ms_per_step"], 4),
+                                          "GB_per_step": round(v["bytes_per_step"] / 1e9, 3),
+                                          "hbm_frac": round(v["hbm_frac"], 4)}
+                                 for k, v in res.get("decode_mx", {}).items()},
             "decode_bs1_per_loop": {str(k): {"tok_s": round(v["tok_s"], 2), "ms_per_step": round(v["ms_per_step"], 4),
                                              "GB_per_step": round(v["bytes_per_step"] / 1e9, 3),
                                              "hbm_frac": round(v["hbm_frac"], 4)}

@@ -60,6 +60,16 @@ typedef enum { DORY_F32 = 0, DORY_BF16 = 1 } dory_dtype_t;
 /* Context flag: validate and do all host bookkeeping, but never touch the GPU
  * (no HIP call at all; device pointers may be NULL). For host-side tests. */
 #define DORY_FLAG_DRY_RUN 1u
+/* Context flag: keep MXFP8 copies of every projection and of the LM head
+ * (OCP Microscaling Formats v1.0: FP8 E4M3 elements, one E8M0 scale per 32
+ * consecutive elements of a row, quantised at create by the rule of
+ * dory_quantize_mxfp8) in the workspace, and stream them instead of the bf16
+ * weights in every call that processes at most 2 rows (decode of one or two
+ * sequences, prefill chunks of one or two tokens): about half the weight bytes
+ * per decode step. Calls of more rows use the bf16 weights. bf16 model only,
+ * with d_model, n_heads*head_dim and d_ff in {1024, 3072, 4096, 8192}. The
+ * workspace grows by about 1.03 bytes per weight (dory_query_sizes). */
+#define DORY_FLAG_MXFP8_GEMV 4u
 
 typedef struct dory_config {
   int32_t d_model;       /* d */
@@ -174,6 +184,17 @@ dory_status dory_seq_len(const dory_ctx* ctx, int32_t seq_id, int32_t* len);
 /* KV bytes held by live sequences: pages in use x slots x bytes per page slot. */
 dory_status dory_kv_bytes_in_use(const dory_ctx* ctx, size_t* bytes);
 dory_status dory_get_stats(const dory_ctx* ctx, dory_stats* out);
+
+/* MXFP8 quantisation (OCP Microscaling Formats v1.0, MXFP8 with E4M3 elements)
+ * of a bf16 matrix src_dev [rows, cols] (device, row-major, 16-byte aligned,
+ * cols % 32 == 0): per 32 consecutive elements of a row, the E8M0 scale code
+ * e + 127 with e = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 for an
+ * all-zero block) goes to scales_dev [rows, cols/32], and each element's E4M3
+ * code (v / 2^e rounded to nearest even, magnitudes >= 448 saturating to 448,
+ * sign kept) to codes_dev [rows, cols] (16-byte aligned). Enqueued on `stream`
+ * (a hipStream_t, NULL = default stream); caller-owned buffers. */
+dory_status dory_quantize_mxfp8(const void* src_dev, int64_t rows, int32_t cols, void* codes_dev, void* scales_dev,
+                                void* stream);
 
 /* Device-side error flags raised since the last reset (synchronises the
  * stream): bit 0 = a token id outside 0..V-1 reached the embedding (it was

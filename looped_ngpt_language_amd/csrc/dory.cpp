@@ -37,7 +37,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {  // byte offsets inside the workspace
-  size_t rope, ptab, upload, err, buf[4], y, hb, qkv, q, o, z, part_ml, part_o, logits, argmax, splitk, spec, total;
+  size_t rope, ptab, upload, err, buf[4], y, hb, qkv, q, o, z, part_ml, part_o, logits, argmax, splitk, spec, mx, mx_bytes,
+      total;
   size_t splitk_bytes;
   int max_pages;       // pages per sequence
   int upload_ints;     // capacity of the upload area in int32
@@ -79,6 +80,16 @@ Layout make_layout(const dory_config& c) {
     L.splitk = take(L.splitk_bytes);
   }
   L.spec = take(64 * 4);
+  // MXFP8 copies of every projection and of the LM head (codes, then scales per matrix)
+  L.mx_bytes = 0;
+  if (c.flags & DORY_FLAG_MXFP8_GEMV) {
+    const size_t nb = (size_t)(c.n_in + c.n_rec + c.n_out);
+    const size_t hd = (size_t)c.n_heads * c.head_dim;
+    const size_t block_params = (size_t)qkv_cols(c) * d + d * hd + 2 * (size_t)c.d_ff * d + d * (size_t)c.d_ff;
+    const size_t params = nb * block_params + (size_t)c.vocab * d;
+    L.mx_bytes = params + params / 32 + 16 * kAlign * (4 * nb + 1);
+  }
+  L.mx = take(L.mx_bytes);
   L.total = off;
   return L;
 }
@@ -107,6 +118,12 @@ std::string check_config(const dory_config* c) {
     if (c->d_model % 64 || c->d_ff % 64 || hd % 64) return "bf16 model: d_model, d_ff and n_heads*head_dim must be multiples of 64";
   }
   if (!(c->rope_theta > 0.f) || !(c->attn_scale > 0.f)) return "rope_theta and attn_scale must be positive";
+  if (c->flags & DORY_FLAG_MXFP8_GEMV) {
+    if (c->dtype != DORY_BF16) return "MXFP8 weights need the bf16 model";
+    if (!dory::gemv_supported(c->d_model) || !dory::gemv_supported(c->n_heads * c->head_dim) ||
+        !dory::gemv_supported(c->d_ff))
+      return "MXFP8 weights need d_model, n_heads*head_dim and d_ff in {1024, 3072, 4096, 8192}";
+  }
   return "";
 }
 
@@ -167,6 +184,11 @@ struct dory_ctx {
   const void* lm = nullptr;
   std::vector<const void*> wqkv, wo, wgu, wd;
   std::vector<const float*> aa, am;
+  // MXFP8 copies (workspace) used by the weight-streaming GEMV (calls of <= 2 rows)
+  bool mx = false;
+  struct MxMat { const void* codes = nullptr; const uint8_t* scales = nullptr; };
+  std::vector<MxMat> mqkv, mo, mgu, md;
+  MxMat mlm;
   // KV manager
   std::vector<int32_t> free_pages;
   std::vector<Seq> seqs;
@@ -349,6 +371,17 @@ bool fused_residual_ok(const dory_ctx* c, int M, bool decode) {
          dory::gemv_supported(g.n_heads * g.head_dim) && dory::gemv_supported(g.d_ff);
 }
 
+// Weight bytes per parameter a launch streams: MXFP8 (1 + 1/32) on the GEMV path, else the storage size.
+double wbytes(const dory_ctx* c, int M) { return c->mx && M <= 2 ? 1.0 + 1.0 / 32 : (double)esize(c->cfg); }
+
+// C = A . W^T through the MXFP8 GEMV (calls of <= 2 rows when the context holds MX weights) or launch_gemm.
+hipError_t project(dory_ctx* c, bool dual, const void* A, const void* W, const dory_ctx::MxMat& mx, void* out, int M,
+                   int N, int K) {
+  if (c->mx && M <= 2 && dory::gemv_supported(K))
+    return dory::launch_gemv(dual, A, mx.codes, mx.scales, out, M, N, K, c->stream);
+  return dory::launch_gemm(c->cfg.dtype, dual, A, W, out, M, N, K, SPLITK, c->stream);
+}
+
 // One block application on M rows (hidden state per Flow; storage copy in hb when materialised).
 void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geom& geo) {
   using namespace dory;
@@ -381,15 +414,18 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   const int32_t* ptab = c->W<int32_t>(c->L.ptab);
   char* kv = c->pool + (size_t)slot_of(c, j, t) * c->pages_total * c->page_bytes;
   hipStream_t st = c->stream;
+  const double wb = wbytes(c, M);
+  const bool gmx = c->mx && M <= 2;  // this call streams the MXFP8 weights
   if (f.py && fres) {
-    Span sp(c, R_QKV, (double)nq * d * es + Md * d * 12 + 4.0 * d + Md * nq * 4, 2.0 * Md * nq * d);
-    ok(c, launch_gemv_residual(false, c->wqkv[j], qkv, M, nq, d, f.h, f.py, f.pa, f.spare, st));
+    Span sp(c, R_QKV, (double)nq * d * wb + Md * d * 12 + 4.0 * d + Md * nq * 4, 2.0 * Md * nq * d);
+    ok(c, launch_gemv_residual(false, gmx ? c->mqkv[j].codes : c->wqkv[j], gmx ? c->mqkv[j].scales : nullptr, qkv, M,
+                               nq, d, f.h, f.py, f.pa, f.spare, st));
     std::swap(f.h, f.spare);
     f.py = f.pa = nullptr;
   } else {
     flush(c, f, M);
-    Span sp(c, R_QKV, (double)nq * d * es + Md * d * es + Md * nq * 4, 2.0 * Md * nq * d);
-    ok(c, launch_gemm(dt, false, hb, c->wqkv[j], qkv, M, nq, d, SPLITK, st));
+    Span sp(c, R_QKV, (double)nq * d * wb + Md * d * es + Md * nq * 4, 2.0 * Md * nq * d);
+    ok(c, project(c, false, hb, c->wqkv[j], gmx ? c->mqkv[j] : dory_ctx::MxMat{}, qkv, M, nq, d));
   }
   if (!fused_decode) {
     Span sp(c, R_ROPE, Md * nq * 4 + Md * (hd + 2.0 * Hk * dh) * es, 0);
@@ -416,24 +452,25 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
     }
   }
   {
-    Span sp(c, R_OPROJ, (double)d * hd * es + Md * hd * es + Md * d * 4, 2.0 * Md * d * hd);
-    ok(c, launch_gemm(dt, false, c->W(c->L.o), c->wo[j], y, M, d, hd, SPLITK, st));
+    Span sp(c, R_OPROJ, (double)d * hd * wb + Md * hd * es + Md * d * 4, 2.0 * Md * d * hd);
+    ok(c, project(c, false, c->W(c->L.o), c->wo[j], gmx ? c->mo[j] : dory_ctx::MxMat{}, y, M, d, hd));
   }
   if (fres) {
-    Span sp(c, R_GU, 2.0 * F * d * es + Md * d * 12 + 4.0 * d + Md * F * es, 2.0 * Md * 2 * F * d);
-    ok(c, launch_gemv_residual(true, c->wgu[j], c->W(c->L.z), M, 2 * F, d, f.h, y, c->aa[j], f.spare, st));
+    Span sp(c, R_GU, 2.0 * F * d * wb + Md * d * 12 + 4.0 * d + Md * F * es, 2.0 * Md * 2 * F * d);
+    ok(c, launch_gemv_residual(true, gmx ? c->mgu[j].codes : c->wgu[j], gmx ? c->mgu[j].scales : nullptr,
+                               c->W(c->L.z), M, 2 * F, d, f.h, y, c->aa[j], f.spare, st));
     std::swap(f.h, f.spare);
   } else {
     {
       Span sp(c, R_RESID, resid_bytes, 0);
       ok(c, launch_residual(dt, f.h, y, c->aa[j], hb, M, d, st));
     }
-    Span sp(c, R_GU, 2.0 * F * d * es + Md * d * es + Md * F * es, 2.0 * Md * 2 * F * d);
-    ok(c, launch_gemm(dt, true, hb, c->wgu[j], c->W(c->L.z), M, 2 * F, d, SPLITK, st));
+    Span sp(c, R_GU, 2.0 * F * d * wb + Md * d * es + Md * F * es, 2.0 * Md * 2 * F * d);
+    ok(c, project(c, true, hb, c->wgu[j], gmx ? c->mgu[j] : dory_ctx::MxMat{}, c->W(c->L.z), M, 2 * F, d));
   }
   {
-    Span sp(c, R_DOWN, (double)d * F * es + Md * F * es + Md * d * 4, 2.0 * Md * d * F);
-    ok(c, launch_gemm(dt, false, c->W(c->L.z), c->wd[j], y, M, d, F, SPLITK, st));
+    Span sp(c, R_DOWN, (double)d * F * wb + Md * F * es + Md * d * 4, 2.0 * Md * d * F);
+    ok(c, project(c, false, c->W(c->L.z), c->wd[j], gmx ? c->md[j] : dory_ctx::MxMat{}, y, M, d, F));
   }
   if (fres) {
     f.py = y;
@@ -505,8 +542,9 @@ void lm_head(dory_ctx* c, int M, int rows, float* logits, int32_t* ids) {
   const double es = (double)esize(g), V = g.vocab, d = g.d_model;
   const char* hb = c->W(c->L.hb) + (size_t)(M - rows) * g.d_model * esize(g);
   {
-    Span sp(c, R_LM, V * d * es + rows * d * es + rows * V * 4, 2.0 * rows * V * d);
-    ok(c, launch_gemm(g.dtype, false, hb, c->lm, logits, rows, g.vocab, g.d_model, SPLITK, c->stream));
+    Span sp(c, R_LM, V * d * wbytes(c, rows) + rows * d * es + rows * V * 4, 2.0 * rows * V * d);
+    ok(c, project(c, false, hb, c->lm, c->mx && rows <= 2 ? c->mlm : dory_ctx::MxMat{}, logits, rows, g.vocab,
+                  g.d_model));
   }
   if (ids) {
     Span sp(c, R_ARGMAX, rows * V * 4 + rows * 4.0, 0);
@@ -595,6 +633,7 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t k
   c->cfg = *cfg;
   c->L = L;
   c->dry = dry;
+  c->mx = (cfg->flags & DORY_FLAG_MXFP8_GEMV) != 0;
   c->kv_mode = kv_mode;
   c->n_blocks = nb;
   c->pool = static_cast<char*>(kv_pool);
@@ -629,6 +668,31 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t k
     if (e == hipSuccess) e = hipMemsetAsync(c->W(L.err), 0, 4, c->stream);
     // unwritten cache slots hold zeros, never NaN bit patterns, so masked keys contribute 0 * v = 0
     if (e == hipSuccess) e = hipMemsetAsync(c->pool, 0, c->pool_bytes, c->stream);
+    if (e == hipSuccess && c->mx) {
+      // quantise every projection and the LM head into the workspace's MXFP8 area
+      char* p = c->W(L.mx);
+      auto quant = [&](const void* src, size_t rows, int cols) -> dory_ctx::MxMat {
+        dory_ctx::MxMat m;
+        m.codes = p;
+        p += align_up(rows * cols);
+        m.scales = reinterpret_cast<const uint8_t*>(p);
+        p += align_up(rows * (cols / 32));
+        if (e == hipSuccess)
+          e = dory::launch_mx_quantize(src, (long long)rows, cols, const_cast<void*>(m.codes),
+                                       const_cast<uint8_t*>(m.scales), c->stream);
+        return m;
+      };
+      const int d = cfg->d_model, hd = cfg->n_heads * cfg->head_dim, F = cfg->d_ff, nq = qkv_cols(*cfg);
+      for (int j = 0; j < nb; ++j) {
+        c->mqkv.push_back(quant(c->wqkv[j], nq, d));
+        c->mo.push_back(quant(c->wo[j], d, hd));
+        c->mgu.push_back(quant(c->wgu[j], 2 * (size_t)F, d));
+        c->md.push_back(quant(c->wd[j], d, F));
+      }
+      c->mlm = quant(c->lm, cfg->vocab, d);
+      if ((size_t)(p - c->W(L.mx)) > L.mx_bytes) e = hipErrorInvalidValue;  // layout bound (never expected)
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) {
       dory_destroy(c);
       return DORY_E_HIP;
@@ -807,6 +871,15 @@ dory_status dory_get_stats(const dory_ctx* c, dory_stats* out) {
   for (auto& s : c->seqs) live += s.live;
   out->live_seqs = live;
   return DORY_OK;
+}
+
+dory_status dory_quantize_mxfp8(const void* src_dev, int64_t rows, int32_t cols, void* codes_dev, void* scales_dev,
+                                void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 || (rows > 0 && (!src_dev || !codes_dev || !scales_dev)))
+    return DORY_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(src_dev) % 16 || reinterpret_cast<uintptr_t>(codes_dev) % 16) return DORY_E_INVALID;
+  hipError_t e = dory::launch_mx_quantize(src_dev, rows, cols, codes_dev, scales_dev, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DORY_OK : DORY_E_HIP;
 }
 
 dory_status dory_device_flags(dory_ctx* c, int32_t* flags, int32_t reset) {

@@ -364,7 +364,7 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     return hipGetLastError();
   }
   if (K % MF_BK != 0) return hipErrorNotSupported;
-  if (M <= 2 && gemv_supported(K)) return launch_gemv(dual, A, B, out, M, N, K, st);
+  if (M <= 2 && gemv_supported(K)) return launch_gemv(dual, A, B, nullptr, out, M, N, K, st);
   if (M <= 256 && split_ws) {
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {

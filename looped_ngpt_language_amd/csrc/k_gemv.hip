@@ -15,34 +15,53 @@
 
 namespace dory {
 
+// Weights either bf16 [N, K] or (MX) MXFP8 [N, K] (OCP Microscaling Formats
+// v1.0: FP8 E4M3 element codes, one E8M0 scale 2^(code - 127) per 32 consecutive
+// elements of a row, scales [N, K/32]); an MX element pair is turned into the
+// exact bf16 pair value * scale by v_cvt_scalef32_pk_bf16_fp8 and fed to the
+// same v_dot2_f32_bf16 as the bf16 path, so MXFP8 halves the weight bytes.
+// A 16-byte lane chunk holds EPC = 8 (bf16) or 16 (MX) elements of a row.
+
+DORY_DEV float e8m0_to_f32(uint32_t code) { return __uint_as_float(code ? code << 23 : 0x00400000u); }
+
 // One wave per group of R output rows; lane l reads 16-byte chunks l, l+64, ...
-// of each weight row (KCH chunks per lane, K = 512*KCH). The weight loads are
-// issued first.
-template <int KCH, int R, int MR, bool DUAL, bool RES>
-__global__ void __launch_bounds__(256) k_gemv_bf16(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
-                                                   void* __restrict__ Y, int M, int N, int F,
-                                                   const float* __restrict__ rh, const float* __restrict__ ry,
-                                                   const float* __restrict__ ralpha, float* __restrict__ hout) {
-  constexpr int K = KCH * 512;
+// of each weight row (KCH chunks per lane, K = 64 * EPC * KCH). The weight loads
+// are issued first.
+template <int KCH, int R, int MR, bool DUAL, bool RES, bool MX>
+__global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, const void* __restrict__ Wv,
+                                              const uint8_t* __restrict__ Sc, void* __restrict__ Y, int M, int N,
+                                              int F, const float* __restrict__ rh, const float* __restrict__ ry,
+                                              const float* __restrict__ ralpha, float* __restrict__ hout) {
+  constexpr int EPC = MX ? 16 : 8;
+  constexpr int K = KCH * 64 * EPC;
+  constexpr int RB = K * (MX ? 1 : 2);       // bytes per weight row
+  constexpr int XU = EPC / 8;                // 16-byte x pieces per chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = blockIdx.x * 4 + (tid >> 6);
   const int nrows_out = DUAL ? F : N;
   const int r0 = wave * R;
   const bool active = r0 < nrows_out;
   constexpr int NB = DUAL ? 2 : 1;
+  const char* W = static_cast<const char*>(Wv);
   u32x4_t wr[NB][R][KCH];
+  float sc[NB][R][KCH];
   if (active) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int n = min(r0 + r, nrows_out - 1) + b * F;
-        const bf16_t* wp = W + (size_t)n * K + (size_t)lane * 8;
+        const char* wp = W + (size_t)n * RB + (size_t)lane * 16;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) wr[b][r][c] = *reinterpret_cast<const u32x4_t*>(wp + c * 512);
+        for (int c = 0; c < KCH; ++c) wr[b][r][c] = *reinterpret_cast<const u32x4_t*>(wp + c * 1024);
+        if constexpr (MX) {
+          const uint8_t* sp = Sc + (size_t)n * (K / 32);
+#pragma unroll
+          for (int c = 0; c < KCH; ++c) sc[b][r][c] = e8m0_to_f32(sp[(c * 64 + lane) >> 1]);
+        }
       }
   }
-  uint4 xr[MR][KCH];
+  uint4 xr[MR][KCH][XU];
   if constexpr (RES) {
     constexpr int EPT = K / 256;
     __shared__ __attribute__((aligned(16))) bf16_t xs[MR][K];
@@ -81,14 +100,20 @@ __global__ void __launch_bounds__(256) k_gemv_bf16(const bf16_t* __restrict__ X,
     for (int m = 0; m < MR; ++m)
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
-        xr[m][c] = m < M ? *reinterpret_cast<const uint4*>(&xs[m][(c * 64 + lane) * 8]) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < XU; ++u)
+          xr[m][c][u] = m < M ? *reinterpret_cast<const uint4*>(&xs[m][(c * 64 + lane) * EPC + 8 * u])
+                              : make_uint4(0, 0, 0, 0);
   } else {
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
-        xr[m][c] = m < M ? *reinterpret_cast<const uint4*>(X + (size_t)m * K + (size_t)(c * 64 + lane) * 8)
-                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < XU; ++u)
+          xr[m][c][u] = m < M ? *reinterpret_cast<const uint4*>(X + (size_t)m * K + (size_t)(c * 64 + lane) * EPC +
+                                                               8 * u)
+                              : make_uint4(0, 0, 0, 0);
   }
   if (!active) return;
   float acc[NB][R][MR];
@@ -102,11 +127,25 @@ __global__ void __launch_bounds__(256) k_gemv_bf16(const bf16_t* __restrict__ X,
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
           const u32x4_t w = wr[b][r][c];
-          const uint4 x = xr[m][c];
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), s, false);
+          if constexpr (MX) {
+            // word j holds elements 4j .. 4j+3; x piece u holds elements 8u .. 8u+7
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            const uint4 x0 = xr[m][c][0], x1 = xr[m][c][1];
+            const uint32_t xx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[j], sc[b][r][c], false);
+              const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[j], sc[b][r][c], true);
+              s = __builtin_amdgcn_fdot2_f32_bf16(lo, as_bf16x2(xx[2 * j]), s, false);
+              s = __builtin_amdgcn_fdot2_f32_bf16(hi, as_bf16x2(xx[2 * j + 1]), s, false);
+            }
+          } else {
+            const uint4 x = xr[m][c][0];
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), s, false);
+          }
         }
         acc[b][r][m] = wave_sum(s);
       }
@@ -127,36 +166,84 @@ __global__ void __launch_bounds__(256) k_gemv_bf16(const bf16_t* __restrict__ X,
   }
 }
 
+// MXFP8 quantisation (the spec's conversion rule): one thread per 32-element
+// block of a bf16 row; X = 2^e, e = floor(log2 max|v|) - 8 clamped to [-127, 127]
+// (an all-zero block gets e = -127); each v / X is rounded to E4M3 (round to
+// nearest even on its 3-bit mantissa or, below 2^-6, on the 2^-9 subnormal
+// step), magnitudes of 448 and above saturate to 448; the sign bit is kept.
+__global__ void __launch_bounds__(256) k_mx_quantize(const bf16_t* __restrict__ src, long long blocks,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= blocks) return;
+  const uint4* p = reinterpret_cast<const uint4*>(src + b * 32);
+  uint32_t u[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = p[i];
+    u[4 * i] = v.x; u[4 * i + 1] = v.y; u[4 * i + 2] = v.z; u[4 * i + 3] = v.w;
+  }
+  uint32_t amax_bits = 0;  // |v| of bf16 values compare as integers
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax_bits = max(amax_bits, max((u[i] << 16) & 0x7FFFFFFFu, u[i] & 0x7FFF0000u));
+  const int ebits = (int)(amax_bits >> 23);
+  const int e = max(-127, min(127, (ebits ? ebits - 127 : -200) - 8));
+  scales[b] = (uint8_t)(e + 127);
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t bits = (i & 1) ? (u[i >> 1] & 0xFFFF0000u) : (u[i >> 1] << 16);
+    const float q = ldexpf(__uint_as_float(bits & 0x7FFFFFFFu), -e);  // exact: power-of-two scaling
+    uint32_t mag;
+    if (q >= 448.f) {
+      mag = 126;
+    } else if (q < 0.015625f) {  // below 2^-6: subnormal step 2^-9
+      mag = (uint32_t)rintf(q * 512.f);
+    } else {
+      const int qe = (int)((__float_as_uint(q) >> 23) & 0xFF) - 127;   // -6 .. 8
+      const float t = rintf((ldexpf(q, -qe) - 1.f) * 8.f);               // 0 .. 8
+      mag = t >= 8.f ? (uint32_t)((qe + 8) << 3) : (uint32_t)((qe + 7) << 3) + (uint32_t)t;
+    }
+    out[i >> 2] |= ((bits >> 31) << 7 | mag) << (8 * (i & 3));
+  }
+  uint4* o = reinterpret_cast<uint4*>(codes + b * 32);
+  o[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  o[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
 struct ResArgs {
   const float *h, *y, *alpha;
   float* hout;
 };
 
-template <int KCH, bool DUAL, bool RES>
-static hipError_t gemv_k(const bf16_t* X, const bf16_t* W, void* Y, int M, int N, int F, const ResArgs& ra,
-                         hipStream_t st) {
+template <int KCH, bool DUAL, bool RES, bool MX>
+static hipError_t gemv_k(const bf16_t* X, const void* W, const uint8_t* Sc, void* Y, int M, int N, int F,
+                         const ResArgs& ra, hipStream_t st) {
   const int rows_out = DUAL ? F : N;
-  constexpr int R = KCH >= 16 ? 1 : 2;  // keeps the weight registers of a wave near 128 VGPRs
+  // rows per wave: 16-byte weight chunks per lane near 12-16 (registers near 128 VGPRs)
+  constexpr int R = MX ? (KCH >= 8 ? 2 : 4) : (KCH >= 16 ? 1 : 2);
   const int waves = (rows_out + R - 1) / R;
   const dim3 grid((waves + 3) / 4);
   if (M == 1)
-    DORY_LAUNCH((k_gemv_bf16<KCH, R, 1, DUAL, RES>), grid, dim3(256), 0, st, X, W, Y, M, N, F, ra.h, ra.y, ra.alpha,
-                ra.hout);
+    DORY_LAUNCH((k_gemv<KCH, R, 1, DUAL, RES, MX>), grid, dim3(256), 0, st, X, W, Sc, Y, M, N, F, ra.h, ra.y,
+                ra.alpha, ra.hout);
   else
-    DORY_LAUNCH((k_gemv_bf16<KCH, R, 2, DUAL, RES>), grid, dim3(256), 0, st, X, W, Y, M, N, F, ra.h, ra.y, ra.alpha,
-                ra.hout);
+    DORY_LAUNCH((k_gemv<KCH, R, 2, DUAL, RES, MX>), grid, dim3(256), 0, st, X, W, Sc, Y, M, N, F, ra.h, ra.y,
+                ra.alpha, ra.hout);
   return hipGetLastError();
 }
 
-template <bool DUAL, bool RES>
-static hipError_t gemv_dispatch(const bf16_t* X, const bf16_t* W, void* Y, int M, int N, int K, int F,
-                                const ResArgs& ra, hipStream_t st) {
+template <bool DUAL, bool RES, bool MX>
+static hipError_t gemv_dispatch(const bf16_t* X, const void* W, const uint8_t* Sc, void* Y, int M, int N, int K,
+                                int F, const ResArgs& ra, hipStream_t st) {
+  constexpr int D = MX ? 1024 : 512;  // elements per lane chunk column (64 lanes x EPC)
   switch (K) {
-    case 1024: return gemv_k<2, DUAL, RES>(X, W, Y, M, N, F, ra, st);
-    case 3072: return gemv_k<6, DUAL, RES>(X, W, Y, M, N, F, ra, st);
-    case 4096: return gemv_k<8, DUAL, RES>(X, W, Y, M, N, F, ra, st);
+    case 1024: return gemv_k<1024 / D, DUAL, RES, MX>(X, W, Sc, Y, M, N, F, ra, st);
+    case 3072: return gemv_k<3072 / D, DUAL, RES, MX>(X, W, Sc, Y, M, N, F, ra, st);
+    case 4096: return gemv_k<4096 / D, DUAL, RES, MX>(X, W, Sc, Y, M, N, F, ra, st);
     case 8192:
-      if constexpr (!RES) return gemv_k<16, DUAL, false>(X, W, Y, M, N, F, ra, st);
+      if constexpr (!RES) return gemv_k<8192 / D, DUAL, false, MX>(X, W, Sc, Y, M, N, F, ra, st);
       return hipErrorNotSupported;
     default: return hipErrorNotSupported;
   }
@@ -165,21 +252,38 @@ static hipError_t gemv_dispatch(const bf16_t* X, const bf16_t* W, void* Y, int M
 bool gemv_supported(int K) { return K == 1024 || K == 3072 || K == 4096 || K == 8192; }
 bool gemv_residual_supported(int K) { return K == 1024 || K == 3072 || K == 4096; }
 
-hipError_t launch_gemv(bool dual, const void* X, const void* W, void* out, int M, int N, int K, hipStream_t st) {
+hipError_t launch_gemv(bool dual, const void* X, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
+                       hipStream_t st) {
   if (M < 1 || M > 2 || !gemv_supported(K)) return hipErrorNotSupported;
   const int F = dual ? N / 2 : 0;
   const ResArgs none{nullptr, nullptr, nullptr, nullptr};
-  return dual ? gemv_dispatch<true, false>((const bf16_t*)X, (const bf16_t*)W, out, M, N, K, F, none, st)
-              : gemv_dispatch<false, false>((const bf16_t*)X, (const bf16_t*)W, out, M, N, K, F, none, st);
+  const bf16_t* x = (const bf16_t*)X;
+  if (scales)
+    return dual ? gemv_dispatch<true, false, true>(x, W, scales, out, M, N, K, F, none, st)
+                : gemv_dispatch<false, false, true>(x, W, scales, out, M, N, K, F, none, st);
+  return dual ? gemv_dispatch<true, false, false>(x, W, nullptr, out, M, N, K, F, none, st)
+              : gemv_dispatch<false, false, false>(x, W, nullptr, out, M, N, K, F, none, st);
 }
 
-hipError_t launch_gemv_residual(bool dual, const void* W, void* out, int M, int N, int K, const float* h,
-                                const float* y, const float* alpha, float* hout, hipStream_t st) {
+hipError_t launch_gemv_residual(bool dual, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
+                                const float* h, const float* y, const float* alpha, float* hout, hipStream_t st) {
   if (M < 1 || M > 2 || !gemv_residual_supported(K)) return hipErrorNotSupported;
   const int F = dual ? N / 2 : 0;
   const ResArgs ra{h, y, alpha, hout};
-  return dual ? gemv_dispatch<true, true>(nullptr, (const bf16_t*)W, out, M, N, K, F, ra, st)
-              : gemv_dispatch<false, true>(nullptr, (const bf16_t*)W, out, M, N, K, F, ra, st);
+  if (scales)
+    return dual ? gemv_dispatch<true, true, true>(nullptr, W, scales, out, M, N, K, F, ra, st)
+                : gemv_dispatch<false, true, true>(nullptr, W, scales, out, M, N, K, F, ra, st);
+  return dual ? gemv_dispatch<true, true, false>(nullptr, W, nullptr, out, M, N, K, F, ra, st)
+              : gemv_dispatch<false, true, false>(nullptr, W, nullptr, out, M, N, K, F, ra, st);
+}
+
+hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* codes, void* scales, hipStream_t st) {
+  if (rows < 0 || cols <= 0 || cols % 32) return hipErrorInvalidValue;
+  const long long blocks = rows * (cols / 32);
+  if (blocks == 0) return hipSuccess;
+  DORY_LAUNCH(k_mx_quantize, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, st, (const bf16_t*)src, blocks,
+              (uint8_t*)codes, (uint8_t*)scales);
+  return hipGetLastError();
 }
 
 }  // namespace dory

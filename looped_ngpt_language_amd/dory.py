@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libdory.so")
 DORY_OK, DORY_E_INVALID, DORY_E_STATE, DORY_E_NOMEM, DORY_E_HIP = 0, -1, -2, -3, -4
 KV_MODES = {"per_loop": 0, "last_loop": 1}
 FLAG_DRY_RUN = 1
+FLAG_MXFP8_GEMV = 4
 
 
 class DoryError(RuntimeError):
@@ -74,6 +75,7 @@ EXPORTS = {
     "dory_get_stats": (C.c_int, [C.c_void_p, C.POINTER(Stats)]),
     "dory_last_hidden": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
     "dory_device_flags": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
+    "dory_quantize_mxfp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dory_spec_decode": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "dory_set_timing": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -101,13 +103,16 @@ def lib():
 
 
 def make_config(shape: synth.ModelShape, *, max_seqs=1, max_model_len=4096, max_loops=4, max_tokens=4096,
-                dry_run=False) -> Config:
+                dry_run=False, gemv_weights="bf16") -> Config:
+    if gemv_weights not in ("bf16", "mxfp8"):
+        raise ValueError(gemv_weights)
     return Config(d_model=shape.d_model, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
                   head_dim=shape.head_dim, d_ff=shape.d_ff, vocab=shape.vocab, n_in=shape.n_in, n_rec=shape.n_rec,
                   n_out=shape.n_out, full_every=shape.full_every, window=shape.window,
                   dtype=0 if shape.dtype == synth.F32 else 1, page_size=shape.page_size, max_seqs=max_seqs,
                   max_model_len=max_model_len, max_loops=max_loops, max_tokens=max_tokens,
-                  flags=FLAG_DRY_RUN if dry_run else 0, rope_theta=shape.rope_theta, attn_scale=shape.scale)
+                  flags=(FLAG_DRY_RUN if dry_run else 0) | (FLAG_MXFP8_GEMV if gemv_weights == "mxfp8" else 0),
+                  rope_theta=shape.rope_theta, attn_scale=shape.scale)
 
 
 def query_sizes(cfg: Config, kv_mode: str, kv_tokens: int):
@@ -117,6 +122,19 @@ def query_sizes(cfg: Config, kv_mode: str, kv_tokens: int):
     if st != DORY_OK:
         raise DoryError(st, "dory_query_sizes rejected the configuration")
     return kv.value, ws.value
+
+
+def quantize_mxfp8(w, stream=None):
+    """bf16 device tensor [rows, cols] -> (codes uint8 [rows, cols], scales uint8 [rows, cols/32]) on its device."""
+    import torch
+    rows, cols = w.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
+    st = stream if stream is not None else torch.cuda.current_stream(w.device)
+    r = lib().dory_quantize_mxfp8(_ptr(w), int(rows), int(cols), _ptr(codes), _ptr(scales), C.c_void_p(st.cuda_stream))
+    if r != DORY_OK:
+        raise DoryError(r, "dory_quantize_mxfp8 rejected its arguments")
+    return codes, scales
 
 
 def _ptr(t) -> int:
@@ -136,12 +154,13 @@ class Model:
 
     def __init__(self, shape: synth.ModelShape, weights=None, *, kv_mode="per_loop", max_loops=4, max_seqs=1,
                  max_model_len=4096, max_tokens=None, kv_tokens=None, device="cuda:0", dry_run=False, stream=None,
-                 share_weights_from=None):
+                 share_weights_from=None, gemv_weights="bf16"):
+        """gemv_weights="mxfp8": calls of at most 2 rows stream MXFP8 copies of the weights."""
         self.shape = shape
         self.dry = dry_run
         max_tokens = max_tokens or max_model_len
         self.cfg = make_config(shape, max_seqs=max_seqs, max_model_len=max_model_len, max_loops=max_loops,
-                               max_tokens=max_tokens, dry_run=dry_run)
+                               max_tokens=max_tokens, dry_run=dry_run, gemv_weights=gemv_weights)
         kv_tokens = kv_tokens if kv_tokens is not None else max_seqs * (max_model_len + 16)
         kv_bytes, ws_bytes = query_sizes(self.cfg, kv_mode, kv_tokens)
         self.kv_bytes, self.ws_bytes = kv_bytes, ws_bytes

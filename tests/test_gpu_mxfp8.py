@@ -1,0 +1,128 @@
+"""GPU parity of the MXFP8 weight path (OCP Microscaling Formats v1.0, E4M3 elements, E8M0
+scale per 32 elements): the device quantiser against the oracle's byte for byte, and decode
+calls that stream the MXFP8 copies against the oracle computing with the same dequantised
+weights (bf16 bars: logits 5e-2, hidden states 3e-2; ids equal except near-ties)."""
+import sys
+
+import numpy as np
+import pytest
+
+from looped_ngpt_language_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from looped_ngpt_language_amd import dory  # noqa: E402
+from oracle import OracleModel  # noqa: E402
+from oracle.mx import E4M3_TABLE, quantize_mxfp8  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_device(a):
+    bits = synth.to_bf16_bits(np.asarray(a, dtype=np.float32)).view(np.int16)
+    return torch.from_numpy(bits).to("cuda:0").view(torch.bfloat16), synth.from_bf16_bits(synth.to_bf16_bits(a))
+
+
+def test_quantizer_byte_exact_against_oracle():
+    rng = np.random.default_rng(7)
+    rows = []
+    rows.append(rng.standard_normal((64, 3072)) / np.sqrt(3072))               # unit-norm-like weight rows
+    rows.append(rng.standard_normal((32, 3072)) * np.exp(rng.uniform(-30, 30, (32, 1))))  # wide dynamic range
+    z = np.zeros((4, 3072))
+    z[1, 5] = -0.0
+    z[2, ::32] = 1.9                                                         # 1.9 / 2^-8 saturates to 448
+    z[3, :] = np.tile(np.concatenate([[256.0], 0.5 * (E4M3_TABLE[:31] + E4M3_TABLE[1:32])]), 96)  # ties
+    rows.append(z)
+    w = np.concatenate(rows).astype(np.float32)
+    dev, w_bf16 = bf16_device(w)
+    codes, scales = dory.quantize_mxfp8(dev)
+    torch.cuda.synchronize()
+    oc, osc = quantize_mxfp8(w_bf16)
+    g_codes, g_scales = codes.cpu().numpy(), scales.cpu().numpy()
+    say(f"[mxfp8] {w.shape[0]} rows x {w.shape[1]}: codes equal {np.mean(g_codes == oc):.6f}, "
+        f"scales equal {np.mean(g_scales == osc):.6f}")
+    np.testing.assert_array_equal(g_scales, osc)
+    np.testing.assert_array_equal(g_codes, oc)
+
+
+@pytest.fixture(scope="module")
+def mid_mx():
+    w = synth.make_weights(synth.MID, seed=0)
+    m = dory.Model(synth.MID, w, kv_mode="per_loop", max_loops=2, max_seqs=2, max_model_len=700, max_tokens=512,
+                   gemv_weights="mxfp8")
+    return w, m
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+@pytest.mark.parametrize("k", [1, 2])
+def test_mid_mxfp8_decode_vs_oracle(mid_mx, mode, k):
+    w, m = mid_mx
+    n_dec = 4
+    say(f"[mid mxfp8] mode={mode} k={k} prompt=300 decode={n_dec} (teacher-forced)")
+    for s in range(2):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    m.set_kv_mode(mode)
+    m.set_loops(k)
+    prompt = synth.prompt_tokens(synth.MID, 300)
+    om = OracleModel(synth.MID, w, mode, k, gemv_weights="mxfp8")
+    _, oid = om.prefill(0, prompt, 1)
+    lg, gid = m.prefill(0, prompt, 1)
+    tok = int(oid[0])
+    g_lg, o_lg, g_h, o_h, g_ids, o_ids = [], [], [], [], [], []
+    for _ in range(n_dec):
+        l1, i1 = m.decode([0], torch.tensor([tok], dtype=torch.int32, device=m.device))
+        ol, oi = om.decode([0], [tok])
+        g_lg.append(l1[0].cpu().numpy())
+        o_lg.append(ol[0])
+        g_h.append(m.last_hidden(1)[0].cpu().numpy())
+        o_h.append(om.last_hidden[0])
+        g_ids.append(int(i1[0].item()))
+        o_ids.append(int(oi[0]))
+        tok = int(oi[0])
+    g_lg, o_lg = np.array(g_lg), np.array(o_lg)
+    err_l = float(np.max(np.abs(g_lg - o_lg)))
+    err_h = float(np.max(np.abs(np.array(g_h) - np.array(o_h))))
+    say(f"  logits max-abs {err_l:.3e}, hidden max-abs {err_h:.3e}, ids {sum(a == b for a, b in zip(g_ids, o_ids))}"
+        f"/{n_dec}")
+    assert err_l <= 5e-2 and err_h <= 3e-2
+    for i in range(n_dec):
+        if g_ids[i] != o_ids[i]:
+            assert o_lg[i][o_ids[i]] - o_lg[i][g_ids[i]] < 2 * np.max(np.abs(g_lg[i] - o_lg[i]))
+
+
+def test_mid_mxfp8_two_sequence_decode_and_wide_call_stays_bf16(mid_mx):
+    """Two sequences per decode call (2-row MXFP8 GEMV) against the oracle; a decode of more
+    rows than two is not possible in this context (max_seqs 2), so the bf16 rule for wide calls
+    is covered by the prefill rows (a 300-token chunk) matching the bf16 oracle."""
+    w, m = mid_mx
+    say("[mid mxfp8] two sequences per decode call, k=2 per-loop")
+    for s in range(2):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    m.set_kv_mode("per_loop")
+    m.set_loops(2)
+    om = OracleModel(synth.MID, w, "per_loop", 2, gemv_weights="mxfp8")
+    ob = OracleModel(synth.MID, w, "per_loop", 2)
+    prompts = [synth.prompt_tokens(synth.MID, 300), synth.prompt_tokens(synth.MID, 120)]
+    for s, p in enumerate(prompts):
+        lg, _ = m.prefill(s, p, 1)
+        olg, _ = om.prefill(s, p, 1)
+        blg, _ = ob.prefill(s, p, 1)
+        np.testing.assert_array_equal(olg, blg)            # wide call: as-given weights in the oracle
+        assert np.max(np.abs(lg.cpu().numpy() - olg)) <= 5e-2
+    toks = [7, 11]
+    for _ in range(3):
+        lg, ids = m.decode([0, 1], torch.tensor(toks, dtype=torch.int32, device=m.device))
+        olg, oids = om.decode([0, 1], toks)
+        err = float(np.max(np.abs(lg.cpu().numpy() - olg)))
+        say(f"  2-row step: logits max-abs {err:.3e}")
+        assert err <= 5e-2
+        toks = [int(x) for x in oids]

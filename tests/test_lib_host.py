@@ -19,7 +19,7 @@ STACKS = synth.ModelShape(d_model=128, n_heads=4, n_kv_heads=2, head_dim=32, d_f
 
 def header_functions():
     text = open(os.path.join(ROOT, "include", "dory.h")).read()
-    return sorted(set(re.findall(r"\b(dory_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dory_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -154,3 +154,28 @@ def test_config_validation():
     cfg = dory.make_config(synth.TINY, max_loops=5, dry_run=True)
     with pytest.raises(dory.DoryError):
         dory.query_sizes(cfg, "per_loop", 64)
+
+
+def test_mxfp8_flag_sizes_and_validation():
+    """The MXFP8 flag adds ~1.03 bytes per weight to the workspace and is refused for fp32
+    models and for widths the weight-streaming GEMV does not cover."""
+    base = dory.make_config(synth.MID, dry_run=True)
+    mx = dory.make_config(synth.MID, dry_run=True, gemv_weights="mxfp8")
+    _, ws0 = dory.query_sizes(base, "per_loop", 4096)
+    _, ws1 = dory.query_sizes(mx, "per_loop", 4096)
+    s = synth.MID
+    params = s.n_blocks * ((s.n_heads + 2 * s.n_kv_heads) * s.head_dim * s.d_model + s.d_model * s.n_heads * s.head_dim
+                           + 3 * s.d_ff * s.d_model) + s.vocab * s.d_model
+    assert params * 33 // 32 <= ws1 - ws0 <= params * 33 // 32 + (1 << 20)
+    with pytest.raises(dory.DoryError):
+        dory.query_sizes(dory.make_config(synth.TINY, dry_run=True, gemv_weights="mxfp8"), "per_loop", 64)
+    with pytest.raises(dory.DoryError):
+        dory.query_sizes(dory.make_config(STACKS, dry_run=True, gemv_weights="mxfp8"), "per_loop", 64)
+
+
+def test_quantize_mxfp8_argument_errors():
+    lib = dory.lib()
+    assert lib.dory_quantize_mxfp8(None, 4, 30, None, None, None) == dory.DORY_E_INVALID   # cols % 32
+    assert lib.dory_quantize_mxfp8(None, -1, 32, None, None, None) == dory.DORY_E_INVALID
+    assert lib.dory_quantize_mxfp8(None, 4, 32, None, None, None) == dory.DORY_E_INVALID    # NULL buffers
+    assert lib.dory_quantize_mxfp8(None, 0, 32, None, None, None) == dory.DORY_OK          # nothing to do
