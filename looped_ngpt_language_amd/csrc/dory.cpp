@@ -87,7 +87,12 @@ Layout make_layout(const dory_config& c) {
     const size_t hd = (size_t)c.n_heads * c.head_dim;
     const size_t block_params = (size_t)qkv_cols(c) * d + d * hd + 2 * (size_t)c.d_ff * d + d * (size_t)c.d_ff;
     const size_t params = nb * block_params + (size_t)c.vocab * d;
-    L.mx_bytes = params + params / 32 + 16 * kAlign * (4 * nb + 1);
+    // lane-major scale rows (mx_scale_row_bytes: 32 bytes per 1024 columns, 3072 padded to 4096)
+    auto srb = [](int K) { return (size_t)dory::mx_scale_row_bytes(K); };
+    const size_t block_scales = (size_t)qkv_cols(c) * srb(d) + d * srb((int)hd) + 2 * (size_t)c.d_ff * srb(d) +
+                                d * srb(c.d_ff);
+    const size_t scales = nb * block_scales + (size_t)c.vocab * srb(d);
+    L.mx_bytes = params + scales + 16 * kAlign * (4 * nb + 1);
   }
   L.mx = take(L.mx_bytes);
   L.total = off;
@@ -676,10 +681,12 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t k
         m.codes = p;
         p += align_up(rows * cols);
         m.scales = reinterpret_cast<const uint8_t*>(p);
-        p += align_up(rows * (cols / 32));
+        const size_t sbytes = rows * (size_t)dory::mx_scale_row_bytes(cols);
+        p += align_up(sbytes);
+        if (e == hipSuccess) e = hipMemsetAsync(const_cast<uint8_t*>(m.scales), 0, sbytes, c->stream);
         if (e == hipSuccess)
           e = dory::launch_mx_quantize(src, (long long)rows, cols, const_cast<void*>(m.codes),
-                                       const_cast<uint8_t*>(m.scales), c->stream);
+                                       const_cast<uint8_t*>(m.scales), true, c->stream);
         return m;
       };
       const int d = cfg->d_model, hd = cfg->n_heads * cfg->head_dim, F = cfg->d_ff, nq = qkv_cols(*cfg);
@@ -878,7 +885,8 @@ dory_status dory_quantize_mxfp8(const void* src_dev, int64_t rows, int32_t cols,
   if (rows < 0 || cols <= 0 || cols % 32 || (rows > 0 && (!src_dev || !codes_dev || !scales_dev)))
     return DORY_E_INVALID;
   if (reinterpret_cast<uintptr_t>(src_dev) % 16 || reinterpret_cast<uintptr_t>(codes_dev) % 16) return DORY_E_INVALID;
-  hipError_t e = dory::launch_mx_quantize(src_dev, rows, cols, codes_dev, scales_dev, static_cast<hipStream_t>(stream));
+  hipError_t e =
+      dory::launch_mx_quantize(src_dev, rows, cols, codes_dev, scales_dev, false, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DORY_OK : DORY_E_HIP;
 }
 

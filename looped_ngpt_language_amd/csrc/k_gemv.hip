@@ -17,16 +17,40 @@ namespace dory {
 
 // Weights either bf16 [N, K] or (MX) MXFP8 [N, K] (OCP Microscaling Formats
 // v1.0: FP8 E4M3 element codes, one E8M0 scale 2^(code - 127) per 32 consecutive
-// elements of a row, scales [N, K/32]); an MX element pair is turned into the
-// exact bf16 pair value * scale by v_cvt_scalef32_pk_bf16_fp8 and fed to the
-// same v_dot2_f32_bf16 as the bf16 path, so MXFP8 halves the weight bytes.
+// elements of a row); an MX element pair is turned into the exact bf16 pair
+// value * scale by v_cvt_scalef32_pk_bf16_fp8 and fed to the same
+// v_dot2_f32_bf16 as the bf16 path, so MXFP8 halves the weight bytes.
 // A 16-byte lane chunk holds EPC = 8 (bf16) or 16 (MX) elements of a row.
+//
+// MX scales are stored lane-major: lane l's chunk c of a row covers scale block
+// j = 32 c + l / 2, and the row's scale bytes are laid out as [32][KCHP] (byte
+// p * KCHP + c holds block 32 c + p; KCHP = KCH rounded up to a power of two,
+// padding bytes unused), so one load of KCHP bytes brings a lane all the scales
+// of its chunks of a row.
 
 DORY_DEV float e8m0_to_f32(uint32_t code) { return __uint_as_float(code ? code << 23 : 0x00400000u); }
 
+template <int KCH> struct MxScaleRow {
+  static constexpr int P = KCH <= 1 ? 1 : KCH <= 2 ? 2 : KCH <= 4 ? 4 : 8;  // bytes per lane pair
+  static constexpr int WORDS = (P + 3) / 4;
+  static constexpr int BYTES = 32 * P;                                         // scale bytes per row
+};
+
+int mx_scale_row_bytes(int K) {
+  switch (K) {
+    case 1024: return MxScaleRow<1>::BYTES;
+    case 3072: return MxScaleRow<3>::BYTES;
+    case 4096: return MxScaleRow<4>::BYTES;
+    case 8192: return MxScaleRow<8>::BYTES;
+    default: return 0;
+  }
+}
+
 // One wave per group of R output rows; lane l reads 16-byte chunks l, l+64, ...
-// of each weight row (KCH chunks per lane, K = 64 * EPC * KCH). The weight loads
-// are issued first.
+// of each weight row (KCH chunks per lane, K = 64 * EPC * KCH). The small loads
+// of the residual prologue (h, y, alpha) are issued before the weight stream, so
+// that the prologue's arithmetic and reductions run while the weights arrive
+// (loads complete in issue order).
 template <int KCH, int R, int MR, bool DUAL, bool RES, bool MX>
 __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, const void* __restrict__ Wv,
                                               const uint8_t* __restrict__ Sc, void* __restrict__ Y, int M, int N,
@@ -36,6 +60,8 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
   constexpr int K = KCH * 64 * EPC;
   constexpr int RB = K * (MX ? 1 : 2);       // bytes per weight row
   constexpr int XU = EPC / 8;                // 16-byte x pieces per chunk
+  constexpr int EPT = RES ? K / 256 : 1;     // prologue elements per thread
+  using SR = MxScaleRow<KCH>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = blockIdx.x * 4 + (tid >> 6);
   const int nrows_out = DUAL ? F : N;
@@ -43,9 +69,26 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
   const bool active = r0 < nrows_out;
   constexpr int NB = DUAL ? 2 : 1;
   const char* W = static_cast<const char*>(Wv);
+  float hv[MR][EPT], yv[MR][EPT], av[EPT];
+  if constexpr (RES) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) av[e] = ralpha[tid + 256 * e];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = tid + 256 * e, mm = min(m, M - 1);
+        hv[m][e] = rh[(size_t)mm * K + i];
+        yv[m][e] = ry[(size_t)mm * K + i];
+      }
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
+  }
+  // Unconditional (the row index is clamped, so idle tail waves re-read the last
+  // row): a branch here would make the in-order load counter wait for the weight
+  // stream before the prologue.
   u32x4_t wr[NB][R][KCH];
-  float sc[NB][R][KCH];
-  if (active) {
+  uint32_t sw[NB][R][SR::WORDS];
+  {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -55,44 +98,46 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
 #pragma unroll
         for (int c = 0; c < KCH; ++c) wr[b][r][c] = *reinterpret_cast<const u32x4_t*>(wp + c * 1024);
         if constexpr (MX) {
-          const uint8_t* sp = Sc + (size_t)n * (K / 32);
-#pragma unroll
-          for (int c = 0; c < KCH; ++c) sc[b][r][c] = e8m0_to_f32(sp[(c * 64 + lane) >> 1]);
+          const uint8_t* sp = Sc + (size_t)n * SR::BYTES + (lane >> 1) * SR::P;
+          if constexpr (SR::P == 8) {
+            const uint2 v = *reinterpret_cast<const uint2*>(sp);
+            sw[b][r][0] = v.x;
+            sw[b][r][SR::WORDS - 1] = v.y;
+          } else if constexpr (SR::P == 4) {
+            sw[b][r][0] = *reinterpret_cast<const uint32_t*>(sp);
+          } else if constexpr (SR::P == 2) {
+            sw[b][r][0] = *reinterpret_cast<const uint16_t*>(sp);
+          } else {
+            sw[b][r][0] = *sp;
+          }
         }
       }
   }
   uint4 xr[MR][KCH][XU];
   if constexpr (RES) {
-    constexpr int EPT = K / 256;
     __shared__ __attribute__((aligned(16))) bf16_t xs[MR][K];
     __shared__ float red[4];
+    // rows m >= M (never launched: MR = M) would repeat row M - 1 and store nothing to hout;
+    // no branch here, so the loads above stay where they are
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      if (m >= M) break;
-      float hv[EPT], yv[EPT];
       float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int i = tid + 256 * e;
-        hv[e] = rh[(size_t)m * K + i];
-        yv[e] = ry[(size_t)m * K + i];
-        ss += yv[e] * yv[e];
-      }
+      for (int e = 0; e < EPT; ++e) ss += yv[m][e] * yv[m][e];
       const float iy = rsqrtf(fmaxf(block_sum(ss, red, 4), DORY_TINY_SS));
       float st = 0.f;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
-        const int i = tid + 256 * e;
-        hv[e] += ralpha[i] * (yv[e] * iy - hv[e]);
-        st += hv[e] * hv[e];
+        hv[m][e] += av[e] * (yv[m][e] * iy - hv[m][e]);
+        st += hv[m][e] * hv[m][e];
       }
       const float ih = rsqrtf(fmaxf(block_sum(st, red, 4), DORY_TINY_SS));
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
         const int i = tid + 256 * e;
-        const float v = hv[e] * ih;
+        const float v = hv[m][e] * ih;
         xs[m][i] = f32_to_bf16(v);
-        if (blockIdx.x == 0) hout[(size_t)m * K + i] = v;
+        if (blockIdx.x == 0 && m < M) hout[(size_t)m * K + i] = v;
       }
     }
     __syncthreads();
@@ -129,13 +174,14 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
           const u32x4_t w = wr[b][r][c];
           if constexpr (MX) {
             // word j holds elements 4j .. 4j+3; x piece u holds elements 8u .. 8u+7
+            const float scale = e8m0_to_f32((sw[b][r][c >> 2] >> (8 * (c & 3))) & 0xFFu);
             const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
             const uint4 x0 = xr[m][c][0], x1 = xr[m][c][1];
             const uint32_t xx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[j], sc[b][r][c], false);
-              const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[j], sc[b][r][c], true);
+              const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[j], scale, false);
+              const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[j], scale, true);
               s = __builtin_amdgcn_fdot2_f32_bf16(lo, as_bf16x2(xx[2 * j]), s, false);
               s = __builtin_amdgcn_fdot2_f32_bf16(hi, as_bf16x2(xx[2 * j + 1]), s, false);
             }
@@ -171,8 +217,11 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
 // (an all-zero block gets e = -127); each v / X is rounded to E4M3 (round to
 // nearest even on its 3-bit mantissa or, below 2^-6, on the 2^-9 subnormal
 // step), magnitudes of 448 and above saturate to 448; the sign bit is kept.
-__global__ void __launch_bounds__(256) k_mx_quantize(const bf16_t* __restrict__ src, long long blocks,
-                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+// With srb > 0 the scales are written lane-major (row stride srb bytes, see
+// above); srb = 0 gives the plain [rows, cols / 32] layout.
+__global__ void __launch_bounds__(256) k_mx_quantize(const bf16_t* __restrict__ src, long long blocks, int nblk,
+                                                     int srb, uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales) {
   const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
   if (b >= blocks) return;
   const uint4* p = reinterpret_cast<const uint4*>(src + b * 32);
@@ -187,7 +236,13 @@ __global__ void __launch_bounds__(256) k_mx_quantize(const bf16_t* __restrict__ 
   for (int i = 0; i < 16; ++i) amax_bits = max(amax_bits, max((u[i] << 16) & 0x7FFFFFFFu, u[i] & 0x7FFF0000u));
   const int ebits = (int)(amax_bits >> 23);
   const int e = max(-127, min(127, (ebits ? ebits - 127 : -200) - 8));
-  scales[b] = (uint8_t)(e + 127);
+  long long si = b;
+  if (srb > 0) {
+    const long long n = b / nblk;
+    const int j = (int)(b - n * nblk), p = srb / 32;
+    si = n * srb + (j & 31) * p + (j >> 5);
+  }
+  scales[si] = (uint8_t)(e + 127);
   uint32_t out[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = 0;
@@ -277,12 +332,15 @@ hipError_t launch_gemv_residual(bool dual, const void* W, const uint8_t* scales,
               : gemv_dispatch<false, true, false>(nullptr, W, nullptr, out, M, N, K, F, ra, st);
 }
 
-hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* codes, void* scales, hipStream_t st) {
+hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* codes, void* scales, bool lane_major,
+                              hipStream_t st) {
   if (rows < 0 || cols <= 0 || cols % 32) return hipErrorInvalidValue;
+  const int srb = lane_major ? mx_scale_row_bytes(cols) : 0;
+  if (lane_major && srb == 0) return hipErrorNotSupported;
   const long long blocks = rows * (cols / 32);
   if (blocks == 0) return hipSuccess;
   DORY_LAUNCH(k_mx_quantize, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, st, (const bf16_t*)src, blocks,
-              (uint8_t*)codes, (uint8_t*)scales);
+              cols / 32, srb, (uint8_t*)codes, (uint8_t*)scales);
   return hipGetLastError();
 }
 

@@ -64,15 +64,20 @@ hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t
 bool gemv_supported(int K);
 bool gemv_residual_supported(int K);
 // GEMV for M <= 2 bf16 rows (k_gemv.hip). W is bf16 [N, K], or with `scales` != NULL
-// MXFP8 element codes [N, K] (uint8) with E8M0 block scales [N, K/32].
+// MXFP8 element codes [N, K] (uint8) with E8M0 block scales in the lane-major layout
+// (mx_scale_row_bytes(K) bytes per row, as written by launch_mx_quantize with lane_major).
 hipError_t launch_gemv(bool dual, const void* X, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
                        hipStream_t st);
 // GEMV (M <= 2) whose input rows are N(h + alpha (N(y) - h)), computed in the prologue; the fp32
 // result is also written to hout (which must not alias h or y).
 hipError_t launch_gemv_residual(bool dual, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
                                 const float* h, const float* y, const float* alpha, float* hout, hipStream_t st);
-// bf16 [rows, cols] -> MXFP8 codes [rows, cols] + scales [rows, cols / 32] (cols % 32 == 0).
-hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* codes, void* scales, hipStream_t st);
+// bf16 [rows, cols] -> MXFP8 codes [rows, cols] + scales [rows, cols / 32] (cols % 32 == 0), or
+// with lane_major the GEMV's scale layout (rows * mx_scale_row_bytes(cols) bytes; padding untouched).
+hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* codes, void* scales, bool lane_major,
+                              hipStream_t st);
+// bytes per weight row of the lane-major MXFP8 scale layout the GEMV reads (0: K unsupported)
+int mx_scale_row_bytes(int K);
 // C = A . B^T (bf16 or fp32 model). split_ws (may be NULL) holds split-K partials for 3..256 rows.
 hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
                        float* split_ws, size_t split_ws_bytes, hipStream_t st);
