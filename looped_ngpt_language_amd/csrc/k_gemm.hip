@@ -4,7 +4,7 @@
 // fused gate/up weight (z = silu(A.Bg^T) * (A.Bu^T), Bg = rows 0..F-1 and
 // Bu = rows F..2F-1 of B) stored in the model's storage type.
 //
-//  - k_gemm_tile: bf16 MFMA (v_mfma_f32_32x32x16_bf16) tiles of 128..256 rows
+//  - k_gemm_tile: bf16 MFMA (v_mfma_f32_16x16x32_bf16) tiles of 128..256 rows
 //    and columns, LDS double-buffered, optional split-K; for the bf16 model at
 //    M > 2 (M <= 2 goes to the weight-streaming GEMV of k_gemv.hip).
 //  - k_gemm_f32: plain FMA tiles for the fp32 model.
@@ -74,12 +74,15 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, c
 
 constexpr int MF_BK = 64;
 
-// 32x32x16 bf16 MFMA operand layouts (checked on gfx950):
-//  A: lane l holds A[l%32][8*(l/32) .. +8);  B: lane l holds B^T[l%32][8*(l/32) .. +8)
-//  D: element v of lane l is D[8*(v/4) + 4*(l/32) + v%4][l%32].
+// 16x16x32 bf16 MFMA operand layouts (gfx950):
+//  A: lane l holds A[l%16][8*(l/16) .. +8);  B: lane l holds B^T[l%16][8*(l/16) .. +8)
+//  D: element v of lane l is D[4*(l/16) + v][l%16].
+// (The 32x32x16 form gives bit-identical results here but sustains a lower
+// MFMA rate under the chip's power management on these shapes: measured
+// 5-10% slower per projection.)
 //
 // Tile BM x BN x 64, WM x WN waves of (BM/WM) x (BN/WN), TM x TN MFMA tiles of
-// 32x32 per wave. LDS is double-buffered; the operand tiles of k-tile kt+1 are
+// 16x16 per wave. LDS is double-buffered; the operand tiles of k-tile kt+1 are
 // loaded into registers (16 bytes per lane per load: lane l of a wave load
 // covers bytes 16l..16l+15 of a 1 KB block = 8 tile rows of 64 bf16) while
 // k-tile kt is multiplied, and written to the idle LDS buffer afterwards, so the
@@ -108,7 +111,8 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
                                                             void* __restrict__ Cv, int M, int N, int K, int F,
                                                             int m_tiles, int n_tiles, int k_len) {
   constexpr int WAVES = WM * WN;
-  constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
+  constexpr int MS = 16;                                     // MFMA tile edge
+  constexpr int TM = BM / (MS * WM), TN = BN / (MS * WN);
   constexpr int IA = BM / (8 * WAVES), IB = BN / (8 * WAVES);  // 1 KB load instructions per wave per k-tile
   static_assert(TM >= 1 && TN >= 1 && IA * 8 * WAVES == BM && IB * 8 * WAVES == BN && (!DUAL || TN % 2 == 0),
                 "tile shape");
@@ -145,23 +149,23 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
     bsrc[i] = B + (size_t)gn * K + kbase + ((lane & 7) ^ lds_swz(r)) * 8;
   }
 
-  f32x16_t acc[TM][TN];
+  f32x4_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
 
   // B-tile row of this wave's column tile j
   int brow[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    if (DUAL) brow[j] = j < TN / 2 ? wn * (BN / (2 * WN)) + j * 32 : BN / 2 + wn * (BN / (2 * WN)) + (j - TN / 2) * 32;
-    else brow[j] = wn * (BN / WN) + j * 32;
+    if (DUAL) brow[j] = j < TN / 2 ? wn * (BN / (2 * WN)) + j * MS : BN / 2 + wn * (BN / (2 * WN)) + (j - TN / 2) * MS;
+    else brow[j] = wn * (BN / WN) + j * MS;
   }
-  const int arow0 = wm * (BM / WM) + (lane & 31);
-  const int khalf = lane >> 5;
+  const int arow0 = wm * (BM / WM) + (lane & 15);
+  const int kgrp = lane >> 4;  // 8-element k group of this lane within an MFMA's 32 k
 
   const int nk = k_len / MF_BK;
   float* const Cf = reinterpret_cast<float*>(Cv) + (size_t)blockIdx.y * M * N;
@@ -181,20 +185,20 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
   do {                                                                                                           \
     const bf16_t* as = As[S];                                                                                    \
     const bf16_t* bs = Bs[S];                                                                                    \
-    _Pragma("unroll") for (int ks = 0; ks < MF_BK / 16; ++ks) {                                                  \
-      const int ch = 2 * ks + khalf; /* logical 16-byte chunk of this lane's 8 k values */                       \
+    _Pragma("unroll") for (int ks = 0; ks < MF_BK / 32; ++ks) {                                                  \
+      const int ch = 4 * ks + kgrp; /* logical 16-byte chunk of this lane's 8 k values */                        \
       bf16x8_t af[TM], bfr[TN];                                                                                  \
       _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                                           \
-        const int r = arow0 + i * 32;                                                                            \
+        const int r = arow0 + i * MS;                                                                            \
         af[i] = *reinterpret_cast<const bf16x8_t*>(&as[r * 64 + ((ch ^ lds_swz(r)) << 3)]);                      \
       }                                                                                                          \
       _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                                           \
-        const int r = brow[j] + (lane & 31);                                                                     \
+        const int r = brow[j] + (lane & 15);                                                                     \
         bfr[j] = *reinterpret_cast<const bf16x8_t*>(&bs[r * 64 + ((ch ^ lds_swz(r)) << 3)]);                     \
       }                                                                                                          \
       _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                             \
         _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                           \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);                \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);                \
     }                                                                                                            \
   } while (0)
   u32x4_t ra[IA], rb[IB];
@@ -238,17 +242,17 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
 #undef DORY_GLOAD
 #undef DORY_SWRITE
 
-  const int col = lane & 31;
+  const int col = lane & 15;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int gm = m0 + wm * (BM / WM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    for (int v = 0; v < 4; ++v) {
+      const int gm = m0 + wm * (BM / WM) + i * MS + 4 * (lane >> 4) + v;
       if (gm >= M) continue;
       if (DUAL) {
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j) {
-          const int gc = n0 + wn * (BN / (2 * WN)) + j * 32 + col;
+          const int gc = n0 + wn * (BN / (2 * WN)) + j * MS + col;
           if (gc < F) {
             const float z = silu(acc[i][j][v]) * acc[i][j + TN / 2][v];
             reinterpret_cast<bf16_t*>(Cv)[(size_t)gm * F + gc] = f32_to_bf16(z);
@@ -257,7 +261,7 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
       } else {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int gn = n0 + wn * (BN / WN) + j * 32 + col;
+          const int gn = n0 + wn * (BN / WN) + j * MS + col;
           if (gn < N) Cf[(size_t)gm * N + gn] = acc[i][j][v];
         }
       }
@@ -294,7 +298,7 @@ static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M
   const int mt = (M + BM - 1) / BM, nt = (ncols + cols_per_tile - 1) / cols_per_tile;
   const dim3 grid(mt * nt), block(64 * WM * WN);
   if (dual) {
-    if constexpr ((BN / (32 * WN)) % 2 == 0)
+    if constexpr ((BN / (16 * WN)) % 2 == 0)
       DORY_LAUNCH((k_gemm_tile<BM, BN, WM, WN, true, PF2>), grid, block, 0, st, A, B, out, M, N, K, F, mt, nt, K);
     else
       return hipErrorNotSupported;
@@ -306,16 +310,16 @@ static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M
 
 // Tile shape: the candidate with the least estimated time, taken as the tiles
 // of the busiest CU (tiles dealt evenly over 256 CUs) times the tile's area over
-// the shape's measured per-CU rate (TFLOP/s per CU on the ~4B prefill shapes:
-// 256x256 on the gate/up projection, 128x192 on down and o, 256x160 on qkv).
-// Shapes that split N into exactly 256 equal tiles (one per CU) avoid the
-// half-empty last round that 256x256 or 128x128 tiles leave on N = 3072.
+// its measured per-CU rate (area per unit time at equal K on the ~4B prefill
+// projections: 256x256 on gate/up, 256x192 on qkv, 128x192 on o and down,
+// 256x128 and 128x128 on the same shapes). Shapes that split N into about 256
+// tiles (one per CU) avoid the half-empty last round a larger tile leaves.
 static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
                                    hipStream_t st) {
   const int ncols = dual ? F : N;
   struct Cand { int bm, bn, tn; double rate; };  // tn: MFMA column tiles per wave (dual needs an even count)
-  static const Cand cands[] = {{256, 256, 2, 4.0}, {128, 192, 3, 3.5}, {256, 160, 5, 3.45},
-                               {128, 320, 5, 3.3}, {256, 128, 2, 3.6}, {128, 128, 2, 3.6}};
+  static const Cand cands[] = {{256, 256, 8, 4.0}, {256, 192, 6, 3.69}, {128, 192, 6, 3.15},
+                               {256, 128, 4, 3.34}, {128, 128, 4, 2.87}};
   int best = 0;
   double best_t = 1e300;
   for (int i = 0; i < (int)(sizeof(cands) / sizeof(cands[0])); ++i) {
@@ -327,11 +331,10 @@ static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, 
     if (t < best_t * 0.999) { best_t = t; best = i; }
   }
   switch (best) {
-    case 0: return tile_launch<256, 256, 2, 4>(A, B, out, M, N, K, F, dual, st);
-    case 1: return tile_launch<128, 192, 4, 2, true>(A, B, out, M, N, K, F, dual, st);
-    case 2: return tile_launch<256, 160, 4, 1>(A, B, out, M, N, K, F, dual, st);
-    case 3: return tile_launch<128, 320, 2, 2>(A, B, out, M, N, K, F, dual, st);
-    case 4: return tile_launch<256, 128, 4, 2>(A, B, out, M, N, K, F, dual, st);
+    case 0: return tile_launch<256, 256, 4, 2>(A, B, out, M, N, K, F, dual, st);
+    case 1: return tile_launch<256, 192, 4, 2>(A, B, out, M, N, K, F, dual, st);
+    case 2: return tile_launch<128, 192, 4, 2, true>(A, B, out, M, N, K, F, dual, st);
+    case 3: return tile_launch<256, 128, 4, 2>(A, B, out, M, N, K, F, dual, st);
     default: return tile_launch<128, 128, 2, 2>(A, B, out, M, N, K, F, dual, st);
   }
 }
