@@ -3,8 +3,9 @@
 Importable by the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
 ``cpu_baseline`` leg, nothing else.
 """
+from . import sampling
 from .model import (LAST_LOOP, PER_LOOP, OracleModel, attend, bf16_round, greedy, l2_normalize,
                     ngpt_residual, rope, self_speculative, silu)
 
-__all__ = ["LAST_LOOP", "PER_LOOP", "OracleModel", "attend", "bf16_round", "greedy", "l2_normalize",
+__all__ = ["sampling", "LAST_LOOP", "PER_LOOP", "OracleModel", "attend", "bf16_round", "greedy", "l2_normalize",
            "ngpt_residual", "rope", "self_speculative", "silu"]
