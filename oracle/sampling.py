@@ -35,13 +35,12 @@ def nucleus(logits, temperature: float, top_p: float) -> np.ndarray:
     if top_p >= 1.0:
         return np.ones(l.shape, dtype=bool)
     p = probabilities(l, temperature)
-    values = np.unique(l)[::-1]                      # distinct logits, largest first
-    mass = 0.0
-    for v in values:                                 # lower the threshold one distinct value at a time
-        mass += p[l == v].sum()
-        if mass >= top_p:
-            return l >= v
-    return np.ones(l.shape, dtype=bool)              # rounding left the total just below top_p
+    order = np.argsort(-l, kind="stable")            # largest logits first
+    running = np.cumsum(p[order])
+    k = int(np.searchsorted(running, top_p, side="left"))   # first position whose running mass reaches top_p
+    if k >= l.size:
+        return np.ones(l.shape, dtype=bool)          # rounding left the total just below top_p
+    return l >= l[order[k]]                          # the boundary logit and every tie of it
 
 
 def sample_row(logits, temperature: float, top_p: float, u: float) -> int:
