@@ -217,6 +217,8 @@ def main():
         mm.close()
         del mm
 
+    res["sampling"] = bench_sampling(shape, args)
+
     if not args.no_batched:
         res["batched"] = bench_batched(m, shape, args, ev)
     if args.long:
@@ -267,11 +269,40 @@ def main():
             "prefill": {str(k): {"tokens": v["tokens"], "tok_s": round(v["tok_s"], 1), "ms": round(v["ms"], 3),
                                  "tflop_s": round(v["tflop_s"], 1), "mfma_frac": round(v["mfma_frac"], 4)}
                         for k, v in res["prefill"].items()},
+            "sampling_top_p": res.get("sampling"),
             "decode_bs128_k2": res.get("batched"),
             "long_context_k4": res.get("long"),
         },
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_sampling(shape, args):
+    """Temperature 1.0 / top-p 0.95 draws (dory_sample) over the vocabulary, for 1 and 128 rows of
+    seeded normal logits: microseconds per call (one workgroup per row; every pass over a row
+    reads it from L2)."""
+    import torch
+
+    from looped_ngpt_language_amd import dory
+    out = {}
+    g = torch.Generator(device="cuda:0").manual_seed(3)
+    for rows in (1, 128):
+        logits = torch.randn(rows, shape.vocab, device="cuda:0", generator=g) * 2
+        us = torch.rand(rows, device="cuda:0", generator=g)
+        for _ in range(3):
+            dory.sample(logits, us, 1.0, 0.95)
+        n = 20
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            dory.sample(logits, us, 1.0, 0.95)
+        b.record()
+        torch.cuda.synchronize()
+        t_us = a.elapsed_time(b) * 1e3 / n
+        out[str(rows)] = {"us_per_call": round(t_us, 2), "rows": rows, "vocab": shape.vocab}
+        log(f"[bench] top-p sampling, {rows} row(s) x {shape.vocab}: {t_us:.1f} us per call")
+    return out
 
 
 def bench_batched(m1, shape, args, ev):

@@ -185,6 +185,25 @@ dory_status dory_seq_len(const dory_ctx* ctx, int32_t seq_id, int32_t* len);
 dory_status dory_kv_bytes_in_use(const dory_ctx* ctx, size_t* bytes);
 dory_status dory_get_stats(const dory_ctx* ctx, dory_stats* out);
 
+/* Temperature / top-p draw (lucasainews article "NVIDIA, 루프 구조 4B 모델
+ * Dory1.0-4B 4가지 정밀도로 공개", section "실행 방법": recommended serving with
+ * temperature 1.0 and top-p 0.95) for each row of logits_dev [rows, vocab]
+ * (device, fp32, row-major, at least one finite value per row, no NaN), with
+ * the caller's uniform uniforms_dev[r] in [0, 1) (device, fp32); the token ids
+ * go to ids_dev [rows] (device, int32). Rule: token i has mass
+ * round(exp((l_i - max l) / temperature) * 2^40), an integer (sums are exact,
+ * so the draw does not depend on reduction order); the nucleus is every token
+ * whose logit is at least the largest logit value whose tokens at or above it
+ * hold at least top_p of the total mass (ties at that value all kept; top_p >= 1
+ * keeps every token, top_p <= 0 the top logit and its ties); the id is the first
+ * nucleus token in id order whose running mass exceeds floor(u * nucleus mass).
+ * temperature <= 0 is greedy (lowest id among the largest logits). Nothing is
+ * allocated; the call is queued on `stream` (a hipStream_t, NULL for the
+ * default stream). DORY_E_INVALID: rows < 0, vocab outside 1..2^23, NULL
+ * buffers with rows > 0, NaN temperature or top_p. */
+dory_status dory_sample(const float* logits_dev, int32_t rows, int32_t vocab, float temperature, float top_p,
+                        const float* uniforms_dev, int32_t* ids_dev, void* stream);
+
 /* MXFP8 quantisation (OCP Microscaling Formats v1.0, MXFP8 with E4M3 elements)
  * of a bf16 matrix src_dev [rows, cols] (device, row-major, 16-byte aligned,
  * cols % 32 == 0): per 32 consecutive elements of a row, the E8M0 scale code

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdory.so")
 OBJ = os.path.join(ROOT, "_build")
-SOURCES = ["k_rows.hip", "k_attn.hip", "k_gemm.hip", "k_gemv.hip", "dory.cpp"]
+SOURCES = ["k_rows.hip", "k_attn.hip", "k_gemm.hip", "k_gemv.hip", "k_sample.hip", "dory.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I" + os.path.join(ROOT, "include"),
          # no packed-fp32 instructions in device code

@@ -18,6 +18,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -878,6 +879,15 @@ dory_status dory_get_stats(const dory_ctx* c, dory_stats* out) {
   for (auto& s : c->seqs) live += s.live;
   out->live_seqs = live;
   return DORY_OK;
+}
+
+dory_status dory_sample(const float* logits_dev, int32_t rows, int32_t vocab, float temperature, float top_p,
+                        const float* uniforms_dev, int32_t* ids_dev, void* stream) {
+  if (rows < 0 || vocab < 1 || vocab > (1 << 23) || std::isnan(temperature) || std::isnan(top_p)) return DORY_E_INVALID;
+  if (rows > 0 && (!logits_dev || !uniforms_dev || !ids_dev)) return DORY_E_INVALID;
+  const hipError_t e =
+      dory::launch_sample(logits_dev, rows, vocab, temperature, top_p, uniforms_dev, ids_dev, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DORY_OK : DORY_E_HIP;
 }
 
 dory_status dory_quantize_mxfp8(const void* src_dev, int64_t rows, int32_t cols, void* codes_dev, void* scales_dev,

@@ -78,6 +78,10 @@ hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* c
                               hipStream_t st);
 // bytes per weight row of the lane-major MXFP8 scale layout the GEMV reads (0: K unsupported)
 int mx_scale_row_bytes(int K);
+// Temperature / top-p draw per row of fp32 logits [rows, V] with the caller's uniforms [rows]
+// (k_sample.hip); temperature <= 0 is greedy. 1 <= V <= 2^23.
+hipError_t launch_sample(const float* logits, int rows, int V, float temperature, float top_p, const float* uniforms,
+                         int32_t* ids, hipStream_t st);
 // C = A . B^T (bf16 or fp32 model). split_ws (may be NULL) holds split-K partials for 3..256 rows.
 hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
                        float* split_ws, size_t split_ws_bytes, hipStream_t st);

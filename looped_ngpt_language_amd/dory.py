@@ -76,6 +76,8 @@ EXPORTS = {
     "dory_last_hidden": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
     "dory_device_flags": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
     "dory_quantize_mxfp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dory_sample": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p, C.c_void_p,
+                              C.c_void_p]),
     "dory_spec_decode": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "dory_set_timing": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -135,6 +137,23 @@ def quantize_mxfp8(w, stream=None):
     if r != DORY_OK:
         raise DoryError(r, "dory_quantize_mxfp8 rejected its arguments")
     return codes, scales
+
+
+def sample(logits, uniforms, temperature=1.0, top_p=0.95, stream=None):
+    """fp32 device logits [rows, V] and uniforms [rows] -> int32 ids [rows] (temperature / top-p draw)."""
+    import torch
+    rows, vocab = logits.shape
+    if logits.dtype != torch.float32 or uniforms.dtype != torch.float32 or not logits.is_contiguous():
+        raise DoryError(DORY_E_INVALID, "sample needs contiguous fp32 logits and fp32 uniforms")
+    if uniforms.numel() != rows or uniforms.device != logits.device:
+        raise DoryError(DORY_E_INVALID, "one uniform per row, on the logits' device")
+    ids = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    st = stream if stream is not None else torch.cuda.current_stream(logits.device)
+    r = lib().dory_sample(_ptr(logits), int(rows), int(vocab), float(temperature), float(top_p),
+                          _ptr(uniforms.contiguous()), _ptr(ids), C.c_void_p(st.cuda_stream))
+    if r != DORY_OK:
+        raise DoryError(r, "dory_sample rejected its arguments")
+    return ids
 
 
 def _ptr(t) -> int:

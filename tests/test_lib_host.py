@@ -179,3 +179,15 @@ def test_quantize_mxfp8_argument_errors():
     assert lib.dory_quantize_mxfp8(None, -1, 32, None, None, None) == dory.DORY_E_INVALID
     assert lib.dory_quantize_mxfp8(None, 4, 32, None, None, None) == dory.DORY_E_INVALID    # NULL buffers
     assert lib.dory_quantize_mxfp8(None, 0, 32, None, None, None) == dory.DORY_OK          # nothing to do
+
+
+def test_sample_argument_errors():
+    lib = dory.lib()
+    nan = float("nan")
+    assert lib.dory_sample(None, -1, 100, 1.0, 0.95, None, None, None) == dory.DORY_E_INVALID
+    assert lib.dory_sample(None, 1, 0, 1.0, 0.95, None, None, None) == dory.DORY_E_INVALID          # vocab < 1
+    assert lib.dory_sample(None, 1, (1 << 23) + 1, 1.0, 0.95, None, None, None) == dory.DORY_E_INVALID
+    assert lib.dory_sample(None, 2, 100, 1.0, 0.95, None, None, None) == dory.DORY_E_INVALID         # NULL buffers
+    assert lib.dory_sample(None, 0, 100, nan, 0.95, None, None, None) == dory.DORY_E_INVALID
+    assert lib.dory_sample(None, 0, 100, 1.0, nan, None, None, None) == dory.DORY_E_INVALID
+    assert lib.dory_sample(None, 0, 100, 1.0, 0.95, None, None, None) == dory.DORY_OK               # nothing to do
