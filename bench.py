@@ -364,29 +364,35 @@ def bench_batched(m1, shape, args, ev):
 
 def bench_long(m1, shape, args, ev):
     """131072-token uniform-random prompt at k = 4, last-loop KV (full layers attend over the
-    whole prompt, sliding-window layers over 4096), then decode at batch 1 and self-speculative
-    decoding (k = 1 draft of 4 tokens, k = 4 verification) on the same weights."""
+    whole prompt, sliding-window layers over 4096), prefilled in 8192-token chunks with
+    sliding-window page recycling, then decode at batch 1 and self-speculative decoding (k = 1
+    draft of 4 tokens, k = 4 verification) on the same weights. Reports the KV pool with and
+    without recycling and the bytes in use."""
     import torch
 
     from looped_ngpt_language_amd import dory, synth
-    T, k, n_dec, n_spec = 131072, 4, 16, 64
+    T, k, n_dec, n_spec, chunk = 131072, 4, 16, 64, 8192
     mb = dory.Model(shape, None, kv_mode="last_loop", max_loops=4, max_seqs=1, max_model_len=T + 256,
-                    max_tokens=T, device="cuda:0", share_weights_from=m1)
+                    max_tokens=chunk, device="cuda:0", share_weights_from=m1, swa_recycle=True)
+    plain_bytes, _ = dory.query_sizes(dory.make_config(shape, max_seqs=1, max_model_len=T + 256, max_loops=4,
+                                                       max_tokens=chunk), "last_loop", T + 256)
     mb.set_loops(k)
     st = mb.stream
     prompt = torch.from_numpy(synth.prompt_tokens(shape, T, seed=1)).to("cuda:0")
     mb.timing(reset=True)
     e0, e1 = ev(), ev()
     e0.record(st)
-    _, ids = mb.prefill(0, prompt, 1)
+    for i in range(0, T, chunk):
+        _, ids = mb.prefill(0, prompt[i:i + chunk], 1)
     e1.record(st)
     torch.cuda.synchronize()
     pf_ms = e0.elapsed_time(e1)
     tim = mb.timing(reset=True)
     flops = sum(v["flops"] for v in tim.values())
     tfs = flops / (pf_ms * 1e-3) / 1e12
-    log(f"[bench] long prefill T={T} k={k}: {pf_ms / 1e3:.2f} s  {T / (pf_ms * 1e-3):,.0f} tok/s  "
-        f"{tfs:.1f} TFLOP/s ({100 * tfs / BF16_PEAK_TFLOPS:.1f}% of MFMA peak)")
+    log(f"[bench] long prefill T={T} k={k} ({chunk}-token chunks): {pf_ms / 1e3:.2f} s  "
+        f"{T / (pf_ms * 1e-3):,.0f} tok/s  {tfs:.1f} TFLOP/s ({100 * tfs / BF16_PEAK_TFLOPS:.1f}% of MFMA peak)")
+    kv_after_prefill = mb.kv_bytes_in_use()
     base_len = mb.seq_len(0)
     cur = ids.clone()
     nxt = [torch.empty(1, dtype=torch.int32, device="cuda:0") for _ in range(2)]
@@ -402,6 +408,10 @@ def bench_long(m1, shape, args, ev):
     gbs = step_bytes / (dec_ms * 1e-3) / 1e9
     log(f"[bench] long decode ctx {T} k={k}: {dec_ms:.2f} ms/step  {1e3 / dec_ms:.1f} tok/s  "
         f"{step_bytes / 1e9:.1f} GB/step -> {gbs:.0f} GB/s")
+    kv_decode = mb.kv_bytes_in_use()
+    log(f"[bench] KV with sliding-window page recycling: pool {mb.kv_bytes / 1e9:.2f} GB (without: "
+        f"{plain_bytes / 1e9:.2f} GB); in use {kv_after_prefill / 1e9:.2f} GB after the prompt, "
+        f"{kv_decode / 1e9:.2f} GB while decoding")
     mb.truncate(0, base_len)
     last = int(ids[0].item())
     t0 = time.perf_counter()
@@ -410,6 +420,7 @@ def bench_long(m1, shape, args, ev):
     sp_s = time.perf_counter() - t0
     calls = None
     spec_tok_s = len(got) / sp_s
+    mb_kv = mb.kv_bytes
     log(f"[bench] self-speculative (k=1 draft x4, k=4 verify): {len(got)} tokens in {sp_s:.2f} s -> "
         f"{spec_tok_s:.1f} tok/s ({spec_tok_s * dec_ms / 1e3:.2f}x plain k=4 decode)")
     mb.close()
@@ -418,7 +429,10 @@ def bench_long(m1, shape, args, ev):
             "prefill_mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4), "decode_tok_s": round(1e3 / dec_ms, 2),
             "decode_GB_per_step": round(step_bytes / 1e9, 2), "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "spec_tok_s": round(spec_tok_s, 2), "spec_speedup": round(spec_tok_s * dec_ms / 1e3, 3),
-            "spec_tokens": int(len(got))}
+            "spec_tokens": int(len(got)), "kv_pool_GB": round(mb_kv / 1e9, 3),
+            "kv_pool_without_recycling_GB": round(plain_bytes / 1e9, 3),
+            "kv_in_use_after_prompt_GB": round(kv_after_prefill / 1e9, 3),
+            "kv_in_use_decoding_GB": round(kv_decode / 1e9, 3)}
 
 
 def measured_traffic(role):

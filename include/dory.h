@@ -70,6 +70,18 @@ typedef enum { DORY_F32 = 0, DORY_BF16 = 1 } dory_dtype_t;
  * with d_model, n_heads*head_dim and d_ff in {1024, 3072, 4096, 8192}. The
  * workspace grows by about 1.03 bytes per weight (dory_query_sizes). */
 #define DORY_FLAG_MXFP8_GEMV 4u
+/* Context flag: sliding-window page recycling. A sliding-window layer reads
+ * only the last `window` keys (trawling.dev digest "NVIDIA, 반복 연산형 4B
+ * 언어 모델 Dory 공개", section "Reddit 반응", on the hybrid attention's cache
+ * efficiency), so its pages are kept in a page space of their own, and the
+ * pages wholly before (length - window + 1 - 64) return to the pool at the
+ * start of every prefill / decode call. Full-attention slots keep every page.
+ * The pool then holds ceil(tokens/16) pages of the full-attention slots plus up
+ * to max_seqs * ((window + 64 + max_tokens)/16 + 3) pages of the sliding-window
+ * slots (dory_query_sizes). dory_seq_truncate refuses a rollback into recycled
+ * pages (rollbacks of up to 64 tokens always succeed). Results are identical
+ * with and without the flag. Ignored without sliding-window or full layers. */
+#define DORY_FLAG_SWA_RECYCLE 8u
 
 typedef struct dory_config {
   int32_t d_model;       /* d */
@@ -124,9 +136,11 @@ typedef struct dory_stats {
   int64_t swa_apps;         /* sliding-window block applications */
   int64_t kernel_launches;  /* kernels enqueued */
   int32_t n_slots;          /* cache layer slots of the current mode */
-  int32_t pages_total;      /* pages the KV pool holds */
+  int32_t pages_total;      /* pages the KV pool holds (of the full-attention slots under SWA recycling) */
   int32_t pages_in_use;
   int32_t live_seqs;
+  int32_t swa_pages_total;  /* sliding-window pages (SWA recycling; else 0) */
+  int32_t swa_pages_in_use;
 } dory_stats;
 
 /* Bytes the caller must allocate. kv_tokens: KV capacity in tokens summed over

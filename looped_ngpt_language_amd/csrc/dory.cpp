@@ -31,6 +31,10 @@ thread_local LaunchEvents g_launch_events = {nullptr, nullptr};
 namespace {
 
 constexpr int kPage = 16;
+// SWA page recycling keeps this many positions below the window, so a sequence can be rolled
+// back (rejected speculative tokens, at most 16) and a chunk's first key block (32 keys, aligned
+// down) never touches a recycled page.
+constexpr int kSwaReserve = 64;
 constexpr int kMaxSplits = 64;
 constexpr int kStageSlots = 4;
 constexpr size_t kAlign = 256;
@@ -54,14 +58,15 @@ Layout make_layout(const dory_config& c) {
   Layout L{};
   const size_t M = c.max_tokens, d = c.d_model, es = esize(c);
   L.max_pages = (c.max_model_len + kPage - 1) / kPage;
-  const int upd_max = c.max_tokens / kPage + 2 + c.max_seqs;
+  const int upd_max = 2 * (c.max_tokens / kPage + 2 + c.max_seqs);  // full and sliding-window page tables
   L.upload_ints = 2 * c.max_tokens + 2 * upd_max + 16;
   L.part_rows = std::min(c.max_tokens, std::max(c.max_seqs, 16));
   L.logit_rows = std::max(c.max_seqs, 8);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   L.rope = take((size_t)c.max_model_len * (c.head_dim / 2) * sizeof(float2));
-  L.ptab = take((size_t)c.max_seqs * L.max_pages * 4);
+  // page tables [max_seqs][max_pages]: the full-attention one, then (SWA recycling) the sliding-window one
+  L.ptab = take((size_t)((c.flags & DORY_FLAG_SWA_RECYCLE) ? 2 : 1) * c.max_seqs * L.max_pages * 4);
   L.upload = take((size_t)L.upload_ints * 4);
   L.err = take(kAlign);
   for (int i = 0; i < 4; ++i) L.buf[i] = take(M * d * 4);
@@ -105,6 +110,43 @@ int n_slots_for(const dory_config& c, int mode) {
 }
 size_t page_elems(const dory_config& c) { return (size_t)2 * c.n_kv_heads * kPage * c.head_dim; }
 
+bool full_block(const dory_config& c, int j) { return j % c.full_every == c.full_every - 1; }
+
+// Layer slots of a KV mode split into full-attention and sliding-window ones (block j's slots
+// follow its attention kind).
+void slot_counts(const dory_config& c, int mode, int* n_full, int* n_swa) {
+  *n_full = *n_swa = 0;
+  const int nb = c.n_in + c.n_rec + c.n_out;
+  for (int j = 0; j < nb; ++j) {
+    const int copies = (mode == DORY_KV_PER_LOOP && j >= c.n_in && j < c.n_in + c.n_rec) ? c.max_loops : 1;
+    (full_block(c, j) ? *n_full : *n_swa) += copies;
+  }
+}
+
+bool recycling(const dory_config& c) {
+  int nf, ns;
+  slot_counts(c, DORY_KV_LAST_LOOP, &nf, &ns);
+  return (c.flags & DORY_FLAG_SWA_RECYCLE) && c.window > 0 && nf > 0 && ns > 0;
+}
+
+// Sliding-window pages one sequence can hold at once: the window, the reserve, one chunk, and
+// the partial pages at either end.
+int swa_pages_per_seq(const dory_config& c) { return (c.window + kSwaReserve + c.max_tokens) / kPage + 3; }
+
+// Page counts (full-attention, sliding-window) a pool of `bytes` holds: as many pages of every
+// slot as fit, except that sliding-window pages stop at what max_seqs sequences can hold, the
+// remaining bytes going to full-attention pages.
+void split_pool(const dory_config& c, int mode, size_t bytes, size_t* full_pages, size_t* swa_pages) {
+  int nf, ns;
+  slot_counts(c, mode, &nf, &ns);
+  const size_t pb = page_elems(c) * (c.dtype == DORY_F32 ? 4 : 2);
+  const size_t all = bytes / ((size_t)(nf + ns) * pb);
+  const size_t smax = (size_t)c.max_seqs * swa_pages_per_seq(c);
+  if (!recycling(c) || all <= smax) { *full_pages = *swa_pages = all; return; }
+  *swa_pages = smax;
+  *full_pages = (bytes - smax * ns * pb) / ((size_t)nf * pb);
+}
+
 std::string check_config(const dory_config* c) {
   if (!c) return "config is NULL";
   if (c->d_model <= 0 || c->d_model > 4096) return "d_model must be in 1..4096";
@@ -136,7 +178,9 @@ std::string check_config(const dory_config* c) {
 struct Seq {
   bool live = false;
   int len = 0;
-  std::vector<int32_t> pages;
+  std::vector<int32_t> pages;      // physical page of every logical page (full-attention slots, or all slots)
+  std::vector<int32_t> swa_pages;  // sliding-window slots under recycling; -1 once recycled
+  int swa_lo = 0;                  // first logical sliding-window page still held
   std::vector<std::pair<int, int>> runs;  // (end position, loops whose KV is valid) -- per-loop mode
   int min_loops() const {
     int m = 4;
@@ -182,6 +226,11 @@ struct dory_ctx {
   hipStream_t stream = nullptr;
   int n_blocks = 0, n_slots = 0, pages_total = 0;
   size_t page_el = 0, page_bytes = 0;
+  // sliding-window page recycling: separate page space for the sliding-window slots
+  bool recycle = false;
+  int n_full_slots = 0, n_swa_slots = 0, swa_pages_total = 0;
+  std::vector<int> slot_class_idx;  // per slot: index within its class, sliding-window ones negated - 1
+  std::vector<int32_t> free_swa;
   char* pool = nullptr;
   size_t pool_bytes = 0;
   char* ws = nullptr;
@@ -292,11 +341,44 @@ void recompute_capacity(dory_ctx* c) {
   c->n_slots = n_slots_for(c->cfg, c->kv_mode);
   c->page_el = page_elems(c->cfg);
   c->page_bytes = c->page_el * esize(c->cfg);
-  const size_t per_page = (size_t)c->n_slots * c->page_bytes;
-  const size_t pages = per_page ? c->pool_bytes / per_page : 0;
-  c->pages_total = (int)std::min<size_t>(pages, (size_t)INT32_MAX);
+  c->recycle = recycling(c->cfg);
+  slot_counts(c->cfg, c->kv_mode, &c->n_full_slots, &c->n_swa_slots);
+  // class of every slot: walk the blocks and loops the way slot_of numbers them
+  c->slot_class_idx.assign(c->n_slots, 0);
+  {
+    int nf = 0, ns = 0;
+    const int nb = c->cfg.n_in + c->cfg.n_rec + c->cfg.n_out;
+    const int loops = c->kv_mode == DORY_KV_PER_LOOP ? c->cfg.max_loops : 1;
+    for (int t = 1; t <= loops; ++t)
+      for (int j = 0; j < nb; ++j) {
+        const bool rec = j >= c->cfg.n_in && j < c->cfg.n_in + c->cfg.n_rec;
+        if (t > 1 && !rec) continue;
+        const int sl = slot_of(c, j, t);
+        c->slot_class_idx[sl] = full_block(c->cfg, j) ? nf++ : -(ns++) - 1;
+      }
+  }
+  size_t fp = 0, sp = 0;
+  split_pool(c->cfg, c->kv_mode, c->pool_bytes, &fp, &sp);
+  c->pages_total = (int)std::min<size_t>(fp, (size_t)INT32_MAX);
+  c->swa_pages_total = c->recycle ? (int)std::min<size_t>(sp, (size_t)INT32_MAX) : 0;
   c->free_pages.clear();
   for (int p = c->pages_total - 1; p >= 0; --p) c->free_pages.push_back(p);
+  c->free_swa.clear();
+  for (int p = c->swa_pages_total - 1; p >= 0; --p) c->free_swa.push_back(p);
+}
+
+// Cache region of layer slot (block j, loop t) and the page table its kernels follow.
+char* slot_base(dory_ctx* c, int j, int t) {
+  const int sl = slot_of(c, j, t);
+  if (!c->recycle) return c->pool + (size_t)sl * c->pages_total * c->page_bytes;
+  const int ci = c->slot_class_idx[sl];
+  const size_t full_region = (size_t)c->n_full_slots * c->pages_total * c->page_bytes;
+  if (ci >= 0) return c->pool + (size_t)ci * c->pages_total * c->page_bytes;
+  return c->pool + full_region + (size_t)(-ci - 1) * c->swa_pages_total * c->page_bytes;
+}
+const int32_t* slot_ptab(dory_ctx* c, int j) {
+  const int32_t* t = c->W<int32_t>(c->L.ptab);
+  return (c->recycle && !full_block(c->cfg, j)) ? t + (size_t)c->cfg.max_seqs * c->L.max_pages : t;
 }
 
 // Copy the host upload image to the device upload area (pinned ring, async).
@@ -417,8 +499,8 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   float* qkv = c->W<float>(c->L.qkv);
   float* y = c->W<float>(c->L.y);
   const int32_t* rows = c->W<int32_t>(c->L.upload);
-  const int32_t* ptab = c->W<int32_t>(c->L.ptab);
-  char* kv = c->pool + (size_t)slot_of(c, j, t) * c->pages_total * c->page_bytes;
+  const int32_t* ptab = slot_ptab(c, j);
+  char* kv = slot_base(c, j, t);
   hipStream_t st = c->stream;
   const double wb = wbytes(c, M);
   const bool gmx = c->mx && M <= 2;  // this call streams the MXFP8 weights
@@ -572,6 +654,15 @@ void take_pages(dory_ctx* c, int sid, int new_len) {
     c->upl.push_back(p);
     s.pages.push_back(p);
   }
+  if (!c->recycle) return;
+  const int swa_table = c->cfg.max_seqs * c->L.max_pages;  // the sliding-window table follows the full one
+  while ((int)s.swa_pages.size() < want) {
+    const int p = c->free_swa.back();
+    c->free_swa.pop_back();
+    c->upl.push_back(swa_table + sid * c->L.max_pages + (int)s.swa_pages.size());
+    c->upl.push_back(p);
+    s.swa_pages.push_back(p);
+  }
 }
 
 void release_pages_from(dory_ctx* c, Seq& s, int new_len) {
@@ -580,9 +671,37 @@ void release_pages_from(dory_ctx* c, Seq& s, int new_len) {
     c->free_pages.push_back(s.pages.back());
     s.pages.pop_back();
   }
+  while ((int)s.swa_pages.size() > keep) {
+    if (s.swa_pages.back() >= 0) c->free_swa.push_back(s.swa_pages.back());
+    s.swa_pages.pop_back();
+  }
+  s.swa_lo = std::min(s.swa_lo, (int)s.swa_pages.size());
+}
+
+// First position whose sliding-window keys a sequence of length len may still read: the next
+// query's window, less the rollback reserve.
+int swa_keep_from(const dory_ctx* c, int len) { return std::max(0, len - c->cfg.window + 1 - kSwaReserve); }
+
+// Return the sliding-window pages that lie wholly before swa_keep_from(len). The device page
+// table keeps their stale entries; no kernel reads below the window. Work already queued on the
+// context's stream that reads them runs before any later call's kernels write them.
+void recycle_swa(dory_ctx* c, Seq& s) {
+  if (!c->recycle || !s.live) return;
+  const int lo_page = std::min(swa_keep_from(c, s.len) / kPage, (int)s.swa_pages.size());
+  for (; s.swa_lo < lo_page; ++s.swa_lo) {
+    c->free_swa.push_back(s.swa_pages[s.swa_lo]);
+    s.swa_pages[s.swa_lo] = -1;
+  }
+}
+
+// Sliding-window pages a sequence needs to reach new_len.
+int swa_need(const dory_ctx* c, const Seq& s, int new_len) {
+  if (!c->recycle) return 0;
+  return (new_len + kPage - 1) / kPage - (int)(s.live ? s.swa_pages.size() : 0);
 }
 
 int pages_in_use(const dory_ctx* c) { return c->pages_total - (int)c->free_pages.size(); }
+int swa_pages_in_use(const dory_ctx* c) { return c->swa_pages_total - (int)c->free_swa.size(); }
 
 }  // namespace
 
@@ -609,7 +728,15 @@ dory_status dory_query_sizes(const dory_config* cfg, int32_t kv_mode, int64_t kv
   if (kv_mode != DORY_KV_PER_LOOP && kv_mode != DORY_KV_LAST_LOOP) return DORY_E_INVALID;
   if (kv_tokens < 0 || !kv_pool_bytes || !workspace_bytes) return DORY_E_INVALID;
   const size_t pages = (size_t)((kv_tokens + kPage - 1) / kPage);
-  *kv_pool_bytes = pages * n_slots_for(*cfg, kv_mode) * page_elems(*cfg) * esize(*cfg);
+  const size_t pb = page_elems(*cfg) * esize(*cfg);
+  *kv_pool_bytes = pages * n_slots_for(*cfg, kv_mode) * pb;
+  if (recycling(*cfg)) {
+    // full-attention slots for every token; sliding-window slots for what max_seqs sequences hold at once
+    int nf, ns;
+    slot_counts(*cfg, kv_mode, &nf, &ns);
+    const size_t swa = std::min(pages, (size_t)cfg->max_seqs * swa_pages_per_seq(*cfg));
+    *kv_pool_bytes = (pages * nf + swa * ns) * pb;
+  }
   *workspace_bytes = make_layout(*cfg).total;
   return DORY_OK;
 }
@@ -760,9 +887,14 @@ dory_status dory_prefill(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, in
     return fail(c, DORY_E_INVALID, "length %d + %d exceeds max_model_len %d", len, n, c->cfg.max_model_len);
   if (c->kv_mode == DORY_KV_PER_LOOP && s.live && len > 0 && s.min_loops() < c->k)
     return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), c->k);
+  recycle_swa(c, s);
   const int need = (len + n + kPage - 1) / kPage - (int)(s.live ? s.pages.size() : 0);
   if (need > (int)c->free_pages.size())
     return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
+  const int need_swa = swa_need(c, s, len + n);
+  if (need_swa > (int)c->free_swa.size())
+    return fail(c, DORY_E_NOMEM, "sliding-window KV pages exhausted: %d needed, %zu free", need_swa,
+                c->free_swa.size());
   // commit host state and build the upload: rows, then page-table updates
   if (!s.live) { s = Seq(); s.live = true; }
   c->upl.clear();
@@ -796,7 +928,7 @@ dory_status dory_decode(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
   if (!seq_ids) return fail(c, DORY_E_INVALID, "seq_ids_host is NULL");
   if (!c->dry && !tokens_dev) return fail(c, DORY_E_INVALID, "tokens_dev is NULL");
   if (!logits_dev && n > c->L.logit_rows) return fail(c, DORY_E_INVALID, "logits scratch holds %d rows", c->L.logit_rows);
-  int need = 0;
+  int need = 0, need_swa = 0;
   for (int i = 0; i < n; ++i) {
     const int sid = seq_ids[i];
     if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
@@ -808,8 +940,13 @@ dory_status dory_decode(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
       return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), c->k);
     need += (s.len + 1 + kPage - 1) / kPage - (int)s.pages.size();
   }
+  for (int i = 0; i < n; ++i) recycle_swa(c, c->seqs[seq_ids[i]]);
+  for (int i = 0; i < n; ++i) need_swa += swa_need(c, c->seqs[seq_ids[i]], c->seqs[seq_ids[i]].len + 1);
   if (need > (int)c->free_pages.size())
     return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
+  if (need_swa > (int)c->free_swa.size())
+    return fail(c, DORY_E_NOMEM, "sliding-window KV pages exhausted: %d needed, %zu free", need_swa,
+                c->free_swa.size());
   c->upl.clear();
   for (int i = 0; i < n; ++i) { c->upl.push_back(seq_ids[i]); c->upl.push_back(c->seqs[seq_ids[i]].len); }
   const size_t n_rows_ints = c->upl.size();
@@ -842,6 +979,9 @@ dory_status dory_seq_truncate(dory_ctx* c, int32_t sid, int32_t new_len) {
   if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
   Seq& s = c->seqs[sid];
   if (new_len < 0 || new_len > s.len) return fail(c, DORY_E_INVALID, "truncate to %d outside 0..%d", new_len, s.len);
+  if (c->recycle && s.swa_lo > 0 && std::max(0, new_len - c->cfg.window + 1) < s.swa_lo * kPage)
+    return fail(c, DORY_E_STATE, "truncate to %d needs sliding-window pages already recycled (held from %d)", new_len,
+                s.swa_lo * kPage);
   release_pages_from(c, s, new_len);
   s.trim_runs(new_len);
   s.len = new_len;
@@ -865,7 +1005,10 @@ dory_status dory_seq_len(const dory_ctx* c, int32_t sid, int32_t* len) {
 
 dory_status dory_kv_bytes_in_use(const dory_ctx* c, size_t* bytes) {
   if (!c || !bytes) return DORY_E_INVALID;
-  *bytes = (size_t)pages_in_use(c) * c->n_slots * c->page_bytes;
+  if (c->recycle)
+    *bytes = ((size_t)pages_in_use(c) * c->n_full_slots + (size_t)swa_pages_in_use(c) * c->n_swa_slots) * c->page_bytes;
+  else
+    *bytes = (size_t)pages_in_use(c) * c->n_slots * c->page_bytes;
   return DORY_OK;
 }
 
@@ -875,6 +1018,8 @@ dory_status dory_get_stats(const dory_ctx* c, dory_stats* out) {
   out->n_slots = c->n_slots;
   out->pages_total = c->pages_total;
   out->pages_in_use = pages_in_use(c);
+  out->swa_pages_total = c->swa_pages_total;
+  out->swa_pages_in_use = swa_pages_in_use(c);
   int live = 0;
   for (auto& s : c->seqs) live += s.live;
   out->live_seqs = live;

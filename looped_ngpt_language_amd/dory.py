@@ -22,6 +22,7 @@ DORY_OK, DORY_E_INVALID, DORY_E_STATE, DORY_E_NOMEM, DORY_E_HIP = 0, -1, -2, -3,
 KV_MODES = {"per_loop": 0, "last_loop": 1}
 FLAG_DRY_RUN = 1
 FLAG_MXFP8_GEMV = 4
+FLAG_SWA_RECYCLE = 8
 
 
 class DoryError(RuntimeError):
@@ -46,7 +47,8 @@ class WeightsC(C.Structure):
 class Stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("calls", "block_apps", "sublayer_apps", "full_apps", "swa_apps",
                                          "kernel_launches")] + \
-              [(n, C.c_int32) for n in ("n_slots", "pages_total", "pages_in_use", "live_seqs")]
+              [(n, C.c_int32) for n in ("n_slots", "pages_total", "pages_in_use", "live_seqs", "swa_pages_total",
+                                        "swa_pages_in_use")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -105,7 +107,7 @@ def lib():
 
 
 def make_config(shape: synth.ModelShape, *, max_seqs=1, max_model_len=4096, max_loops=4, max_tokens=4096,
-                dry_run=False, gemv_weights="bf16") -> Config:
+                dry_run=False, gemv_weights="bf16", swa_recycle=False) -> Config:
     if gemv_weights not in ("bf16", "mxfp8"):
         raise ValueError(gemv_weights)
     return Config(d_model=shape.d_model, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
@@ -113,7 +115,8 @@ def make_config(shape: synth.ModelShape, *, max_seqs=1, max_model_len=4096, max_
                   n_out=shape.n_out, full_every=shape.full_every, window=shape.window,
                   dtype=0 if shape.dtype == synth.F32 else 1, page_size=shape.page_size, max_seqs=max_seqs,
                   max_model_len=max_model_len, max_loops=max_loops, max_tokens=max_tokens,
-                  flags=(FLAG_DRY_RUN if dry_run else 0) | (FLAG_MXFP8_GEMV if gemv_weights == "mxfp8" else 0),
+                  flags=(FLAG_DRY_RUN if dry_run else 0) | (FLAG_MXFP8_GEMV if gemv_weights == "mxfp8" else 0)
+                  | (FLAG_SWA_RECYCLE if swa_recycle else 0),
                   rope_theta=shape.rope_theta, attn_scale=shape.scale)
 
 
@@ -173,13 +176,16 @@ class Model:
 
     def __init__(self, shape: synth.ModelShape, weights=None, *, kv_mode="per_loop", max_loops=4, max_seqs=1,
                  max_model_len=4096, max_tokens=None, kv_tokens=None, device="cuda:0", dry_run=False, stream=None,
-                 share_weights_from=None, gemv_weights="bf16"):
-        """gemv_weights="mxfp8": calls of at most 2 rows stream MXFP8 copies of the weights."""
+                 share_weights_from=None, gemv_weights="bf16", swa_recycle=False):
+        """gemv_weights="mxfp8": calls of at most 2 rows stream MXFP8 copies of the weights.
+        swa_recycle: sliding-window layers keep only the pages their window (plus a 64-token
+        rollback reserve) can reach; kv_tokens then sizes the full-attention pages."""
         self.shape = shape
         self.dry = dry_run
         max_tokens = max_tokens or max_model_len
         self.cfg = make_config(shape, max_seqs=max_seqs, max_model_len=max_model_len, max_loops=max_loops,
-                               max_tokens=max_tokens, dry_run=dry_run, gemv_weights=gemv_weights)
+                               max_tokens=max_tokens, dry_run=dry_run, gemv_weights=gemv_weights,
+                               swa_recycle=swa_recycle)
         kv_tokens = kv_tokens if kv_tokens is not None else max_seqs * (max_model_len + 16)
         kv_bytes, ws_bytes = query_sizes(self.cfg, kv_mode, kv_tokens)
         self.kv_bytes, self.ws_bytes = kv_bytes, ws_bytes

@@ -191,3 +191,62 @@ def test_sample_argument_errors():
     assert lib.dory_sample(None, 0, 100, nan, 0.95, None, None, None) == dory.DORY_E_INVALID
     assert lib.dory_sample(None, 0, 100, 1.0, nan, None, None, None) == dory.DORY_E_INVALID
     assert lib.dory_sample(None, 0, 100, 1.0, 0.95, None, None, None) == dory.DORY_OK               # nothing to do
+
+
+def test_swa_recycling_pool_size_4b_long_context():
+    # 131072 + 512 tokens, last-loop KV: the 9 full-attention slots keep every page, the 27
+    # sliding-window slots only what one sequence's window, reserve and chunk reach
+    s = synth.DORY4B
+    kw = dict(max_seqs=1, max_model_len=131072 + 512 + 16, max_tokens=4096, dry_run=True)
+    tokens = 131072 + 512
+    b0, _ = dory.query_sizes(dory.make_config(s, **kw), "last_loop", tokens)
+    b1, _ = dory.query_sizes(dory.make_config(s, swa_recycle=True, **kw), "last_loop", tokens)
+    pb = 2 * s.n_kv_heads * 16 * s.head_dim * 2
+    pages = -(-tokens // 16)
+    assert b0 == pages * 36 * pb                                     # ~19.4 GB
+    assert b1 == (pages * 9 + ((4096 + 64 + 4096) // 16 + 3) * 27) * pb
+    # the pool also holds one 4096-token chunk of window pages: ~5.8 GB allocated, ~5.3 GB in use
+    # while decoding (full pages + window and reserve)
+    assert 19.0e9 < b0 < 19.6e9 and 5.5e9 < b1 < 5.9e9
+
+
+def test_swa_recycling_page_accounting():
+    s = synth.TINY                      # window 16; blocks 3 and 7 full: last-loop 2 full + 6 window slots
+    m = dry(s, mode="last_loop", max_model_len=1024, max_tokens=32, max_seqs=2, swa_recycle=True)
+    pb = 2 * s.n_kv_heads * 16 * s.head_dim * 4
+    m.prefill(0, list(range(32)), 1)
+    before = 32
+    for _ in range(300):
+        m.decode([0], [1])
+        before += 1
+    length = before
+    st = m.stats()
+    assert st["pages_in_use"] == -(-length // 16)
+    # held window pages: logical pages from (len_before_last_call - 16 + 1 - 64) // 16 to the end
+    lo = max(0, (length - 1) - 16 + 1 - 64) // 16
+    assert st["swa_pages_in_use"] == -(-length // 16) - lo
+    assert m.kv_bytes_in_use() == (st["pages_in_use"] * 2 + st["swa_pages_in_use"] * 6) * pb
+    m.truncate(0, length - 10)                       # inside the reserve
+    with pytest.raises(dory.DoryError) as e:
+        m.truncate(0, length - 200)                  # its window pages are gone
+    assert e.value.status == dory.DORY_E_STATE
+    assert m.seq_len(0) == length - 10
+    # a second sequence reuses recycled window pages
+    m.prefill(1, list(range(32)), 1)
+    st2 = m.stats()
+    assert st2["swa_pages_in_use"] == (-(-(length - 10) // 16) - lo) + 2   # truncated seq 0, plus 2 pages of seq 1
+    m.release(0)
+    m.release(1)
+    st3 = m.stats()
+    assert st3["pages_in_use"] == 0 and st3["swa_pages_in_use"] == 0
+
+
+def test_swa_recycling_off_keeps_every_slot_page():
+    s = synth.TINY
+    m = dry(s, mode="last_loop", max_model_len=1024, max_tokens=32, max_seqs=2)
+    m.prefill(0, list(range(32)), 1)
+    for _ in range(300):
+        m.decode([0], [1])
+    st = m.stats()
+    assert st["swa_pages_total"] == 0 and st["swa_pages_in_use"] == 0
+    assert m.kv_bytes_in_use() == st["pages_in_use"] * 8 * (2 * s.n_kv_heads * 16 * s.head_dim * 4)
