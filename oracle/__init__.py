@@ -5,7 +5,7 @@ Importable by the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
 """
 from . import sampling
 from .model import (LAST_LOOP, PER_LOOP, OracleModel, attend, bf16_round, greedy, l2_normalize,
-                    ngpt_residual, rope, self_speculative, silu)
+                    ngpt_residual, rope, self_speculative, self_speculative_reuse, silu)
 
 __all__ = ["sampling", "LAST_LOOP", "PER_LOOP", "OracleModel", "attend", "bf16_round", "greedy", "l2_normalize",
-           "ngpt_residual", "rope", "self_speculative", "silu"]
+           "ngpt_residual", "rope", "self_speculative", "self_speculative_reuse", "silu"]

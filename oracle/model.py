@@ -265,17 +265,25 @@ class OracleModel:
 
     def forward_chunk(self, seq: _Seq, tokens, pos0: int, trace=None, mx=False):
         """Hidden states after the output stack for one chunk [onedev-how]."""
-        s = self.s
-        tokens = np.asarray(tokens, dtype=np.int64)
         pos = pos0 + np.arange(len(tokens))
-        h = self.E[tokens]
-        for j in range(s.n_in):
-            h = self._block(h, j, 1, seq, pos, mx)
-        x = h
-        st = x                                   # s_0 = x
+        x = self.input_stack(seq, tokens, pos, mx)
         if trace is not None:
             trace["x"] = x
-        for t in range(1, self.k + 1):
+        st = self.core_loops(seq, x, x, 1, pos, trace, mx)   # s_0 = x
+        return self.output_stack(seq, st, pos, mx)
+
+    def input_stack(self, seq: _Seq, tokens, pos, mx=False):
+        """Embedding and the input stack: x."""
+        h = self.E[np.asarray(tokens, dtype=np.int64)]
+        for j in range(self.s.n_in):
+            h = self._block(h, j, 1, seq, pos, mx)
+        return h
+
+    def core_loops(self, seq: _Seq, x, st, t_first: int, pos, trace=None, mx=False, t_last=None):
+        """Loops t_first..t_last (default k) of the recurrent core from state st = s_{t_first - 1}:
+        u_t = N(s_{t-1} + x), s_t = N(F(u_t)). Returns s_{t_last}."""
+        s = self.s
+        for t in range(t_first, (self.k if t_last is None else t_last) + 1):
             u = l2_normalize(st + x)             # u_t = N(s_{t-1} + x)
             h = u
             for j in range(s.n_in, s.n_in + s.n_rec):
@@ -284,8 +292,11 @@ class OracleModel:
             if trace is not None:
                 trace.setdefault("u", []).append(u)
                 trace.setdefault("s", []).append(st)
+        return st
+
+    def output_stack(self, seq: _Seq, st, pos, mx=False):
         h = st
-        for j in range(s.n_in + s.n_rec, s.n_blocks):
+        for j in range(self.s.n_in + self.s.n_rec, self.s.n_blocks):
             h = self._block(h, j, 1, seq, pos, mx)
         return h
 
@@ -342,6 +353,26 @@ class OracleModel:
             seq.V[sl][new_len:] = np.nan
         seq.len = new_len
 
+    def head_rows(self, seq_id: int, tokens):
+        """Input stack and loop 1 only, for a chunk appended to the sequence (its KV written in
+        those slots): returns (x, s_1)."""
+        seq = self.seqs[seq_id]
+        pos = seq.len + np.arange(len(tokens))
+        x = self.input_stack(seq, tokens, pos)
+        s1 = self.core_loops(seq, x, x, 1, pos, t_last=1)
+        seq.len += len(tokens)
+        return x, s1
+
+    def resume_rows(self, seq_id: int, pos0: int, x, s1, logits_rows: int):
+        """Loops 2..k, the output stack and the LM head for the rows at positions pos0.. whose x
+        and s_1 are given (their input-stack and loop-1 KV already in the cache)."""
+        seq = self.seqs[seq_id]
+        pos = pos0 + np.arange(len(x))
+        st = self.core_loops(seq, np.asarray(x), np.asarray(s1), 2, pos)
+        h = self.output_stack(seq, st, pos)
+        self.last_hidden = h
+        return self.lm_head(h[len(x) - logits_rows:])
+
     def release(self, seq_id: int):
         del self.seqs[seq_id]
 
@@ -392,6 +423,44 @@ def self_speculative(model: OracleModel, seq_id: int, prompt, n_tokens: int,
         model.truncate(seq_id, base)
         model.set_loops(k_verify)
         _, v = model.prefill(seq_id, [last] + drafts, gamma + 1)
+        n_acc = 0
+        while n_acc < gamma and drafts[n_acc] == int(v[n_acc]):
+            n_acc += 1
+        out.extend(drafts[:n_acc])
+        out.append(int(v[n_acc]))
+        model.truncate(seq_id, base + n_acc + 1)
+    return np.array(out, dtype=np.int32)
+
+
+def self_speculative_reuse(model: OracleModel, seq_id: int, prompt, n_tokens: int,
+                           gamma: int = 4, k_verify: int = 4):
+    """Self-speculative greedy decoding with a k = 1 draft whose work the verify pass reuses
+    [onedev-limits]. Under the chunk semantics, a drafted row's input-stack output x, its loop-1
+    state s_1 and the KV both write are what the verify chunk would compute again (the input
+    stack and loop 1 see the same keys either way, in both KV modes), so the verify pass keeps
+    the draft's cache, runs the input stack and loop 1 only for the one row the draft never ran
+    (d_gamma), and runs loops 2..k_verify, the output stack and the LM head for all gamma + 1
+    rows from the saved x and s_1. In exact arithmetic this equals self_speculative with
+    k_draft = 1. Returns the ids produced after the prompt (at least n_tokens of them)."""
+    model.set_loops(k_verify)
+    _, ids = model.prefill(seq_id, prompt, 1)
+    out = [int(ids[0])]
+    while len(out) < n_tokens:
+        base = model.seq_len(seq_id)
+        last = out[-1]
+        model.set_loops(1)
+        xs, s1s, drafts = [], [], []
+        tok = last
+        for _ in range(gamma):
+            tr = {}
+            _, i = model.prefill(seq_id, [tok], 1, trace=tr)   # a one-token chunk: one decode step
+            xs.append(tr["x"][0])
+            s1s.append(tr["s"][0][0])
+            tok = int(i[0])
+            drafts.append(tok)
+        x_l, s1_l = model.head_rows(seq_id, [drafts[-1]])
+        model.set_loops(k_verify)
+        _, v = model.resume_rows(seq_id, base, np.array(xs + [x_l[0]]), np.array(s1s + [s1_l[0]]), gamma + 1)
         n_acc = 0
         while n_acc < gamma and drafts[n_acc] == int(v[n_acc]):
             n_acc += 1

@@ -14,7 +14,7 @@ import pytest
 
 from looped_ngpt_language_amd import synth
 from oracle import (LAST_LOOP, PER_LOOP, OracleModel, attend, bf16_round, greedy, l2_normalize,
-                    ngpt_residual, rope, self_speculative, silu)
+                    ngpt_residual, rope, self_speculative, self_speculative_reuse, silu)
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))
 
@@ -371,6 +371,56 @@ def test_self_speculative_per_loop_equals_k4_greedy(tiny_weights):
     m = OracleModel(synth.TINY, tiny_weights, PER_LOOP, 4)
     got = self_speculative(m, 0, toks, 13)
     np.testing.assert_array_equal(got[:13], ref[:13])
+
+
+@pytest.mark.parametrize("mode", [PER_LOOP, LAST_LOOP])
+def test_spec_reuse_round_equals_plain_verify(tiny_weights, mode):
+    """One draft/verify round both ways: the verify logits of the reuse procedure (input stack and
+    loop 1 of drafted rows taken from the k = 1 draft, cache kept) equal those of a fresh verify
+    chunk, to fp64 rounding."""
+    toks = synth.prompt_tokens(synth.TINY, 20)
+    gamma = 4
+    ma = OracleModel(synth.TINY, tiny_weights, mode, 4)
+    mb = OracleModel(synth.TINY, tiny_weights, mode, 4)
+    _, ida = ma.prefill(0, toks, 1)
+    mb.prefill(0, toks, 1)
+    last = int(ida[0])
+    base = ma.seq_len(0)
+    # plain: draft at k = 1, truncate, verify [last, d1..d4] at k = 4
+    ma.set_loops(1)
+    drafts, tok = [], last
+    for _ in range(gamma):
+        _, i = ma.decode([0], [tok])
+        tok = int(i[0])
+        drafts.append(tok)
+    ma.truncate(0, base)
+    ma.set_loops(4)
+    la, _ = ma.prefill(0, [last] + drafts, gamma + 1)
+    # reuse: same drafts, x and s_1 kept, loops 2..4 + output stack for all rows
+    mb.set_loops(1)
+    xs, s1s = [], []
+    for t in [last] + drafts[:-1]:
+        tr = {}
+        mb.prefill(0, [t], 1, trace=tr)
+        xs.append(tr["x"][0])
+        s1s.append(tr["s"][0][0])
+    xl, s1l = mb.head_rows(0, [drafts[-1]])
+    mb.set_loops(4)
+    lb, _ = mb.resume_rows(0, base, np.array(xs + [xl[0]]), np.array(s1s + [s1l[0]]), gamma + 1)
+    assert np.max(np.abs(la - lb)) < 1e-9
+    assert ma.seq_len(0) == mb.seq_len(0) == base + gamma + 1
+
+
+@pytest.mark.parametrize("mode", [PER_LOOP, LAST_LOOP])
+@pytest.mark.parametrize("gamma", [2, 4])
+def test_spec_reuse_ids_equal_plain_spec(tiny_weights, mode, gamma):
+    toks = synth.prompt_tokens(synth.TINY, 16)
+    a = self_speculative(OracleModel(synth.TINY, tiny_weights, mode, 4), 0, toks, 14, gamma=gamma, k_draft=1)
+    b = self_speculative_reuse(OracleModel(synth.TINY, tiny_weights, mode, 4), 0, toks, 14, gamma=gamma)
+    np.testing.assert_array_equal(a[:14], b[:14])
+    if mode == PER_LOOP:                          # and both equal plain k = 4 greedy
+        ref, _ = run_greedy(tiny_weights, PER_LOOP, 4, toks, 13)
+        np.testing.assert_array_equal(b[:14], ref[:14])
 
 
 def test_error_paths(tiny_weights):
