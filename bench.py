@@ -82,7 +82,7 @@ def main():
     w = synth.make_weights(shape, seed=0)
     log(f"[bench] weights drawn in {time.time() - t0:.1f}s")
     prompt = synth.prompt_tokens(shape, max(args.prompt, args.prefill_len))
-    max_len = args.prompt + args.warmup + args.steps + 32
+    max_len = args.prompt + max(args.warmup + args.steps, 48 + 4 + 1) + 32   # decode steps, or the speculative run
     t0 = time.time()
     # created in per-loop mode so the pool also holds a per-loop sequence (96 cache slots per page)
     m = dory.Model(shape, w, kv_mode="per_loop", max_loops=4, max_seqs=1, max_model_len=max_len,
@@ -218,6 +218,7 @@ def main():
         del mm
 
     res["sampling"] = bench_sampling(shape, args)
+    res["spec"] = bench_spec(m, ptoks, plog, res["decode"].get(4), args)
 
     if not args.no_batched:
         res["batched"] = bench_batched(m, shape, args, ev)
@@ -270,11 +271,43 @@ def main():
                                  "tflop_s": round(v["tflop_s"], 1), "mfma_frac": round(v["mfma_frac"], 4)}
                         for k, v in res["prefill"].items()},
             "sampling_top_p": res.get("sampling"),
+            "self_speculative_k1x4_k4": res.get("spec"),
             "decode_bs128_k2": res.get("batched"),
             "long_context_k4": res.get("long"),
         },
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_spec(m, ptoks, plog, plain4, args):
+    """Self-speculative greedy decoding at batch 1 on the same context (k = 1 draft of 4 tokens,
+    k = 4 verify, last-loop KV), with and without reuse of the draft's input-stack output,
+    loop-1 state and cache in the verify pass; tok/s over 48 produced ids (host round trip per
+    verify included), against plain k = 4 decode."""
+    import torch
+    out = {"plain_k4_tok_s": round(plain4["tok_s"], 2) if plain4 else None}
+    m.set_kv_mode("last_loop")
+    for reuse in (False, True):
+        m.set_loops(4)
+        _, pid = m.prefill(0, ptoks, 1, logits=plog)
+        first = int(pid[0].item())
+        m.spec_decode(0, first, 8, gamma=4, k_draft=1, k_verify=4, reuse=reuse)    # warm-up
+        m.release(0)
+        _, pid = m.prefill(0, ptoks, 1, logits=plog)
+        first = int(pid[0].item())
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        got = m.spec_decode(0, first, 48, gamma=4, k_draft=1, k_verify=4, reuse=reuse)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        m.release(0)
+        key = "reuse" if reuse else "no_reuse"
+        out[f"{key}_tok_s"] = round(len(got) / dt, 2)
+        out[f"{key}_tokens"] = int(len(got))
+        log(f"[bench] self-speculative k=1 x4 / k=4, {'with' if reuse else 'without'} reuse: {len(got)} ids in "
+            f"{dt:.3f} s -> {len(got) / dt:.1f} tok/s"
+            + (f" ({len(got) / dt / plain4['tok_s']:.2f}x plain k=4)" if plain4 else ""))
+    return out
 
 
 def bench_sampling(shape, args):
@@ -412,24 +445,29 @@ def bench_long(m1, shape, args, ev):
     log(f"[bench] KV with sliding-window page recycling: pool {mb.kv_bytes / 1e9:.2f} GB (without: "
         f"{plain_bytes / 1e9:.2f} GB); in use {kv_after_prefill / 1e9:.2f} GB after the prompt, "
         f"{kv_decode / 1e9:.2f} GB while decoding")
-    mb.truncate(0, base_len)
     last = int(ids[0].item())
-    t0 = time.perf_counter()
-    got = mb.spec_decode(0, last, n_spec, gamma=4, k_draft=1, k_verify=4)
-    torch.cuda.synchronize()
-    sp_s = time.perf_counter() - t0
-    calls = None
-    spec_tok_s = len(got) / sp_s
+    spec = {}
+    for reuse in (False, True):
+        mb.truncate(0, base_len)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        got = mb.spec_decode(0, last, n_spec, gamma=4, k_draft=1, k_verify=4, reuse=reuse)
+        torch.cuda.synchronize()
+        sp_s = time.perf_counter() - t0
+        spec[reuse] = (len(got), len(got) / sp_s)
+        log(f"[bench] self-speculative (k=1 draft x4, k=4 verify, {'with' if reuse else 'without'} reuse): "
+            f"{len(got)} tokens in {sp_s:.2f} s -> {len(got) / sp_s:.1f} tok/s "
+            f"({len(got) / sp_s * dec_ms / 1e3:.2f}x plain k=4 decode)")
+    got, spec_tok_s = [0] * spec[False][0], spec[False][1]
     mb_kv = mb.kv_bytes
-    log(f"[bench] self-speculative (k=1 draft x4, k=4 verify): {len(got)} tokens in {sp_s:.2f} s -> "
-        f"{spec_tok_s:.1f} tok/s ({spec_tok_s * dec_ms / 1e3:.2f}x plain k=4 decode)")
     mb.close()
     return {"prompt_tokens": T, "loops": k, "prefill_s": round(pf_ms / 1e3, 3),
             "prefill_tok_s": round(T / (pf_ms * 1e-3), 1), "prefill_tflop_s": round(tfs, 1),
             "prefill_mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4), "decode_tok_s": round(1e3 / dec_ms, 2),
             "decode_GB_per_step": round(step_bytes / 1e9, 2), "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "spec_tok_s": round(spec_tok_s, 2), "spec_speedup": round(spec_tok_s * dec_ms / 1e3, 3),
-            "spec_tokens": int(len(got)), "kv_pool_GB": round(mb_kv / 1e9, 3),
+            "spec_tokens": int(len(got)), "spec_reuse_tok_s": round(spec[True][1], 2),
+            "spec_reuse_speedup": round(spec[True][1] * dec_ms / 1e3, 3), "kv_pool_GB": round(mb_kv / 1e9, 3),
             "kv_pool_without_recycling_GB": round(plain_bytes / 1e9, 3),
             "kv_in_use_after_prompt_GB": round(kv_after_prefill / 1e9, 3),
             "kv_in_use_decoding_GB": round(kv_decode / 1e9, 3)}

@@ -240,15 +240,22 @@ dory_status dory_device_flags(dory_ctx* ctx, int32_t* flags, int32_t reset);
 dory_status dory_last_hidden(dory_ctx* ctx, float* dst_dev, int32_t rows);
 
 /* Self-speculative greedy decoding on one live sequence (onedev.kr summary,
- * section "전제와 한계"): draft `gamma` tokens with k_draft loops by decode calls,
- * roll the cache back, verify [last, d_1..d_gamma] as one chunk with k_verify
- * loops, keep the longest agreeing prefix plus the verifier's next token and
- * roll back past the rest. `last_host` is the newest generated id (not yet in
- * the cache). Produces at least n_new ids into out_ids_host (capacity
- * n_new + gamma) and returns their count in *n_out. Synchronises the stream once
- * per verify step (the accepted length decides the next step). */
+ * section "전제와 한계"): draft `gamma` (1..16) tokens with k_draft loops by
+ * decode calls, verify [last, d_1..d_gamma] as one chunk with k_verify loops,
+ * keep the longest agreeing prefix plus the verifier's next token and roll the
+ * cache back past the rest. reuse = 0: the cache is rolled back to the start of
+ * the draft and the verify chunk runs the whole stack. reuse = 1 (needs
+ * k_draft = 1): a drafted row's input-stack output, loop-1 state and the KV both
+ * write are what the verify chunk would compute again, so the draft's cache is
+ * kept, d_gamma alone runs the input stack and loop 1, and loops 2..k_verify,
+ * the output stack and the LM head run for all gamma + 1 rows from the saved
+ * states (equal to reuse = 0 in exact arithmetic). `last_host` is the newest
+ * generated id (not yet in the cache). Produces at least n_new ids into
+ * out_ids_host (capacity n_new + gamma) and returns their count in *n_out.
+ * Synchronises the stream once per verify step (the accepted length decides the
+ * next step). */
 dory_status dory_spec_decode(dory_ctx* ctx, int32_t seq_id, int32_t last_host, int32_t n_new,
-                             int32_t gamma, int32_t k_draft, int32_t k_verify,
+                             int32_t gamma, int32_t k_draft, int32_t k_verify, int32_t reuse,
                              int32_t* out_ids_host, int32_t* n_out);
 
 /* Per-kernel accounting, one entry per kernel role of the forward pass

@@ -36,14 +36,15 @@ constexpr int kPage = 16;
 // down) never touches a recycled page.
 constexpr int kSwaReserve = 64;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxGamma = 16;  // speculative draft length limit
 constexpr int kStageSlots = 4;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {  // byte offsets inside the workspace
-  size_t rope, ptab, upload, err, buf[4], y, hb, qkv, q, o, z, part_ml, part_o, logits, argmax, splitk, spec, mx, mx_bytes,
-      total;
+  size_t rope, ptab, upload, err, buf[4], y, hb, qkv, q, o, z, part_ml, part_o, logits, argmax, splitk, spec, spec_x,
+      spec_s1, mx, mx_bytes, total;
   size_t splitk_bytes;
   int max_pages;       // pages per sequence
   int upload_ints;     // capacity of the upload area in int32
@@ -86,6 +87,9 @@ Layout make_layout(const dory_config& c) {
     L.splitk = take(L.splitk_bytes);
   }
   L.spec = take(64 * 4);
+  // self-speculative decoding with reuse: input-stack output and loop-1 state of the drafted rows
+  L.spec_x = take((size_t)(kMaxGamma + 1) * d * 4);
+  L.spec_s1 = take((size_t)(kMaxGamma + 1) * d * 4);
   // MXFP8 copies of every projection and of the LM head (codes, then scales per matrix)
   L.mx_bytes = 0;
   if (c.flags & DORY_FLAG_MXFP8_GEMV) {
@@ -571,7 +575,19 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
 
 // Whole forward pass over M rows whose (seq, pos) pairs are in the upload area.
 // Leaves the final hidden rows in c->last_h and their storage copy in hb.
-void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, const Geom& geo) {
+// What one forward call runs: the whole stack (FULL), or only the embedding, input stack and
+// loop 1 (HEAD), or loops 2..k and the output stack for rows whose input-stack output and
+// loop-1 state are given (RESUME). FULL and HEAD can copy those two states of their rows out.
+struct FwdOpts {
+  enum Phase { FULL, HEAD, RESUME } phase = FULL;
+  float* cap_x = nullptr;
+  float* cap_s1 = nullptr;
+  const float* res_x = nullptr;
+  const float* res_s1 = nullptr;
+};
+
+void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, const Geom& geo,
+                 const FwdOpts& o = FwdOpts()) {
   using namespace dory;
   const dory_config& g = c->cfg;
   const int dt = g.dtype, d = g.d_model;
@@ -579,24 +595,38 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, con
   float* b[4] = {c->W<float>(c->L.buf[0]), c->W<float>(c->L.buf[1]), c->W<float>(c->L.buf[2]),
                  c->W<float>(c->L.buf[3])};
   void* hb = c->W(c->L.hb);
-  if (!c->dry) {
-    Span sp(c, R_EMBED, Md * d * (2 * es + 4) + Md * 4, 0);
-    ok(c, launch_embed(dt, tokens_dev, c->embed, g.vocab, d, M, b[0], hb, c->W<int32_t>(c->L.err), c->stream));
-  } else {
-    c->stats.kernel_launches++;
-  }
+  auto copy_rows = [&](float* dst, const float* src) {
+    if (c->dry) { c->stats.kernel_launches++; return; }
+    ok(c, launch_copy_f32(dst, src, (size_t)M * d, c->stream));
+  };
+  float* x;
   Flow f{b[0], b[3]};
-  for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, f, decode, geo);
-  flush(c, f, M);
-  // x = input-stack output; the other three buffers hold h, s and the spare
-  float* x = f.h;
+  if (o.phase != FwdOpts::RESUME) {
+    if (!c->dry) {
+      Span sp(c, R_EMBED, Md * d * (2 * es + 4) + Md * 4, 0);
+      ok(c, launch_embed(dt, tokens_dev, c->embed, g.vocab, d, M, b[0], hb, c->W<int32_t>(c->L.err), c->stream));
+    } else {
+      c->stats.kernel_launches++;
+    }
+    for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, f, decode, geo);
+    flush(c, f, M);
+    x = f.h;  // input-stack output
+    if (o.cap_x) copy_rows(o.cap_x, x);
+  } else {
+    x = b[0];
+    copy_rows(x, o.res_x);
+  }
+  // the other three buffers hold h, s and the spare
   float* rest[3];
   int nr = 0;
   for (float* p : b)
     if (p != x) rest[nr++] = p;
   float* s = rest[1];
   f = Flow{rest[0], rest[2]};
-  for (int t = 1; t <= c->k; ++t) {
+  if (o.phase == FwdOpts::RESUME) copy_rows(s, o.res_s1);
+  const int t_first = o.phase == FwdOpts::RESUME ? 2 : 1;
+  const int t_last = o.phase == FwdOpts::HEAD ? 1 : c->k;
+  for (int t = t_first; t <= t_last; ++t) {
     // u_t = N(s_{t-1} + x), with s_0 = x
     if (!c->dry) {
       Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
@@ -613,6 +643,12 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, con
     } else {
       c->stats.kernel_launches++;
     }
+    if (t == 1 && o.cap_s1) copy_rows(o.cap_s1, s);
+  }
+  if (o.phase == FwdOpts::HEAD) {
+    c->last_h = s;
+    c->last_rows = M;
+    return;
   }
   for (int j = g.n_in + g.n_rec; j < c->n_blocks; ++j) run_block(c, j, 1, M, f, decode, geo);
   flush(c, f, M);
@@ -702,6 +738,150 @@ int swa_need(const dory_ctx* c, const Seq& s, int new_len) {
 
 int pages_in_use(const dory_ctx* c) { return c->pages_total - (int)c->free_pages.size(); }
 int swa_pages_in_use(const dory_ctx* c) { return c->swa_pages_total - (int)c->free_swa.size(); }
+
+}  // namespace
+
+namespace {
+
+dory_status prefill_impl(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, int32_t n, int32_t logits_rows,
+                         float* logits_dev, int32_t* ids_dev, const FwdOpts& o) {
+  const bool head = o.phase == FwdOpts::HEAD;  // input stack and loop 1 only: no logits
+  const int k_run = head ? 1 : c->k;
+  if (!c) return DORY_E_INVALID;
+  if (!valid_seq(c, sid)) return fail(c, DORY_E_INVALID, "seq_id %d outside 0..%d", sid, c->cfg.max_seqs - 1);
+  if (n < 1 || n > c->cfg.max_tokens) return fail(c, DORY_E_INVALID, "n_tokens %d outside 1..%d", n, c->cfg.max_tokens);
+  if (!head && (logits_rows < 1 || logits_rows > n))
+    return fail(c, DORY_E_INVALID, "logits_rows %d outside 1..%d", logits_rows, n);
+  if (!c->dry && (!tokens_dev || (!head && !logits_dev)))
+    return fail(c, DORY_E_INVALID, "tokens_dev and logits_dev are required");
+  Seq& s = c->seqs[sid];
+  const int len = s.live ? s.len : 0;
+  if ((int64_t)len + n > c->cfg.max_model_len)
+    return fail(c, DORY_E_INVALID, "length %d + %d exceeds max_model_len %d", len, n, c->cfg.max_model_len);
+  if (c->kv_mode == DORY_KV_PER_LOOP && s.live && len > 0 && s.min_loops() < k_run)
+    return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), k_run);
+  recycle_swa(c, s);
+  const int need = (len + n + kPage - 1) / kPage - (int)(s.live ? s.pages.size() : 0);
+  if (need > (int)c->free_pages.size())
+    return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
+  const int need_swa = swa_need(c, s, len + n);
+  if (need_swa > (int)c->free_swa.size())
+    return fail(c, DORY_E_NOMEM, "sliding-window KV pages exhausted: %d needed, %zu free", need_swa,
+                c->free_swa.size());
+  // commit host state and build the upload: rows, then page-table updates
+  if (!s.live) { s = Seq(); s.live = true; }
+  c->upl.clear();
+  for (int i = 0; i < n; ++i) { c->upl.push_back(sid); c->upl.push_back(len + i); }
+  const size_t n_rows_ints = c->upl.size();
+  take_pages(c, sid, len + n);
+  const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
+  c->herr = hipSuccess;
+  if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
+  if (!c->dry && n_upd) {
+    Span sp(c, R_PTAB, 12.0 * n_upd, 0);
+    ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
+                                     c->stream));
+  }
+  s.len = len + n;
+  s.append_run(s.len, k_run);
+  Geom geo;
+  geo.add_chunk(len, n, c->cfg.window);
+  run_forward(c, tokens_dev, n, false, geo, o);
+  if (!head) lm_head(c, n, logits_rows, logits_dev, ids_dev);
+  c->stats.calls++;
+  if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
+  return DORY_OK;
+}
+
+dory_status decode_impl(dory_ctx* c, int32_t n, const int32_t* seq_ids, const int32_t* tokens_dev, float* logits_dev,
+                        int32_t* next_ids_dev, const FwdOpts& o) {
+  if (!c) return DORY_E_INVALID;
+  if (n < 1 || n > c->cfg.max_tokens || n > c->cfg.max_seqs)
+    return fail(c, DORY_E_INVALID, "n_seqs %d outside 1..%d", n, std::min(c->cfg.max_tokens, c->cfg.max_seqs));
+  if (!seq_ids) return fail(c, DORY_E_INVALID, "seq_ids_host is NULL");
+  if (!c->dry && !tokens_dev) return fail(c, DORY_E_INVALID, "tokens_dev is NULL");
+  if (!logits_dev && n > c->L.logit_rows) return fail(c, DORY_E_INVALID, "logits scratch holds %d rows", c->L.logit_rows);
+  int need = 0, need_swa = 0;
+  for (int i = 0; i < n; ++i) {
+    const int sid = seq_ids[i];
+    if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
+    for (int j = 0; j < i; ++j)
+      if (seq_ids[j] == sid) return fail(c, DORY_E_INVALID, "seq %d listed twice", sid);
+    const Seq& s = c->seqs[sid];
+    if (s.len + 1 > c->cfg.max_model_len) return fail(c, DORY_E_INVALID, "seq %d reached max_model_len", sid);
+    if (c->kv_mode == DORY_KV_PER_LOOP && s.len > 0 && s.min_loops() < c->k)
+      return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), c->k);
+    need += (s.len + 1 + kPage - 1) / kPage - (int)s.pages.size();
+  }
+  for (int i = 0; i < n; ++i) recycle_swa(c, c->seqs[seq_ids[i]]);
+  for (int i = 0; i < n; ++i) need_swa += swa_need(c, c->seqs[seq_ids[i]], c->seqs[seq_ids[i]].len + 1);
+  if (need > (int)c->free_pages.size())
+    return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
+  if (need_swa > (int)c->free_swa.size())
+    return fail(c, DORY_E_NOMEM, "sliding-window KV pages exhausted: %d needed, %zu free", need_swa,
+                c->free_swa.size());
+  c->upl.clear();
+  for (int i = 0; i < n; ++i) { c->upl.push_back(seq_ids[i]); c->upl.push_back(c->seqs[seq_ids[i]].len); }
+  const size_t n_rows_ints = c->upl.size();
+  for (int i = 0; i < n; ++i) take_pages(c, seq_ids[i], c->seqs[seq_ids[i]].len + 1);
+  const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
+  c->herr = hipSuccess;
+  if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
+  if (!c->dry && n_upd) {
+    Span sp(c, R_PTAB, 12.0 * n_upd, 0);
+    ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
+                                     c->stream));
+  }
+  Geom geo;
+  for (int i = 0; i < n; ++i) {
+    Seq& s = c->seqs[seq_ids[i]];
+    geo.add_chunk(s.len, 1, c->cfg.window);
+    s.len += 1;
+    s.append_run(s.len, c->k);
+  }
+  run_forward(c, tokens_dev, n, true, geo, o);
+  float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
+  lm_head(c, n, n, logits, next_ids_dev);
+  c->stats.calls++;
+  if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
+  return DORY_OK;
+}
+
+// Loops 2..k, the output stack and the LM head for the last n positions of a sequence, from
+// their input-stack output res_x and loop-1 state res_s1 (device, fp32 [n][d]); their input-stack
+// and loop-1 KV must already be in the cache (self-speculative verify with reuse).
+dory_status resume_impl(dory_ctx* c, int32_t sid, int32_t n, const float* res_x, const float* res_s1, float* logits_dev,
+                        int32_t* ids_dev) {
+  Seq& s = c->seqs[sid];
+  if (!s.live || n < 1 || n > s.len || n > c->cfg.max_tokens) return fail(c, DORY_E_INVALID, "bad resume rows");
+  const int pos0 = s.len - n;
+  if (c->kv_mode == DORY_KV_PER_LOOP && pos0 > 0) {
+    int m = 4;  // loops held by the positions before the resumed rows
+    int start = 0;
+    for (auto& r : s.runs) {
+      if (start < pos0) m = std::min(m, r.second);
+      start = r.first;
+    }
+    if (m < c->k) return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, m, c->k);
+  }
+  c->upl.clear();
+  for (int i = 0; i < n; ++i) { c->upl.push_back(sid); c->upl.push_back(pos0 + i); }
+  c->herr = hipSuccess;
+  if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
+  s.trim_runs(pos0);
+  s.append_run(s.len, c->k);
+  Geom geo;
+  geo.add_chunk(pos0, n, c->cfg.window);
+  FwdOpts o;
+  o.phase = FwdOpts::RESUME;
+  o.res_x = res_x;
+  o.res_s1 = res_s1;
+  run_forward(c, nullptr, n, false, geo, o);
+  lm_head(c, n, n, logits_dev, ids_dev);
+  c->stats.calls++;
+  if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
+  return DORY_OK;
+}
 
 }  // namespace
 
@@ -876,103 +1056,14 @@ dory_status dory_kv_mode(dory_ctx* c, int32_t mode) {
 
 dory_status dory_prefill(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, int32_t n, int32_t logits_rows,
                          float* logits_dev, int32_t* ids_dev) {
-  if (!c) return DORY_E_INVALID;
-  if (!valid_seq(c, sid)) return fail(c, DORY_E_INVALID, "seq_id %d outside 0..%d", sid, c->cfg.max_seqs - 1);
-  if (n < 1 || n > c->cfg.max_tokens) return fail(c, DORY_E_INVALID, "n_tokens %d outside 1..%d", n, c->cfg.max_tokens);
-  if (logits_rows < 1 || logits_rows > n) return fail(c, DORY_E_INVALID, "logits_rows %d outside 1..%d", logits_rows, n);
-  if (!c->dry && (!tokens_dev || !logits_dev)) return fail(c, DORY_E_INVALID, "tokens_dev and logits_dev are required");
-  Seq& s = c->seqs[sid];
-  const int len = s.live ? s.len : 0;
-  if ((int64_t)len + n > c->cfg.max_model_len)
-    return fail(c, DORY_E_INVALID, "length %d + %d exceeds max_model_len %d", len, n, c->cfg.max_model_len);
-  if (c->kv_mode == DORY_KV_PER_LOOP && s.live && len > 0 && s.min_loops() < c->k)
-    return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), c->k);
-  recycle_swa(c, s);
-  const int need = (len + n + kPage - 1) / kPage - (int)(s.live ? s.pages.size() : 0);
-  if (need > (int)c->free_pages.size())
-    return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
-  const int need_swa = swa_need(c, s, len + n);
-  if (need_swa > (int)c->free_swa.size())
-    return fail(c, DORY_E_NOMEM, "sliding-window KV pages exhausted: %d needed, %zu free", need_swa,
-                c->free_swa.size());
-  // commit host state and build the upload: rows, then page-table updates
-  if (!s.live) { s = Seq(); s.live = true; }
-  c->upl.clear();
-  for (int i = 0; i < n; ++i) { c->upl.push_back(sid); c->upl.push_back(len + i); }
-  const size_t n_rows_ints = c->upl.size();
-  take_pages(c, sid, len + n);
-  const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
-  c->herr = hipSuccess;
-  if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
-  if (!c->dry && n_upd) {
-    Span sp(c, R_PTAB, 12.0 * n_upd, 0);
-    ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
-                                     c->stream));
-  }
-  s.len = len + n;
-  s.append_run(s.len, c->k);
-  Geom geo;
-  geo.add_chunk(len, n, c->cfg.window);
-  run_forward(c, tokens_dev, n, false, geo);
-  lm_head(c, n, logits_rows, logits_dev, ids_dev);
-  c->stats.calls++;
-  if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
-  return DORY_OK;
+  return prefill_impl(c, sid, tokens_dev, n, logits_rows, logits_dev, ids_dev, FwdOpts());
 }
 
 dory_status dory_decode(dory_ctx* c, int32_t n, const int32_t* seq_ids, const int32_t* tokens_dev, float* logits_dev,
                         int32_t* next_ids_dev) {
-  if (!c) return DORY_E_INVALID;
-  if (n < 1 || n > c->cfg.max_tokens || n > c->cfg.max_seqs)
-    return fail(c, DORY_E_INVALID, "n_seqs %d outside 1..%d", n, std::min(c->cfg.max_tokens, c->cfg.max_seqs));
-  if (!seq_ids) return fail(c, DORY_E_INVALID, "seq_ids_host is NULL");
-  if (!c->dry && !tokens_dev) return fail(c, DORY_E_INVALID, "tokens_dev is NULL");
-  if (!logits_dev && n > c->L.logit_rows) return fail(c, DORY_E_INVALID, "logits scratch holds %d rows", c->L.logit_rows);
-  int need = 0, need_swa = 0;
-  for (int i = 0; i < n; ++i) {
-    const int sid = seq_ids[i];
-    if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
-    for (int j = 0; j < i; ++j)
-      if (seq_ids[j] == sid) return fail(c, DORY_E_INVALID, "seq %d listed twice", sid);
-    const Seq& s = c->seqs[sid];
-    if (s.len + 1 > c->cfg.max_model_len) return fail(c, DORY_E_INVALID, "seq %d reached max_model_len", sid);
-    if (c->kv_mode == DORY_KV_PER_LOOP && s.len > 0 && s.min_loops() < c->k)
-      return fail(c, DORY_E_STATE, "per-loop cache of seq %d holds %d loops, %d requested", sid, s.min_loops(), c->k);
-    need += (s.len + 1 + kPage - 1) / kPage - (int)s.pages.size();
-  }
-  for (int i = 0; i < n; ++i) recycle_swa(c, c->seqs[seq_ids[i]]);
-  for (int i = 0; i < n; ++i) need_swa += swa_need(c, c->seqs[seq_ids[i]], c->seqs[seq_ids[i]].len + 1);
-  if (need > (int)c->free_pages.size())
-    return fail(c, DORY_E_NOMEM, "KV pool exhausted: %d pages needed, %zu free", need, c->free_pages.size());
-  if (need_swa > (int)c->free_swa.size())
-    return fail(c, DORY_E_NOMEM, "sliding-window KV pages exhausted: %d needed, %zu free", need_swa,
-                c->free_swa.size());
-  c->upl.clear();
-  for (int i = 0; i < n; ++i) { c->upl.push_back(seq_ids[i]); c->upl.push_back(c->seqs[seq_ids[i]].len); }
-  const size_t n_rows_ints = c->upl.size();
-  for (int i = 0; i < n; ++i) take_pages(c, seq_ids[i], c->seqs[seq_ids[i]].len + 1);
-  const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
-  c->herr = hipSuccess;
-  if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
-  if (!c->dry && n_upd) {
-    Span sp(c, R_PTAB, 12.0 * n_upd, 0);
-    ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
-                                     c->stream));
-  }
-  Geom geo;
-  for (int i = 0; i < n; ++i) {
-    Seq& s = c->seqs[seq_ids[i]];
-    geo.add_chunk(s.len, 1, c->cfg.window);
-    s.len += 1;
-    s.append_run(s.len, c->k);
-  }
-  run_forward(c, tokens_dev, n, true, geo);
-  float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
-  lm_head(c, n, n, logits, next_ids_dev);
-  c->stats.calls++;
-  if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
-  return DORY_OK;
+  return decode_impl(c, n, seq_ids, tokens_dev, logits_dev, next_ids_dev, FwdOpts());
 }
+
 
 dory_status dory_seq_truncate(dory_ctx* c, int32_t sid, int32_t new_len) {
   if (!c) return DORY_E_INVALID;
@@ -1111,10 +1202,11 @@ dory_status dory_get_timing(dory_ctx* c, dory_kernel_time* out, int32_t max, int
 }
 
 dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_new, int32_t gamma, int32_t k_draft,
-                             int32_t k_verify, int32_t* out_ids, int32_t* n_out) {
+                             int32_t k_verify, int32_t reuse, int32_t* out_ids, int32_t* n_out) {
   if (!c || !out_ids || !n_out) return DORY_E_INVALID;
   if (!valid_seq(c, sid) || !c->seqs[sid].live) return fail(c, DORY_E_INVALID, "seq %d is not live", sid);
-  if (gamma < 1 || gamma > 16 || n_new < 1) return fail(c, DORY_E_INVALID, "gamma must be 1..16 and n_new >= 1");
+  if (gamma < 1 || gamma > kMaxGamma || n_new < 1) return fail(c, DORY_E_INVALID, "gamma must be 1..16 and n_new >= 1");
+  if (reuse && k_draft != 1) return fail(c, DORY_E_INVALID, "reusing the draft needs k_draft = 1");
   if (k_draft < 1 || k_draft > c->cfg.max_loops || k_verify < 1 || k_verify > c->cfg.max_loops)
     return fail(c, DORY_E_INVALID, "loop counts outside 1..%d", c->cfg.max_loops);
   if (gamma + 1 > c->cfg.max_tokens || gamma + 1 > c->L.logit_rows)
@@ -1133,11 +1225,30 @@ dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_n
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);  // `last` lives on this host stack frame
     if (e != hipSuccess) { st = fail(c, DORY_E_HIP, "%s", hipGetErrorString(e)); break; }
     c->k = k_draft;
-    for (int i = 0; i < gamma && st == DORY_OK; ++i) st = dory_decode(c, 1, &sid, toks + i, nullptr, toks + i + 1);
+    const size_t dm = (size_t)c->cfg.d_model;
+    float* sx = c->W<float>(c->L.spec_x);
+    float* ss = c->W<float>(c->L.spec_s1);
+    for (int i = 0; i < gamma && st == DORY_OK; ++i) {
+      FwdOpts o;  // with reuse, keep each drafted row's x and loop-1 state
+      if (reuse) { o.cap_x = sx + i * dm; o.cap_s1 = ss + i * dm; }
+      st = decode_impl(c, 1, &sid, toks + i, nullptr, toks + i + 1, o);
+    }
     if (st != DORY_OK) break;
-    if ((st = dory_seq_truncate(c, sid, base)) != DORY_OK) break;
-    c->k = k_verify;
-    if ((st = dory_prefill(c, sid, toks, gamma + 1, gamma + 1, logits, vids)) != DORY_OK) break;
+    if (reuse) {
+      // the draft's cache stays: input stack and loop 1 for d_gamma only, then loops 2..k_verify,
+      // the output stack and the LM head for all gamma + 1 rows
+      FwdOpts o;
+      o.phase = FwdOpts::HEAD;
+      o.cap_x = sx + gamma * dm;
+      o.cap_s1 = ss + gamma * dm;
+      if ((st = prefill_impl(c, sid, toks + gamma, 1, 1, nullptr, nullptr, o)) != DORY_OK) break;
+      c->k = k_verify;
+      if ((st = resume_impl(c, sid, gamma + 1, sx, ss, logits, vids)) != DORY_OK) break;
+    } else {
+      if ((st = dory_seq_truncate(c, sid, base)) != DORY_OK) break;
+      c->k = k_verify;
+      if ((st = dory_prefill(c, sid, toks, gamma + 1, gamma + 1, logits, vids)) != DORY_OK) break;
+    }
     e = hipMemcpyAsync(host.data(), toks, (gamma + 1) * 4, hipMemcpyDeviceToHost, c->stream);
     if (e == hipSuccess) e = hipMemcpyAsync(host.data() + gamma + 1, vids, (gamma + 1) * 4, hipMemcpyDeviceToHost, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);

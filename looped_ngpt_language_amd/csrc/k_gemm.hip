@@ -305,14 +305,16 @@ static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M
 // of the busiest CU (tiles dealt evenly over 256 CUs) times the tile's area over
 // its measured per-CU rate (area per unit time at equal K on the ~4B prefill
 // projections: 256x256 on gate/up, 256x192 on qkv, 128x192 on o and down,
-// 256x128 and 128x128 on the same shapes). Shapes that split N into about 256
+// 256x128 and 128x128 on the same shapes; 256x128 over several rounds, where
+// its activation re-reads cost most: 2560-token gate/up fetched 1.46 GB per
+// launch from beyond L2 against 0.30 GB for 256x256). Shapes that split N into about 256
 // tiles (one per CU) avoid the half-empty last round a larger tile leaves.
 static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, int M, int N, int K, int F, bool dual,
                                    hipStream_t st) {
   const int ncols = dual ? F : N;
   struct Cand { int bm, bn, tn; double rate; };  // tn: MFMA column tiles per wave (dual needs an even count)
   static const Cand cands[] = {{256, 256, 8, 4.0}, {256, 192, 6, 3.69}, {128, 192, 6, 3.15},
-                               {256, 128, 4, 3.34}, {128, 128, 4, 2.87}};
+                               {256, 128, 4, 3.0}, {128, 128, 4, 2.87}};
   int best = 0;
   double best_t = 1e300;
   for (int i = 0; i < (int)(sizeof(cands) / sizeof(cands[0])); ++i) {

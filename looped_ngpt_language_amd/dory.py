@@ -81,7 +81,7 @@ EXPORTS = {
     "dory_sample": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p, C.c_void_p,
                               C.c_void_p]),
     "dory_spec_decode": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                   C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+                                   C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "dory_set_timing": (C.c_int, [C.c_void_p, C.c_int32]),
     "dory_get_timing": (C.c_int, [C.c_void_p, C.POINTER(KernelTime), C.c_int32, C.POINTER(C.c_int32), C.c_int32]),
     "dory_last_error": (C.c_char_p, [C.c_void_p]),
@@ -361,10 +361,12 @@ class Model:
                                     "timed_launches": e.timed_launches, "ms": e.total_ms}
         return out
 
-    def spec_decode(self, seq_id: int, last: int, n_new: int, gamma=4, k_draft=1, k_verify=4):
+    def spec_decode(self, seq_id: int, last: int, n_new: int, gamma=4, k_draft=1, k_verify=4, reuse=False):
+        """reuse=True (k_draft 1): the verify pass reuses the draft's input-stack output, loop-1
+        state and cache instead of recomputing them."""
         buf = (C.c_int32 * (n_new + gamma + 1))()
         n = C.c_int32()
         st = lib().dory_spec_decode(self.ctx, int(seq_id), int(last), int(n_new), int(gamma), int(k_draft),
-                                    int(k_verify), buf, C.byref(n))
+                                    int(k_verify), int(bool(reuse)), buf, C.byref(n))
         self._check(st, "dory_spec_decode")
         return np.array(buf[:n.value], dtype=np.int32)

@@ -203,6 +203,52 @@ def test_tiny_fp32_self_speculative(tiny, mode):
 
 
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_tiny_fp32_self_speculative_reuse(tiny, mode):
+    """dory_spec_decode with reuse (the verify pass takes the k=1 draft's input-stack output,
+    loop-1 state and cache) against the oracle's reuse driver, ids bit-exact; the same ids as
+    without reuse."""
+    from oracle import self_speculative_reuse
+    w, m = tiny
+    say(f"[tiny fp32] self-speculative decoding with reuse, {mode}")
+    for s in range(4):
+        if m.seq_len(s) >= 0:
+            m.release(s)
+    m.set_kv_mode(mode)
+    m.set_loops(4)
+    prompt = synth.prompt_tokens(synth.TINY, 30)
+    _, ids = m.prefill(0, prompt, 1)
+    first = int(ids[0].item())
+    got = m.spec_decode(0, first, 20, gamma=4, k_draft=1, k_verify=4, reuse=True)
+    m.release(0)
+    _, ids = m.prefill(0, prompt, 1)
+    plain = m.spec_decode(0, first, 20, gamma=4, k_draft=1, k_verify=4, reuse=False)
+    om = OracleModel(synth.TINY, w, mode, 4)
+    want = self_speculative_reuse(om, 0, prompt, 21, gamma=4, k_verify=4)
+    say(f"  gpu {list(got[:20])}\n  oracle {list(want[1:21])}")
+    np.testing.assert_array_equal(got[:20], want[1:21])
+    np.testing.assert_array_equal(got[:20], plain[:20])
+    with pytest.raises(dory.DoryError):
+        m.spec_decode(0, int(plain[-1]), 4, gamma=4, k_draft=2, k_verify=4, reuse=True)
+
+
+def test_mid_bf16_self_speculative_reuse_matches_plain():
+    """bf16 mid model, last-loop KV: speculative decoding with and without reuse produce the same
+    ids (the reused rows' states come from the decode kernels instead of the chunk kernels)."""
+    w = synth.make_weights(synth.MID, seed=0)
+    m = dory.Model(synth.MID, w, kv_mode="last_loop", max_loops=4, max_seqs=1, max_model_len=512, max_tokens=256)
+    m.set_loops(4)
+    prompt = synth.prompt_tokens(synth.MID, 200)
+    out = []
+    for reuse in (False, True):
+        _, ids = m.prefill(0, prompt, 1)
+        out.append(m.spec_decode(0, int(ids[0].item()), 24, gamma=4, k_draft=1, k_verify=4, reuse=reuse)[:24])
+        m.release(0)
+    agree = int(np.argmin(np.append(out[0] == out[1], False)))
+    say(f"[mid bf16] self-speculative with / without reuse: first {agree} of 24 ids agree")
+    np.testing.assert_array_equal(out[0], out[1])
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
 def test_mid_bf16_batched_decode(mode):
     """Serving-style batched decode: 6 sequences with ragged prompt lengths decode together
     (one call per step, rows = sequences); every sequence against its own oracle run,
