@@ -258,6 +258,8 @@ struct dory_ctx {
   int stage_cur = 0;
   size_t stage_bytes = 0;
   std::vector<int32_t> upl;  // host image of the upload
+  // the running call: a chunk of consecutive positions of one sequence (prefill, resume), or -1
+  int chunk_seq = -1, chunk_pos0 = -1;
   // last call
   int last_rows = 0;
   float* last_h = nullptr;
@@ -522,7 +524,7 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   if (!fused_decode) {
     Span sp(c, R_ROPE, Md * nq * 4 + Md * (hd + 2.0 * Hk * dh) * es, 0);
     ok(c, launch_rope_qk_kv(dt, qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), c->W(c->L.q), kv, M, H,
-                            Hk, dh, c->page_el, st));
+                            Hk, dh, c->page_el, decode ? -1 : c->chunk_seq, decode ? -1 : c->chunk_pos0, st));
   }
   {
     // fused decode reads q/k/v from the projection output and writes the new key/value itself
@@ -786,7 +788,10 @@ dory_status prefill_impl(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, in
   s.append_run(s.len, k_run);
   Geom geo;
   geo.add_chunk(len, n, c->cfg.window);
+  c->chunk_seq = sid;
+  c->chunk_pos0 = len;
   run_forward(c, tokens_dev, n, false, geo, o);
+  c->chunk_seq = c->chunk_pos0 = -1;
   if (!head) lm_head(c, n, logits_rows, logits_dev, ids_dev);
   c->stats.calls++;
   if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
@@ -876,7 +881,10 @@ dory_status resume_impl(dory_ctx* c, int32_t sid, int32_t n, const float* res_x,
   o.phase = FwdOpts::RESUME;
   o.res_x = res_x;
   o.res_s1 = res_s1;
+  c->chunk_seq = sid;
+  c->chunk_pos0 = pos0;
   run_forward(c, nullptr, n, false, geo, o);
+  c->chunk_seq = c->chunk_pos0 = -1;
   lm_head(c, n, n, logits_dev, ids_dev);
   c->stats.calls++;
   if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));

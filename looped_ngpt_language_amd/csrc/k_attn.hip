@@ -71,6 +71,73 @@ __global__ void __launch_bounds__(64) k_rope_qk_kv(const float* __restrict__ qkv
   }
 }
 
+// RoPE + per-head L2 norm + KV write for a chunk of consecutive positions pos0 .. pos0+M-1 of
+// one sequence (bf16, d_h = 128), one workgroup per (16-token page, KV head): the G query heads,
+// the key head and the value head of the group's rows are processed one wave per (row, head), 16
+// waves, so that each wave has few dependent load round trips;
+// the page's key block [16][128] and value block V^T [128][16] (token t at column vperm(t)) are
+// assembled in LDS and written as whole 4 KB blocks (only the chunk's own rows / columns on the
+// partial pages at either end of the chunk, whose other tokens belong to earlier calls).
+__global__ void __launch_bounds__(1024) k_rope_page(const float* __restrict__ qkv, int seq, int pos0, int M,
+                                                   const int32_t* __restrict__ ptab, int max_pages,
+                                                   const float2* __restrict__ rope, bf16_t* __restrict__ q_out,
+                                                   bf16_t* __restrict__ kv_slot, int H, int Hkv,
+                                                   size_t page_elems) {
+  constexpr int DH = 128;
+  __shared__ __attribute__((aligned(16))) bf16_t kt[16][DH];
+  __shared__ __attribute__((aligned(16))) bf16_t vt[DH][16];
+  const int g = blockIdx.y, G = H / Hkv;
+  const int pg = pos0 / 16 + blockIdx.x;            // page of the sequence
+  const int r0 = pg * 16 - pos0;                     // chunk row of the page's token 0 (may be < 0)
+  const int i_lo = max(0, -r0), i_hi = min(16, M - r0);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nq = (H + 2 * Hkv) * DH;
+  const int units = 16 * (G + 2);
+  for (int u = w; u < units; u += 16) {
+    const int i = u / (G + 2), hu = u % (G + 2);
+    if (i < i_lo || i >= i_hi) continue;
+    const int r = r0 + i, pos = pos0 + r;
+    const float* src = qkv + (size_t)r * nq;
+    if (hu == G + 1) {                               // value: no rotation, no norm
+      const float* v = src + (size_t)(H + Hkv + g) * DH;
+      vt[lane][vperm(i)] = f32_to_bf16(v[lane]);
+      vt[lane + 64][vperm(i)] = f32_to_bf16(v[lane + 64]);
+      continue;
+    }
+    const int head = hu < G ? g * G + hu : H + g;    // query head, or the key head
+    const float* x = src + (size_t)head * DH;
+    const float x1 = x[lane], x2 = x[lane + 64];
+    const float2 cs = rope[(size_t)pos * 64 + lane];
+    const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
+    const float rn = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    if (hu < G) {
+      bf16_t* q = q_out + ((size_t)r * H + head) * DH;
+      q[lane] = f32_to_bf16(a0 * rn);
+      q[lane + 64] = f32_to_bf16(a1 * rn);
+    } else {
+      kt[i][lane] = f32_to_bf16(a0 * rn);
+      kt[i][lane + 64] = f32_to_bf16(a1 * rn);
+    }
+  }
+  __syncthreads();
+  const int page = ptab[(size_t)seq * max_pages + pg];
+  bf16_t* kp = kv_slot + (size_t)page * page_elems + (size_t)g * 16 * DH;
+  bf16_t* vp = kv_slot + (size_t)page * page_elems + (size_t)Hkv * 16 * DH + (size_t)g * DH * 16;
+  const int t = threadIdx.x;
+  if (i_lo == 0 && i_hi == 16) {                    // whole page: 256 lanes x 16 bytes per block
+    if (t < 256) reinterpret_cast<uint4*>(kp)[t] = reinterpret_cast<const uint4*>(&kt[0][0])[t];
+    else if (t < 512) reinterpret_cast<uint4*>(vp)[t - 256] = reinterpret_cast<const uint4*>(&vt[0][0])[t - 256];
+  } else {
+    for (int e = t; e < 16 * DH; e += 1024) {
+      const int i = e / DH, d = e % DH;              // key element (token i, dim d)
+      if (i >= i_lo && i < i_hi) kp[e] = kt[i][d];
+      const int dv = e / 16, c = e % 16;             // value element (dim dv, column c)
+      const int iv = vperm(c);                       // vperm is its own inverse
+      if (iv >= i_lo && iv < i_hi) vp[e] = vt[dv][c];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- generic row attention
 
 constexpr int ATT_THREADS = 256;
@@ -881,7 +948,13 @@ __global__ void __launch_bounds__(256 * KSPLIT) k_attn_prefill(const bf16_t* __r
 
 hipError_t launch_rope_qk_kv(int dtype, const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                              const float2* rope, void* q_out, void* kv_slot, int M, int H, int Hkv, int dh,
-                             size_t page_elems, hipStream_t st) {
+                             size_t page_elems, int seq, int pos0, hipStream_t st) {
+  if (dtype != 0 && dh == 128 && seq >= 0 && pos0 >= 0) {
+    const int tiles = (pos0 + M - 1) / 16 - pos0 / 16 + 1;
+    DORY_LAUNCH(k_rope_page, dim3(tiles, Hkv), dim3(1024), 0, st, qkv, seq, pos0, M, ptab, max_pages, rope,
+                (bf16_t*)q_out, (bf16_t*)kv_slot, H, Hkv, page_elems);
+    return hipGetLastError();
+  }
   dim3 grid(M, H + Hkv);
   if (dtype == 0)
     DORY_LAUNCH(k_rope_qk_kv<float>, grid, dim3(64), 0, st, qkv, rows, ptab, max_pages, rope,

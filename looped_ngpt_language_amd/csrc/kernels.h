@@ -44,9 +44,11 @@ hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, hipSt
 hipError_t launch_rope_table(float2* tab, int max_len, int dh, double theta, hipStream_t st);
 hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t st);
 
+// RoPE + per-head q/k norm + KV write of M rows. seq, pos0 >= 0: the rows are the consecutive
+// positions pos0 .. pos0+M-1 of sequence seq (a prefill chunk; page-tiled kernel for bf16 d_h 128).
 hipError_t launch_rope_qk_kv(int dtype, const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                              const float2* rope, void* q_out, void* kv_slot, int M, int H, int Hkv, int dh,
-                             size_t page_elems, hipStream_t st);
+                             size_t page_elems, int seq, int pos0, hipStream_t st);
 hipError_t launch_attn_rows(int dtype, const void* q, const int32_t* rows, const int32_t* ptab, int max_pages,
                             const void* kv, size_t page_elems, int M, int H, int Hkv, int dh, int window,
                             float scale, int splits, void* out, float* part_ml, float* part_o, hipStream_t st);
