@@ -127,10 +127,14 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
   constexpr int WAVES = WM * WN, MS = 16;
   constexpr int TM = BM / (MS * WM), TN = BN / (MS * WN);
   constexpr int IA = BM / (8 * WAVES), IB = BN / (8 * WAVES);  // 1 KB loads per wave per k-tile
-  constexpr int PER_TILE = IA + IB;
-  static_assert(TM >= 1 && TN >= 1 && IA * 8 * WAVES == BM && IB * 8 * WAVES == BN && (!DUAL || TN % 2 == 0),
-                "tile shape");
-  static_assert(S >= 2 && (S - 2) * PER_TILE <= 63, "stages");
+  // EVEN: every wave loads IA blocks of A and IB of B. Otherwise the (BM + BN) / 8 blocks of a
+  // k-tile are dealt round-robin over the waves (NL per wave at most, the last round partial);
+  // the per-wave load counts then differ, so only two stages (whose waits are for zero) are allowed.
+  constexpr bool EVEN = IA * 8 * WAVES == BM && IB * 8 * WAVES == BN;
+  constexpr int NB = (BM + BN) / 8, NL = (NB + WAVES - 1) / WAVES;
+  constexpr int PER_TILE = EVEN ? IA + IB : NL;
+  static_assert(TM >= 1 && TN >= 1 && BM % 8 == 0 && BN % 8 == 0 && (!DUAL || TN % 2 == 0), "tile shape");
+  static_assert(S >= 2 && (S - 2) * PER_TILE <= 63 && (EVEN || S == 2), "stages");
   __shared__ __attribute__((aligned(1024))) bf16_t As[S][BM * MF_BK];
   __shared__ __attribute__((aligned(1024))) bf16_t Bs[S][BN * MF_BK];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -148,19 +152,28 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
   // byte offset of this lane's source (row, logical chunk) for each load: lane l
   // fills physical slot l & 7 of tile row 8i + l/8, i.e. logical chunk (l & 7) ^ swz
   const int lrow = lane >> 3;
-  uint32_t offa[IA], offb[IB];
-#pragma unroll
-  for (int i = 0; i < IA; ++i) {
-    const int r = (wid * IA + i) * 8 + lrow;
-    offa[i] = ((uint32_t)min(m0 + r, M - 1) * (uint32_t)K + ((lane & 7) ^ lds_swz(r)) * 8) * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < IB; ++i) {
-    const int r = (wid * IB + i) * 8 + lrow;
+  auto a_off = [&](int r) __attribute__((always_inline)) {
+    return ((uint32_t)min(m0 + r, M - 1) * (uint32_t)K + ((lane & 7) ^ lds_swz(r)) * 8) * 2;
+  };
+  auto b_off = [&](int r) __attribute__((always_inline)) {
     int gn;
     if (DUAL) gn = (r < BN / 2) ? min(n0 + r, F - 1) : F + min(n0 + r - BN / 2, F - 1);
     else gn = min(n0 + r, N - 1);
-    offb[i] = ((uint32_t)gn * (uint32_t)K + ((lane & 7) ^ lds_swz(r)) * 8) * 2;
+    return ((uint32_t)gn * (uint32_t)K + ((lane & 7) ^ lds_swz(r)) * 8) * 2;
+  };
+  constexpr int IAE = EVEN ? IA : 1, IBE = EVEN ? IB : 1, NLE = EVEN ? 1 : NL;
+  uint32_t offa[IAE], offb[IBE], offl[NLE];
+  if constexpr (EVEN) {
+#pragma unroll
+    for (int i = 0; i < IA; ++i) offa[i] = a_off((wid * IA + i) * 8 + lrow);
+#pragma unroll
+    for (int i = 0; i < IB; ++i) offb[i] = b_off((wid * IB + i) * 8 + lrow);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int blk = min(wid + WAVES * i, NB - 1);  // blocks past NB are never issued
+      offl[i] = blk < BM / 8 ? a_off(blk * 8 + lrow) : b_off((blk - BM / 8) * 8 + lrow);
+    }
   }
   const bf16_t* const Ak = A + (size_t)blockIdx.y * k_len;
   const bf16_t* const Bk = B + (size_t)blockIdx.y * k_len;
@@ -168,10 +181,19 @@ __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __rest
   auto issue = [&](int kt, int st) __attribute__((always_inline)) {
     const bf16_t* a = Ak + kt * MF_BK;
     const bf16_t* bb = Bk + kt * MF_BK;
+    if constexpr (EVEN) {
 #pragma unroll
-    for (int i = 0; i < IA; ++i) lds_dma16(a, offa[i], lds_a + st * (BM * MF_BK * 2) + (wid * IA + i) * 1024);
+      for (int i = 0; i < IA; ++i) lds_dma16(a, offa[i], lds_a + st * (BM * MF_BK * 2) + (wid * IA + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < IB; ++i) lds_dma16(bb, offb[i], lds_b + st * (BN * MF_BK * 2) + (wid * IB + i) * 1024);
+      for (int i = 0; i < IB; ++i) lds_dma16(bb, offb[i], lds_b + st * (BN * MF_BK * 2) + (wid * IB + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int blk = wid + WAVES * i;  // wave-uniform
+        if (blk < BM / 8) lds_dma16(a, offl[i], lds_a + st * (BM * MF_BK * 2) + blk * 1024);
+        else if (blk < NB) lds_dma16(bb, offl[i], lds_b + st * (BN * MF_BK * 2) + (blk - BM / 8) * 1024);
+      }
+    }
   };
 
   f32x4_t acc[TM][TN];
@@ -304,8 +326,8 @@ static hipError_t tile_launch(const bf16_t* A, const bf16_t* B, void* out, int M
 // Tile shape: the candidate with the least estimated time, taken as the tiles
 // of the busiest CU (tiles dealt evenly over 256 CUs) times the tile's area over
 // its measured per-CU rate (area per unit time at equal K on the ~4B prefill
-// projections: 256x256 on gate/up, 256x192 on qkv, 128x192 on o and down,
-// 256x128 and 128x128 on the same shapes; 256x128 over several rounds, where
+// projections: 256x256 on gate/up, 256x192 and 256x160 on qkv, 128x192 on o and
+// down, 256x128 and 128x128 on the same shapes; 256x128 over several rounds, where
 // its activation re-reads cost most: 2560-token gate/up fetched 1.46 GB per
 // launch from beyond L2 against 0.30 GB for 256x256). Shapes that split N into about 256
 // tiles (one per CU) avoid the half-empty last round a larger tile leaves.
@@ -314,7 +336,7 @@ static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, 
   const int ncols = dual ? F : N;
   struct Cand { int bm, bn, tn; double rate; };  // tn: MFMA column tiles per wave (dual needs an even count)
   static const Cand cands[] = {{256, 256, 8, 4.0}, {256, 192, 6, 3.69}, {128, 192, 6, 3.15},
-                               {256, 128, 4, 3.0}, {128, 128, 4, 2.87}};
+                               {256, 128, 4, 3.0}, {128, 128, 4, 2.87}, {256, 160, 5, 3.4}};
   int best = 0;
   double best_t = 1e300;
   for (int i = 0; i < (int)(sizeof(cands) / sizeof(cands[0])); ++i) {
@@ -330,6 +352,7 @@ static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, 
     case 1: return tile_launch<256, 192, 4, 2>(A, B, out, M, N, K, F, dual, st);
     case 2: return tile_launch<128, 192, 4, 2, 3>(A, B, out, M, N, K, F, dual, st);
     case 3: return tile_launch<256, 128, 4, 2>(A, B, out, M, N, K, F, dual, st);
+    case 5: return tile_launch<256, 160, 4, 2>(A, B, out, M, N, K, F, dual, st);
     default: return tile_launch<128, 128, 2, 2>(A, B, out, M, N, K, F, dual, st);
   }
 }
