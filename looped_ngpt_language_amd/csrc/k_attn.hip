@@ -772,6 +772,12 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
   float mrun = FIXED ? scale : -INFINITY, lrun = 0.f;
   // score -> exp2 argument: s * scale * log2(e) - offset * log2(e)
   const float k2 = scale * LOG2E;
+  // this lane's LDS element offsets: K row qi (+ 32 t rows), chunk 2 ks + hh swizzled by the key;
+  // V^T row qi (+ page and dim-tile rows), half hh swizzled by the dim
+  int koff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * DH + (((2 * ks + hh) ^ (qi & 15)) << 3);
+  const int voff = qi * 16 + ((hh ^ ((qi >> 3) & 1)) << 3);
 
   // this wave's share of its key group's 64-key block: four 1 KB pieces of K and of V^T
   const int kkey_lo = lane >> 4;                 // key within a 4-key quarter
@@ -821,56 +827,65 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
         f32x16_t st;
 #pragma unroll
         for (int v = 0; v < 16; ++v) st[v] = 0.f;
-        const int key = 32 * t + qi;             // A operand row: key of the block
+        // A operand row: key 32 t + qi of the block
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          const int ch = (2 * ks + hh) ^ (key & 15);
-          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks_ + key * DH + ch * 8);
+          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks_ + 32 * t * DH + koff[ks]);
           st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], st, 0, 0, 0);
         }
-        // keys of this half-block that some query of the wave must not see
+        // keys of this half-block that some query of the wave must not see (wave-uniform)
         const bool edge = k0 + 31 > pos_first || (window > 0 && k0 <= pos_last - window);
-        float sv[16];
-        float mb = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kp = k0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          const bool ok = !edge || (kp <= qpos && (window <= 0 || kp > qpos - window));
-          sv[v] = ok ? st[v] : -INFINITY;
-          if (!FIXED) mb = fmaxf(mb, sv[v]);
-        }
-        float c = 1.f;
-        if (!FIXED) {
-          mb = fmaxf(mb * scale, __shfl_xor(mb * scale, 32, 64));
-          const float mn = fmaxf(mrun, mb);
-          c = safe_scale(mrun, mn);
-          mrun = mn;
-        }
-        const float off = mrun * LOG2E;
-        float psum = 0.f;
         bf16x8_t pb[2];
+        if (FIXED && !edge) {
+          // every score is visible: no mask, and the row sums stay lane-local until the end
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = sv[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] * k2 - off);
-          psum += p;
-          pb[v >> 3][v & 7] = (__bf16)p;
-        }
-        psum += __shfl_xor(psum, 32, 64);
-        lrun = lrun * c + psum;
-        if (!FIXED) {
+          for (int v = 0; v < 16; ++v) {
+            const float p = __builtin_amdgcn_exp2f(st[v] * k2 - k2);
+            lrun += p;
+            pb[v >> 3][v & 7] = (__bf16)p;
+          }
+        } else {
+          float sv[16];
+          float mb = -INFINITY;
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
+          for (int v = 0; v < 16; ++v) {
+            const int kp = k0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+            const bool ok = !edge || (kp <= qpos && (window <= 0 || kp > qpos - window));
+            sv[v] = ok ? st[v] : -INFINITY;
+            if (!FIXED) mb = fmaxf(mb, sv[v]);
+          }
+          float c = 1.f;
+          if (!FIXED) {
+            mb = fmaxf(mb * scale, __shfl_xor(mb * scale, 32, 64));
+            const float mn = fmaxf(mrun, mb);
+            c = safe_scale(mrun, mn);
+            mrun = mn;
+          }
+          const float off = mrun * LOG2E;
+          float psum = 0.f;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[dt][v] *= c;
+          for (int v = 0; v < 16; ++v) {
+            const float p = sv[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] * k2 - off);
+            psum += p;
+            pb[v >> 3][v & 7] = (__bf16)p;
+          }
+          if (FIXED) {
+            lrun += psum;
+          } else {
+            psum += __shfl_xor(psum, 32, 64);
+            lrun = lrun * c + psum;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[dt][v] *= c;
+          }
         }
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int page = 2 * t + pp;
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const int dim = dt * 32 + qi;
-            const int half = hh ^ ((dim >> 3) & 1);
-            const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vs_ + (page * DH + dim) * 16 + half * 8);
+            const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vs_ + (page * DH + dt * 32) * 16 + voff);
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[pp], acc[dt], 0, 0, 0);
           }
         }
@@ -884,6 +899,7 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
   }
 #undef DORY_KV_GLOAD
 #undef DORY_KV_SWRITE
+  if (FIXED) lrun += __shfl_xor(lrun, 32, 64);  // the two halves of a query's keys
   if constexpr (KSPLIT == 2) {
     // key group 1 hands (max, sum, output) to key group 0 through the (now idle) LDS:
     // the 64 output floats per lane fill the K buffers exactly (4 waves x 64 lanes,
