@@ -93,3 +93,16 @@ DORY_DEV float silu(float z) { return z / (1.f + __expf(-z)); }
 // The smallest positive normal float: lower bound of a sum of squares before
 // the reciprocal square root, so a zero vector yields zeros instead of NaN.
 #define DORY_TINY_SS 1.17549435e-38f
+
+// s_waitcnt immediate for vmcnt(n) (gfx9 encoding), other counters left free
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// One 16-byte-per-lane load from gbase + voff (bytes) straight into LDS at lds_byte + 16 lane
+// (global_load_lds_dwordx4; M0 holds the wave's LDS base). Issued from inline assembly so that
+// the compiler, which cannot tell LDS stages apart, does not wait for it before unrelated LDS
+// reads; the caller waits with s_waitcnt vmcnt before the barrier that publishes the data.
+DORY_DEV void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}

@@ -779,43 +779,40 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
   for (int ks = 0; ks < 8; ++ks) koff[ks] = qi * DH + (((2 * ks + hh) ^ (qi & 15)) << 3);
   const int voff = qi * 16 + ((hh ^ ((qi >> 3) & 1)) << 3);
 
-  // this wave's share of its key group's 64-key block: four 1 KB pieces of K and of V^T
-  const int kkey_lo = lane >> 4;                 // key within a 4-key quarter
-  const int kslot = lane & 15;
-  const int vdim_lo = lane >> 1;                 // dim within a 32-dim quarter
-  const int vslot = lane & 1;
-  u32x4_t rk[4], rv[4];
-#define DORY_KV_GLOAD(STEP0)                                                                                  \
-  do {                                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                           \
-      const int ci = wq * 4 + i, pi = ci >> 2, qt = ci & 3;                                                   \
-      const int pidx = min(((STEP0) + kg * KB >> 4) + pi, last_page);                                         \
-      const bf16_t* pg = kv_slot + (size_t)prow[pidx] * page_elems;                                           \
-      const int key = qt * 4 + kkey_lo;                                                                       \
-      rk[i] = *reinterpret_cast<const u32x4_t*>(pg + ((size_t)g * 16 + key) * DH + (kslot ^ (key & 15)) * 8); \
-      const int dim = qt * 32 + vdim_lo;                                                                      \
-      rv[i] = *reinterpret_cast<const u32x4_t*>(pg + (size_t)Hkv * 16 * DH + ((size_t)g * DH + dim) * 16 +    \
-                                                (vslot ^ ((dim >> 3) & 1)) * 8);                              \
-    }                                                                                                         \
-  } while (0)
-#define DORY_KV_SWRITE(S)                                                                                     \
-  do {                                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                           \
-      const int ci = wq * 4 + i, pi = ci >> 2, qt = ci & 3;                                                   \
-      *reinterpret_cast<u32x4_t*>(&Ks[S][kg][(pi * 16 + qt * 4) * DH + lane * 8]) = rk[i];                    \
-      *reinterpret_cast<u32x4_t*>(&Vs[S][kg][(pi * DH + qt * 32) * 16 + lane * 8]) = rv[i];                   \
-    }                                                                                                         \
-  } while (0)
+  // this wave's share of its key group's 64-key block: the 4 KB K block and the 4 KB V^T block
+  // of page wq (four 1 KB pieces each), loaded straight into LDS, 16 bytes per lane, lane l
+  // filling bytes 16 l of a piece; the source is the chunk that belongs in that LDS slot
+  const int wqu = __builtin_amdgcn_readfirstlane(wq), kgu = __builtin_amdgcn_readfirstlane(kg);
+  uint32_t kofs[4], vofs[4];  // byte offsets within a page
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const int key = qt * 4 + (lane >> 4), dim = qt * 32 + (lane >> 1);
+    kofs[qt] = (uint32_t)((((size_t)g * 16 + key) * DH + (((lane & 15) ^ (key & 15)) << 3)) * 2);
+    vofs[qt] = (uint32_t)(((size_t)Hkv * 16 * DH + ((size_t)g * DH + dim) * 16 + (((lane & 1) ^ ((dim >> 3) & 1)) << 3)) * 2);
+  }
+  const uint32_t lds_k = (uint32_t)(size_t)&Ks[0][kgu][wqu * 16 * DH];
+  const uint32_t lds_v = (uint32_t)(size_t)&Vs[0][kgu][wqu * DH * 16];
+  constexpr uint32_t kStageBytes = KSPLIT * PF_KB * 128 * 2;
+  auto kv_dma = [&](int step0, int st_) __attribute__((always_inline)) {
+    const int pidx = min(((step0 + kgu * KB) >> 4) + wqu, last_page);
+    const bf16_t* pg = kv_slot + (size_t)prow[pidx] * page_elems;
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      lds_dma16(pg, kofs[qt], lds_k + st_ * kStageBytes + qt * 4 * DH * 2);
+      lds_dma16(pg, vofs[qt], lds_v + st_ * kStageBytes + qt * 32 * 16 * 2);
+    }
+  };
 
   const int klo = window > 0 ? max(0, wg_first - window + 1) : 0;
   const int wlo = window > 0 ? max(0, pos_first - window + 1) : 0;
   const int kstart = klo & ~(KB - 1);
-  DORY_KV_GLOAD(kstart);
-  DORY_KV_SWRITE(0);
-  if (kstart + STEP <= wg_last) DORY_KV_GLOAD(kstart + STEP);
+  kv_dma(kstart, 0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   int stage = 0;
   for (int kstep = kstart; kstep <= wg_last; kstep += STEP, stage ^= 1) {
+    // the other stage was last read before the barrier that ended the previous step
+    if (kstep + STEP <= wg_last) kv_dma(kstep + STEP, stage ^ 1);
     const int kb = kstep + kg * KB;              // this key group's 64-key block
     if (nrow > 0 && kb <= pos_last && kb + KB > wlo) {
       const bf16_t* ks_ = Ks[stage][kg];
@@ -891,14 +888,9 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
         }
       }
     }
-    if (kstep + STEP <= wg_last) {
-      DORY_KV_SWRITE(stage ^ 1);  // every wave finished reading that buffer before the last barrier
-      if (kstep + 2 * STEP <= wg_last) DORY_KV_GLOAD(kstep + 2 * STEP);
-    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the next block has landed before the barrier publishes it
     __syncthreads();
   }
-#undef DORY_KV_GLOAD
-#undef DORY_KV_SWRITE
   if (FIXED) lrun += __shfl_xor(lrun, 32, 64);  // the two halves of a query's keys
   if constexpr (KSPLIT == 2) {
     // key group 1 hands (max, sum, output) to key group 0 through the (now idle) LDS:

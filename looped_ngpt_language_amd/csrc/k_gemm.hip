@@ -110,15 +110,6 @@ constexpr int MF_BK = 64;
 // Byte offsets are 32-bit: the host refuses operands of 4 GiB or more.
 DORY_DEV int lds_swz(int r) { return (r >> 1) & 7; }
 
-// s_waitcnt immediate for vmcnt(n) (gfx9 encoding), other counters left free
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// One 16-byte-per-lane load from gbase + voff (bytes) into LDS at lds_byte + 16 lane.
-DORY_DEV void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_byte) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(voff), "s"(gbase)
-               : "memory", "m0");
-}
 
 template <int BM, int BN, int WM, int WN, bool DUAL, int S>
 __global__ void __launch_bounds__(64 * WM * WN) k_gemm_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
