@@ -742,8 +742,8 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
                              bf16_t (*Vs)[KSPLIT][PF_KB * 128]) {
   constexpr int DH = 128, KB = PF_KB, STEP = KB * KSPLIT;
   constexpr float LOG2E = 1.4426950408889634f;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int wq = wv & 3, kg = wv >> 2;             // query group, key group
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wq = wv & 3, kg = wv >> 2;             // query group, key group (wave-uniform)
   const int hq = blockIdx.y, g = hq / (H / Hkv);
   const int row0 = wrow0 + wq * 32;
   const int nrow = max(0, min(32, M - row0));
@@ -782,7 +782,7 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
   // this wave's share of its key group's 64-key block: the 4 KB K block and the 4 KB V^T block
   // of page wq (four 1 KB pieces each), loaded straight into LDS, 16 bytes per lane, lane l
   // filling bytes 16 l of a piece; the source is the chunk that belongs in that LDS slot
-  const int wqu = __builtin_amdgcn_readfirstlane(wq), kgu = __builtin_amdgcn_readfirstlane(kg);
+  const int wqu = wq, kgu = kg;
   uint32_t kofs[4], vofs[4];  // byte offsets within a page
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) {
@@ -814,7 +814,45 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
     // the other stage was last read before the barrier that ended the previous step
     if (kstep + STEP <= wg_last) kv_dma(kstep + STEP, stage ^ 1);
     const int kb = kstep + kg * KB;              // this key group's 64-key block
-    if (nrow > 0 && kb <= pos_last && kb + KB > wlo) {
+    // every key of the block visible to every query of the wave (fixed offset only)
+    const bool whole = FIXED && nrow > 0 && kb + KB - 1 <= pos_first && (window <= 0 || kb > pos_last - window);
+    if (whole) {
+      // both 32-key halves in one straight run, so the second half's score MFMAs can overlap
+      // the first half's exponentials and the first half's P.V MFMAs the second's
+      const bf16_t* ks_ = Ks[stage][kg];
+      const bf16_t* vs_ = Vs[stage][kg];
+      f32x16_t st0, st1;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st0[v] = st1[v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(ks_ + koff[ks]), qb[ks],
+                                                      st0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8_t*>(ks_ + 32 * DH + koff[ks]), qb[ks], st1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = __builtin_amdgcn_exp2f((t ? st1[v] : st0[v]) * k2 - k2);
+          lrun += p;
+          pb[v >> 3][v & 7] = (__bf16)p;
+        }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const bf16x8_t va =
+                *reinterpret_cast<const bf16x8_t*>(vs_ + ((2 * t + pp) * DH + dt * 32) * 16 + voff);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[pp], acc[dt], 0, 0, 0);
+          }
+      }
+    } else if (nrow > 0 && kb <= pos_last && kb + KB > wlo) {
       const bf16_t* ks_ = Ks[stage][kg];
       const bf16_t* vs_ = Vs[stage][kg];
 #pragma unroll
