@@ -383,12 +383,29 @@ def bench_batched(m1, shape, args, ev):
         step_bytes = sum(v["bytes"] for v in tim.values()) / steps
         gbs = step_bytes / (ms * 1e-3) / 1e9
         kvb = mb.kv_bytes_in_use()
+        # instrumented pass: a few more steps with an event pair around every launch
+        n_inst = 4
+        mb.set_timing(True)
+        for i in range(n_inst):
+            mb.decode(sids, cur, logits=None, out_ids=nxt[i % 2])
+            cur = nxt[i % 2]
+        inst = mb.timing(reset=True)
+        mb.set_timing(False)
+        roles = {}
+        for name, v in inst.items():
+            if v["timed_launches"]:
+                avg_ms = v["ms"] / v["timed_launches"]
+                per_launch = v["bytes"] / v["launches"]
+                roles[name] = {"avg_us": round(1e3 * avg_ms, 2), "ms_per_step": round(v["ms"] / n_inst, 3),
+                               "GBs": round(per_launch / (avg_ms * 1e-3) / 1e9, 1)}
         out[mode] = {"tok_s": round(n_seq * 1e3 / ms, 1), "ms_per_step": round(ms, 3),
                      "GB_per_step": round(step_bytes / 1e9, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "kv_bytes_in_use": kvb, "prefill_s": round(t_pf, 1)}
+                     "kv_bytes_in_use": kvb, "prefill_s": round(t_pf, 1), "kernels": roles}
         log(f"[bench] decode bs{n_seq} k={k} {mode}: {ms:.2f} ms/step  {n_seq * 1e3 / ms:,.0f} tok/s  "
             f"{step_bytes / 1e9:.1f} GB/step -> {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak); "
             f"KV in use {kvb / 1e9:.1f} GB; prefill of {int(sum(lens))} tokens took {t_pf:.1f} s")
+        for name, r in sorted(roles.items(), key=lambda x: -x[1]["ms_per_step"]):
+            log(f"         {name:22s} avg {r['avg_us']:9.2f} us  {r['ms_per_step']:7.3f} ms/step  {r['GBs']:7.0f} GB/s")
         for s_ in sids:
             mb.release(s_)
     mb.close()

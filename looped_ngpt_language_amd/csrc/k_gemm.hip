@@ -383,8 +383,14 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {
       const int mt = (M + 127) / 128, nt = (N + 127) / 128;
-      DORY_LAUNCH((k_gemm_tile<128, 128, 2, 4, false, 2>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
-                  (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
+      // a long K range per workgroup streams its weights through a 4-stage ring (3 k-tiles in
+      // flight, one workgroup per CU); short ranges keep 2 stages, so two workgroups share a CU
+      if (K / S / MF_BK >= 16)
+        DORY_LAUNCH((k_gemm_tile<128, 128, 2, 4, false, 4>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
+                    (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
+      else
+        DORY_LAUNCH((k_gemm_tile<128, 128, 2, 4, false, 2>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
+                    (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
       const size_t outs = (size_t)M * (dual ? F : N);
       if (dual)
         DORY_LAUNCH(k_splitk_reduce<true>, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st,
