@@ -8,6 +8,7 @@ Bars (written in each test):
     oracle margin between the two ids is below twice the step's max logit error (near-ties,
     counted and reported).
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -248,19 +249,31 @@ def test_mid_bf16_self_speculative_reuse_matches_plain():
     np.testing.assert_array_equal(out[0], out[1])
 
 
-@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
-def test_mid_bf16_batched_decode(mode):
-    """Serving-style batched decode: 6 sequences with ragged prompt lengths decode together
+# bf16 with 128-wide heads (the batched split-attention kernels need them) but narrow and
+# shallow, so the oracle runs 20 sequences of ~300 tokens in seconds; the window sits
+# inside the prompts
+NARROW = dataclasses.replace(synth.MID, d_model=256, n_heads=2, n_kv_heads=1, d_ff=512, vocab=2048, n_in=2, n_rec=4,
+                             n_out=2, window=192)
+
+
+@pytest.mark.parametrize("shape_name,mode,n_seq,min_len,max_len",
+                         [("mid", "per_loop", 6, 17, 300), ("mid", "last_loop", 6, 17, 300),
+                          ("narrow", "last_loop", 20, 257, 360), ("narrow", "per_loop", 20, 257, 360)])
+def test_bf16_batched_decode(shape_name, mode, n_seq, min_len, max_len):
+    """Serving-style batched decode: sequences with ragged prompt lengths decode together
     (one call per step, rows = sequences); every sequence against its own oracle run,
-    teacher-forced. Exercises the split-K small-M GEMM and multi-row split attention."""
-    w = synth.make_weights(synth.MID, seed=0)
-    m = dory.Model(synth.MID, w, kv_mode=mode, max_loops=2, max_seqs=6, max_model_len=512, max_tokens=512)
+    teacher-forced. Exercises the split-K small-M GEMM and multi-row split attention (the
+    MFMA kernel up to 16 rows, the VALU kernel above; prompts over 256 tokens give it two
+    key splits per row)."""
+    shape = synth.MID if shape_name == "mid" else NARROW
+    w = synth.make_weights(shape, seed=0)
+    m = dory.Model(shape, w, kv_mode=mode, max_loops=2, max_seqs=n_seq, max_model_len=512, max_tokens=512)
     m.set_loops(2)
-    lens = synth.batch_prompt_lengths(6, 17, 300, seed=2)
-    prompts = synth.batch_prompts(synth.MID, lens, seed=1)
-    say(f"[mid bf16] batched decode, {mode}, k=2, prompt lengths {list(lens)}")
+    lens = synth.batch_prompt_lengths(n_seq, min_len, max_len, seed=2)
+    prompts = synth.batch_prompts(shape, lens, seed=1)
+    say(f"[{shape_name} bf16] batched decode, {mode}, k=2, {n_seq} sequences, prompt lengths {list(lens)}")
     n_dec = 3
-    o_all = [oracle_greedy(synth.MID, w, mode, 2, p, n_dec) for p in prompts]
+    o_all = [oracle_greedy(shape, w, mode, 2, p, n_dec) for p in prompts]
     first = []
     for s, p in enumerate(prompts):
         lg, ids = m.prefill(s, p, 1)
@@ -268,14 +281,14 @@ def test_mid_bf16_batched_decode(mode):
     g_lg = [[f[0]] for f in first]
     g_ids = [[f[1]] for f in first]
     for step in range(n_dec):
-        toks = torch.tensor([int(o_all[s][0][step]) for s in range(6)], dtype=torch.int32, device=m.device)
-        lg, ids = m.decode(list(range(6)), toks)
+        toks = torch.tensor([int(o_all[s][0][step]) for s in range(n_seq)], dtype=torch.int32, device=m.device)
+        lg, ids = m.decode(list(range(n_seq)), toks)
         lg = lg.cpu().numpy()
         ids = ids.cpu().numpy()
-        for s in range(6):
+        for s in range(n_seq):
             g_lg[s].append(lg[s])
             g_ids[s].append(int(ids[s]))
-    for s in range(6):
+    for s in range(n_seq):
         o_ids, o_lg, _ = o_all[s]
         err = float(np.max(np.abs(np.array(g_lg[s]) - o_lg)))
         agree = int(np.sum(np.array(g_ids[s]) == o_ids))
