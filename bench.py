@@ -458,6 +458,22 @@ def bench_long(m1, shape, args, ev):
     gbs = step_bytes / (dec_ms * 1e-3) / 1e9
     log(f"[bench] long decode ctx {T} k={k}: {dec_ms:.2f} ms/step  {1e3 / dec_ms:.1f} tok/s  "
         f"{step_bytes / 1e9:.1f} GB/step -> {gbs:.0f} GB/s")
+    # instrumented pass: a few more steps with an event pair around every launch
+    n_inst = 4
+    mb.set_timing(True)
+    for i in range(n_inst):
+        mb.decode([0], cur, logits=None, out_ids=nxt[i % 2])
+        cur = nxt[i % 2]
+    inst = mb.timing(reset=True)
+    mb.set_timing(False)
+    long_roles = {}
+    for name, v in sorted(inst.items(), key=lambda x: -x[1]["ms"]):
+        if v["timed_launches"]:
+            avg_ms = v["ms"] / v["timed_launches"]
+            long_roles[name] = {"avg_us": round(1e3 * avg_ms, 2), "ms_per_step": round(v["ms"] / n_inst, 3),
+                                "GBs": round(v["bytes"] / v["launches"] / (avg_ms * 1e-3) / 1e9, 1)}
+            log(f"         {name:22s} avg {1e3 * avg_ms:9.2f} us  {v['ms'] / n_inst:7.3f} ms/step  "
+                f"{long_roles[name]['GBs']:7.0f} GB/s")
     kv_decode = mb.kv_bytes_in_use()
     log(f"[bench] KV with sliding-window page recycling: pool {mb.kv_bytes / 1e9:.2f} GB (without: "
         f"{plain_bytes / 1e9:.2f} GB); in use {kv_after_prefill / 1e9:.2f} GB after the prompt, "
@@ -480,7 +496,7 @@ def bench_long(m1, shape, args, ev):
     mb.close()
     return {"prompt_tokens": T, "loops": k, "prefill_s": round(pf_ms / 1e3, 3),
             "prefill_tok_s": round(T / (pf_ms * 1e-3), 1), "prefill_tflop_s": round(tfs, 1),
-            "prefill_mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4), "decode_tok_s": round(1e3 / dec_ms, 2),
+            "prefill_mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4), "decode_tok_s": round(1e3 / dec_ms, 2), "decode_kernels": long_roles,
             "decode_GB_per_step": round(step_bytes / 1e9, 2), "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "spec_tok_s": round(spec_tok_s, 2), "spec_speedup": round(spec_tok_s * dec_ms / 1e3, 3),
             "spec_tokens": int(len(got)), "spec_reuse_tok_s": round(spec[True][1], 2),

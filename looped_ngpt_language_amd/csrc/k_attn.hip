@@ -308,11 +308,12 @@ DORY_DEV float bf16r(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 // rows as the A operand of S^T = K . Q^T (lane l: key l%32, dims 16ks + 8(l/32)),
 // the value rows as the A operand of O^T = V^T . P^T (page pp, dim tile dt:
 // dim 32dt + l%32, tokens vperm 8(l/32) .. +8).
-#define DORY_DEC_FETCH(KF, VF, P0)                                                                            \
+// IT is the wave's block index: its two page ids sit in lane IT % 64 of pid0 / pid1.
+#define DORY_DEC_FETCH(KF, VF, IT)                                                                            \
   do {                                                                                                        \
-    const int p0_ = (P0);                                                                                     \
-    const bf16_t* pg0_ = kv_slot + (size_t)prow[p0_] * page_elems;                                            \
-    const bf16_t* pg1_ = p0_ + 1 <= sp_last ? kv_slot + (size_t)prow[p0_ + 1] * page_elems : pg0_;            \
+    const int it_ = (IT) & 63;                                                                                \
+    const bf16_t* pg0_ = kv_slot + (size_t)__builtin_amdgcn_readlane(pid0, it_) * page_elems;                 \
+    const bf16_t* pg1_ = kv_slot + (size_t)__builtin_amdgcn_readlane(pid1, it_) * page_elems;                 \
     const bf16_t* kp_ = (qi < 16 ? pg0_ : pg1_) + ((size_t)g * 16 + (qi & 15)) * DH + 8 * hh;                 \
     _Pragma("unroll") for (int ks = 0; ks < 8; ++ks) KF[ks] = *reinterpret_cast<const bf16x8_t*>(kp_ + 16 * ks); \
     _Pragma("unroll") for (int dt = 0; dt < 4; ++dt) {                                                        \
@@ -343,7 +344,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   __shared__ float wm[4][G], wl[4][G];
   __shared__ float wacc[4][G][DH];
   const int m = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = lane & 31, hh = lane >> 5;
   const int seq = rows[2 * m], pos = rows[2 * m + 1];
   const int lo = window > 0 ? max(0, pos - window + 1) : 0;
@@ -359,9 +360,21 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   const int npair = sp_last >= sp_first ? (sp_last - sp_first + 2) / 2 : 0;
   const int nw = npair > wv ? (npair - wv + 3) / 4 : 0;  // blocks of this wave: pairs wv, wv+4, ...
   bf16x8_t kA[8], vA[8], kB[8], vB[8];
+  // page ids of the wave's blocks, block it in lane it % 64 (its second page repeats the first
+  // past the split's end), read once so the block loop holds no dependent page-table load
+  int pid0 = 0, pid1 = 0;
+  auto load_pids = [&](int it0) __attribute__((always_inline)) {
+    const int itl = it0 + lane;
+    if (itl < nw) {
+      const int p0 = sp_first + 2 * (wv + 4 * itl);
+      pid0 = prow[p0];
+      pid1 = p0 + 1 <= sp_last ? prow[p0 + 1] : pid0;
+    }
+  };
+  load_pids(0);
   // the first block's operands are requested before the query prologue (the
   // writer split fetches after writing the new key/value)
-  if (!writer && nw > 0) DORY_DEC_FETCH(kA, vA, sp_first + 2 * wv);
+  if (!writer && nw > 0) DORY_DEC_FETCH(kA, vA, 0);
 
   // queries of the group: q^ = N(RoPE(q)) in bf16
   for (int gi = wv; gi < G; gi += 4) {
@@ -408,20 +421,26 @@ __global__ void __launch_bounds__(256) k_attn_decode(
     for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
 
-  if (writer && nw > 0) DORY_DEC_FETCH(kA, vA, sp_first + 2 * wv);
-  for (int it = 0; it < nw; ++it) {
-    const int p0 = sp_first + 2 * (wv + 4 * it);
-    const bool odd = it & 1;
-    if (it + 1 < nw) {
-      if (odd) DORY_DEC_FETCH(kA, vA, p0 + 8);
-      else DORY_DEC_FETCH(kB, vB, p0 + 8);
+  if (writer && nw > 0) DORY_DEC_FETCH(kA, vA, 0);
+  // block it's operands into KF / VF. Past the last block it re-reads the last one, so every path
+  // issues the same loads and the compiler's wait counts stay exact (a skipped prefetch on one
+  // path makes it wait for the other path's prefetch too). Page ids are reloaded every 64 blocks,
+  // that load awaited at once so that none of it is left in flight.
+  auto prefetch = [&](bf16x8_t (&KF)[8], bf16x8_t (&VF)[8], int it) __attribute__((always_inline)) {
+    if (it < nw && (it & 63) == 0) {
+      load_pids(it);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
+    DORY_DEC_FETCH(KF, VF, min(it, nw - 1));
+  };
+  // one 32-key block whose operands are in KB / VB: scores, online softmax, P.V
+  auto block = [&](const bf16x8_t (&KB)[8], const bf16x8_t (&VB)[8], int it) __attribute__((always_inline)) {
+    const int p0 = sp_first + 2 * (wv + 4 * it);
     f32x16_t st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(odd ? kB[ks] : kA[ks], qb[ks], st, 0, 0, 0);
+    for (int ks = 0; ks < 8; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KB[ks], qb[ks], st, 0, 0, 0);
     float sv[16];
     float mb = -INFINITY;
 #pragma unroll
@@ -449,9 +468,18 @@ __global__ void __launch_bounds__(256) k_attn_decode(
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[dt][v] *= c;
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(odd ? vB[dt] : vA[dt], pb[0], acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(odd ? vB[4 + dt] : vA[4 + dt], pb[1], acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VB[dt], pb[0], acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(VB[4 + dt], pb[1], acc[dt], 0, 0, 0);
     }
+  };
+  // two blocks per trip, so each operand buffer keeps its registers: the next block's loads are
+  // in flight while the current one is computed
+  for (int it = 0; it < nw; it += 2) {
+    prefetch(kB, vB, it + 1);
+    block(kA, vA, it);
+    if (it + 1 >= nw) break;
+    prefetch(kA, vA, it + 2);
+    block(kB, vB, it + 1);
   }
   // waves -> LDS: lanes of query qi < G hold O[qi][32dt + 8(v/4) + 4hh + v%4]
   if (qi < G) {
