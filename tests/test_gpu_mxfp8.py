@@ -126,3 +126,40 @@ def test_mid_mxfp8_two_sequence_decode_and_wide_call_stays_bf16(mid_mx):
         say(f"  2-row step: logits max-abs {err:.3e}")
         assert err <= 5e-2
         toks = [int(x) for x in oids]
+
+
+def test_4b_width_mxfp8_decode_vs_oracle():
+    """The MXFP8 GEMV instances the benchmark's ~4B decode streams (K = 3072 for qkv, o and
+    gate/up, with and without the residual prologue; K = 8192 for down) on a 3-block model of the
+    ~4B widths (d=3072, 24/8 heads, FFN 8192): 64-token prompt, 3 decode steps at k=2 against the
+    oracle computing with the same dequantised weights."""
+    shape = synth.ModelShape(d_model=3072, n_heads=24, n_kv_heads=8, head_dim=128, d_ff=8192, vocab=4096,
+                             n_in=1, n_rec=1, n_out=1, window=4096, dtype=synth.BF16)
+    w = synth.make_weights(shape, seed=4)
+    m = dory.Model(shape, w, kv_mode="last_loop", max_loops=2, max_seqs=1, max_model_len=128, max_tokens=64,
+                   gemv_weights="mxfp8")
+    m.set_loops(2)
+    prompt = synth.prompt_tokens(shape, 64)
+    say("[4B width mxfp8] 64-token prompt + 3 decode steps, k=2, last-loop")
+    om = OracleModel(shape, w, "last_loop", 2, gemv_weights="mxfp8")
+    _, oid = om.prefill(0, prompt, 1)
+    m.prefill(0, prompt, 1)
+    tok = int(oid[0])
+    errs, errs_h, g_ids, o_ids, g_lg, o_lg = [], [], [], [], [], []
+    for _ in range(3):
+        l1, i1 = m.decode([0], torch.tensor([tok], dtype=torch.int32, device=m.device))
+        ol, oi = om.decode([0], [tok])
+        g_lg.append(l1[0].cpu().numpy())
+        o_lg.append(ol[0])
+        errs.append(float(np.max(np.abs(g_lg[-1] - o_lg[-1]))))
+        errs_h.append(float(np.max(np.abs(m.last_hidden(1)[0].cpu().numpy() - om.last_hidden[0]))))
+        g_ids.append(int(i1[0].item()))
+        o_ids.append(int(oi[0]))
+        tok = int(oi[0])
+    say(f"  logits max-abs {['%.2e' % e for e in errs]}, hidden max-abs {max(errs_h):.2e}, "
+        f"ids {sum(a == b for a, b in zip(g_ids, o_ids))}/3")
+    assert max(errs) <= 5e-2 and max(errs_h) <= 3e-2
+    for i in range(3):
+        if g_ids[i] != o_ids[i]:
+            assert o_lg[i][o_ids[i]] - o_lg[i][g_ids[i]] < 2 * errs[i]
+    m.close()
