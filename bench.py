@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-batched", action="store_true")
     p.add_argument("--no-mx", action="store_true", help="skip the MXFP8-weight decode measurement")
+    p.add_argument("--no-spec", action="store_true", help="skip the self-speculative decoding measurement")
+    p.add_argument("--no-sampling", action="store_true", help="skip the top-p sampler measurement")
     p.add_argument("--no-decode", action="store_true",
                    help="prefill only (for profiling): the JSON value is then the prefill rate at --k")
     p.add_argument("--batched-steps", type=int, default=16)
@@ -217,8 +219,10 @@ def main():
         mm.close()
         del mm
 
-    res["sampling"] = bench_sampling(shape, args)
-    res["spec"] = bench_spec(m, ptoks, plog, res["decode"].get(4), args)
+    if not args.no_sampling:
+        res["sampling"] = bench_sampling(shape, args)
+    if not args.no_spec:
+        res["spec"] = bench_spec(m, ptoks, plog, res["decode"].get(4), args)
 
     if not args.no_batched:
         res["batched"] = bench_batched(m, shape, args, ev)
