@@ -60,7 +60,7 @@ Layout make_layout(const dory_config& c) {
   const size_t M = c.max_tokens, d = c.d_model, es = esize(c);
   L.max_pages = (c.max_model_len + kPage - 1) / kPage;
   const int upd_max = 2 * (c.max_tokens / kPage + 2 + c.max_seqs);  // full and sliding-window page tables
-  L.upload_ints = 2 * c.max_tokens + 2 * upd_max + 16;
+  L.upload_ints = 3 * c.max_tokens + 2 * upd_max + 16;  // rows, page-table updates, batched row order
   L.part_rows = std::min(c.max_tokens, std::max(c.max_seqs, 16));
   L.logit_rows = std::max(c.max_seqs, 8);
   size_t off = 0;
@@ -260,6 +260,7 @@ struct dory_ctx {
   std::vector<int32_t> upl;  // host image of the upload
   // the running call: a chunk of consecutive positions of one sequence (prefill, resume), or -1
   int chunk_seq = -1, chunk_pos0 = -1;
+  const int32_t* row_order = nullptr;  // device: batched decode rows, longest context first (this call only)
   // last call
   int last_rows = 0;
   float* last_h = nullptr;
@@ -406,10 +407,15 @@ bool stage_upload(dory_ctx* c, int n_ints) {
 }
 
 // Key splits per (row, KV head) for split attention: enough workgroups to fill
-// the chip with few serial steps per wave, at most kMaxSplits.
+// the chip with few serial steps per wave, at most kMaxSplits. The batched VALU kernel
+// (more than kDecodeMfmaRows rows, taken longest context first) aims at 8192 workgroups:
+// at 128 rows of 256..4096 tokens, targets of 2048 / 8192 / 16384 gave 6235 / 6600 / 6422
+// tok/s at k = 2 (shorter splits shorten the tail; more of them cost merge work).
+constexpr int kBatchedWorkTarget = 8192;
 int choose_splits(const dory_ctx* c, int M, int keys, bool paged_kernel) {
   if (M > c->L.part_rows) return 1;
-  const int by_work = (2048 + M * c->cfg.n_kv_heads - 1) / (M * c->cfg.n_kv_heads);
+  const int target = paged_kernel && M > dory::kDecodeMfmaRows ? kBatchedWorkTarget : 2048;
+  const int by_work = (target + M * c->cfg.n_kv_heads - 1) / (M * c->cfg.n_kv_heads);
   // MFMA decode kernel (few rows): one 32-key block per wave; VALU kernel: 16 pages per workgroup
   const int by_keys = !paged_kernel ? (keys + 63) / 64 : M <= dory::kDecodeMfmaRows ? (keys + 127) / 128
                                                                                     : (keys + 255) / 256;
@@ -534,7 +540,7 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
     if (paged && (decode || !flash)) {
       ok(c, launch_attn_decode(qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), kv, c->page_el, M, H, Hk,
                                win, g.attn_scale, splits, fused_decode ? 1 : 0, c->W(c->L.o), c->W<float>(c->L.part_ml),
-                               c->W<float>(c->L.part_o), st));
+                               c->W<float>(c->L.part_o), c->row_order, st));
     } else if (flash) {
       ok(c, launch_attn_prefill(c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, win,
                                 g.attn_scale, c->W(c->L.o), st));
@@ -830,6 +836,17 @@ dory_status decode_impl(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
   const size_t n_rows_ints = c->upl.size();
   for (int i = 0; i < n; ++i) take_pages(c, seq_ids[i], c->seqs[seq_ids[i]].len + 1);
   const int n_upd = (int)(c->upl.size() - n_rows_ints) / 2;
+  // batched rows: the attention kernels take them longest context first, so that the short ones
+  // fill the tail instead of a long one running alone at the end
+  const bool ordered = n > dory::kDecodeMfmaRows;
+  if (ordered) {
+    std::vector<int32_t> ord(n);
+    for (int i = 0; i < n; ++i) ord[i] = i;
+    std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) {
+      return c->seqs[seq_ids[a]].len > c->seqs[seq_ids[b]].len;
+    });
+    c->upl.insert(c->upl.end(), ord.begin(), ord.end());
+  }
   c->herr = hipSuccess;
   if (!stage_upload(c, (int)c->upl.size())) return fail(c, DORY_E_HIP, "upload failed: %s", hipGetErrorString(c->herr));
   if (!c->dry && n_upd) {
@@ -844,7 +861,9 @@ dory_status decode_impl(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
     s.len += 1;
     s.append_run(s.len, c->k);
   }
+  c->row_order = ordered ? c->W<int32_t>(c->L.upload) + n_rows_ints + 2 * n_upd : nullptr;
   run_forward(c, tokens_dev, n, true, geo, o);
+  c->row_order = nullptr;
   float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
   lm_head(c, n, n, logits, next_ids_dev);
   c->stats.calls++;

@@ -727,6 +727,195 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
   }
 }
 
+// Fixed-offset form of the VALU kernel (attention scale <= kFixedMaxScale): q^ and k^ are unit
+// vectors, so the probabilities are exp(scale (q^.k^ - 1)) with no running maximum, no rescaling
+// and a lane-local row sum. Scores are packed-bf16 dot products (v_dot2_f32_bf16) of the query
+// with the key words as loaded; each key's probability is the same for every lane and is taken
+// with readlane, rounded to bf16 in pairs (as the MFMA kernels feed P) and dotted with the
+// packed value words. Partials carry max = scale, so the wave combine and k_attn_merge apply.
+template <int G>
+__global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
+    const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
+    const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window,
+    float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
+    float* __restrict__ part_o, const int32_t* __restrict__ order) {
+  constexpr int DH = 128;
+  constexpr float LOG2E = 1.4426950408889634f;
+  __shared__ __attribute__((aligned(16))) bf16_t qh[G][DH];
+  __shared__ __attribute__((aligned(16))) bf16_t knew[DH];
+  __shared__ __attribute__((aligned(16))) bf16_t vnew[DH];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wacc[4][G][DH];
+  const int m = order ? order[blockIdx.x] : (int)blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int seq = rows[2 * m], pos = rows[2 * m + 1];
+  const int lo = window > 0 ? max(0, pos - window + 1) : 0;
+  const int nkeys = pos - lo + 1;
+  const int chunk = (((nkeys + splits - 1) / splits) + 15) & ~15;
+  const int kbeg = lo + sp * chunk;
+  const int kend = min(pos + 1, kbeg + chunk);
+  const float* src = qkv + (size_t)m * (size_t)((H + 2 * Hkv) * DH);
+  const float2 cs = rope[(size_t)pos * 64 + lane];
+
+  // queries of the group: q^ = N(RoPE(q)) in bf16
+  for (int gi = wv; gi < G; gi += 4) {
+    const float* x = src + (size_t)(g * G + gi) * DH;
+    const float x1 = x[lane], x2 = x[lane + 64];
+    const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
+    const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    qh[gi][lane] = f32_to_bf16(a0 * r);
+    qh[gi][lane + 64] = f32_to_bf16(a1 * r);
+  }
+  // the split holding the row's own position writes its key/value and keeps them in LDS: the
+  // key loop takes that key and value from LDS, not from memory
+  const bool writer = write_kv && kbeg <= pos && pos < kend;
+  const int tok = pos & 15;
+  if (writer && wv < 2) {
+    const int page = ptab[(size_t)seq * max_pages + (pos >> 4)];
+    bf16_t* pg = kv_slot + (size_t)page * page_elems;
+    if (wv == 0) {
+      const float* x = src + (size_t)(H + g) * DH;
+      const float x1 = x[lane], x2 = x[lane + 64];
+      const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
+      const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+      const bf16_t k0 = f32_to_bf16(a0 * r), k1 = f32_to_bf16(a1 * r);
+      bf16_t* kp = pg + ((size_t)g * 16 + tok) * DH;
+      kp[lane] = k0;
+      kp[lane + 64] = k1;
+      knew[lane] = k0;
+      knew[lane + 64] = k1;
+    } else {
+      const float* v = src + (size_t)(H + Hkv + g) * DH;
+      const bf16_t v0 = f32_to_bf16(v[lane]), v1 = f32_to_bf16(v[lane + 64]);
+      bf16_t* vt = pg + (size_t)Hkv * 16 * DH + (size_t)g * DH * 16 + vperm(tok);
+      vt[(size_t)lane * 16] = v0;
+      vt[(size_t)(lane + 64) * 16] = v1;
+      vnew[lane] = v0;
+      vnew[lane + 64] = v1;
+    }
+  }
+  __syncthreads();
+
+  // lane l: key r = l / 4 of a page, dims 32 db .. +32 (db = l % 4) for the scores; value rows
+  // 2l and 2l + 1 (all 16 keys of the page, vperm order) for the output
+  const int r = lane >> 2, db = lane & 3;
+  uint32_t qw[G][16];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qw[gi][i] = *reinterpret_cast<const uint32_t*>(&qh[gi][db * 32 + 2 * i]);
+  const float k2 = scale * LOG2E;
+  float lrun[G], acc[G][2];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) { lrun[gi] = 0.f; acc[gi][0] = acc[gi][1] = 0.f; }
+
+  if (kbeg < kend) {
+    const int p_first = (kbeg >> 4) + wv, p_last = (kend - 1) >> 4;
+    const int np = p_first <= p_last ? (p_last - p_first) / 4 + 1 : 0;  // pages of this wave
+    const size_t vofs = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16 + (size_t)lane * 32;
+    const size_t kofs = ((size_t)g * 16 + r) * DH + db * 32;
+    const int32_t* prow = ptab + (size_t)seq * max_pages;
+    // page ids of this wave's pages, 64 at a time, one per lane
+    int pid = lane < np ? prow[p_first + 4 * lane] : 0;
+    uint4 kr[4], vr[4];
+    auto fetch = [&](int it) __attribute__((always_inline)) {
+      const int page = __builtin_amdgcn_readlane(pid, it & 63);
+      const bf16_t* pg = kv_slot + (size_t)page * page_elems;
+      const uint4* kp = reinterpret_cast<const uint4*>(pg + kofs);
+      const uint4* vp = reinterpret_cast<const uint4*>(pg + vofs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kr[i] = kp[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vr[i] = vp[i];
+    };
+    if (np > 0) fetch(0);
+    for (int it = 0; it < np; ++it) {
+      const int p = p_first + 4 * it;
+      uint32_t kw[16], v0w[8], v1w[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kw[4 * i] = kr[i].x; kw[4 * i + 1] = kr[i].y; kw[4 * i + 2] = kr[i].z; kw[4 * i + 3] = kr[i].w;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        v0w[4 * i] = vr[i].x; v0w[4 * i + 1] = vr[i].y; v0w[4 * i + 2] = vr[i].z; v0w[4 * i + 3] = vr[i].w;
+        v1w[4 * i] = vr[i + 2].x; v1w[4 * i + 1] = vr[i + 2].y; v1w[4 * i + 2] = vr[i + 2].z;
+        v1w[4 * i + 3] = vr[i + 2].w;
+      }
+      // next page's loads are in flight while this page is computed
+      if (it + 1 < np) {
+        if (((it + 1) & 63) == 0) pid = lane + it + 1 < np ? prow[p_first + 4 * (it + 1 + lane)] : 0;
+        fetch(it + 1);
+      }
+      const int key = p * 16 + r;
+      const bool valid = key >= kbeg && key < kend;
+      if (writer && p == (pos >> 4)) {
+        if (r == tok) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) kw[i] = *reinterpret_cast<const uint32_t*>(&knew[db * 32 + 2 * i]);
+        }
+        // value words: token tok sits at vperm position vperm(tok), half (vperm(tok) & 1) of word vperm(tok) / 2
+        const int ptok = vperm(tok), sh = 16 * (ptok & 1);
+        const uint32_t n0 = (uint32_t)vnew[2 * lane] << sh, n1 = (uint32_t)vnew[2 * lane + 1] << sh;
+        const uint32_t keep = sh ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          if (w == (ptok >> 1)) {
+            v0w[w] = (v0w[w] & keep) | n0;
+            v1w[w] = (v1w[w] & keep) | n1;
+          }
+        }
+      }
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[gi][i]), as_bf16x2(kw[i]), s, false);
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        const float pr = valid ? __builtin_amdgcn_exp2f(s * k2 - k2) : 0.f;
+        if (db == 0) lrun[gi] += pr;
+        float a0 = acc[gi][0], a1 = acc[gi][1];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {  // value word w holds the tokens vperm(2w), vperm(2w + 1)
+          const float pa = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), 4 * vperm(2 * w)));
+          const float pb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), 4 * vperm(2 * w + 1)));
+          const uint32_t pw = (uint32_t)f32_to_bf16(pa) | ((uint32_t)f32_to_bf16(pb) << 16);
+          a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v0w[w]), as_bf16x2(pw), a0, false);
+          a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v1w[w]), as_bf16x2(pw), a1, false);
+        }
+        acc[gi][0] = a0;
+        acc[gi][1] = a1;
+      }
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const float l = wave_sum(lrun[gi]);
+    if (lane == 0) { wm[wv][gi] = scale; wl[wv][gi] = l; }
+    wacc[wv][gi][2 * lane] = acc[gi][0];
+    wacc[wv][gi][2 * lane + 1] = acc[gi][1];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * DH; idx += 256) {
+    const int gi = idx / DH, e = idx % DH;
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      L += wl[w][gi];
+      A += wacc[w][gi][e];
+    }
+    const int hq = g * G + gi;
+    if (splits == 1) {
+      out[((size_t)m * H + hq) * DH + e] = f32_to_bf16(L > 0.f ? A / L : 0.f);
+    } else {
+      const size_t pi = ((size_t)m * H + hq) * splits + sp;
+      part_o[pi * DH + e] = A;
+      if (e == 0) { part_ml[2 * pi] = scale; part_ml[2 * pi + 1] = L; }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- bf16 flash attention for prefill, d_h = 128
 
 // grid (row-block slots, H), 256 threads; a workgroup handles 128-query row
@@ -1078,10 +1267,14 @@ bool attn_decode_supported(int dtype, int H, int Hkv, int dh) {
 hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                               const float2* rope, void* kv, size_t page_elems, int M, int H, int Hkv, int window,
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
-                              hipStream_t st) {
+                              const int32_t* order, hipStream_t st) {
   dim3 grid(M, Hkv, splits);
 #define DORY_DEC(GV)                                                                                             \
-  if (M > kDecodeMfmaRows)                                                                                     \
+  if (M > kDecodeMfmaRows && scale <= kFixedMaxScale)                                                          \
+    DORY_LAUNCH(k_attn_decode_valu_fx<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope,           \
+                (bf16_t*)kv, page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o, \
+                order);                                                                                        \
+  else if (M > kDecodeMfmaRows)                                                                                \
     DORY_LAUNCH(k_attn_decode_valu<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv, \
                 page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o);           \
   else                                                                                                         \

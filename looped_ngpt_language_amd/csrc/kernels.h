@@ -55,10 +55,12 @@ hipError_t launch_attn_rows(int dtype, const void* q, const int32_t* rows, const
 
 bool attn_decode_supported(int dtype, int H, int Hkv, int dh);
 constexpr int kDecodeMfmaRows = 16;  // split-key attention: MFMA kernel up to this many rows, VALU kernel above
+// order (may be NULL): a permutation of the M rows giving the order in which the batched (more than
+// kDecodeMfmaRows rows) kernels take them, longest context first, so that short rows fill the tail.
 hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                               const float2* rope, void* kv, size_t page_elems, int M, int H, int Hkv, int window,
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
-                              hipStream_t st);
+                              const int32_t* order, hipStream_t st);
 hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
                                hipStream_t st);
