@@ -349,12 +349,20 @@ static hipError_t launch_tile_gemm(const bf16_t* A, const bf16_t* B, void* out, 
 }
 
 // out: fp32 [M,N] (plain) or storage-type z [M,F] (dual, N = 2F).
-// Few rows (3..256): 128x128 tiles leave most CUs idle, so K is split until the
-// grid has >= 256 workgroups (partials in `split_ws`, then a reduce kernel).
+// Few rows (3..256): 128x128 tiles leave most CUs idle, so K is split (partials in
+// `split_ws`, then a reduce kernel) until the grid has enough workgroups: 256, or from 64
+// rows on 128 (at least two splits while the tiles alone are fewer than 256). Each split
+// writes and the reduce re-reads an M x N fp32 slice, which at 128 rows of the ~4B
+// projections costs more than the wider grid gains: 128 workgroups (with the 4-stage ring
+// below) beat 256 on o / qkv / down (14.5 / 18.5 / 21.4 vs 17.5 / 21.6 / 25.9 us), while
+// gate/up (128 tiles) needs its 2 splits (31 vs 49 us unsplit). At a few rows the slices are
+// small and the wider grid streams the weights faster (5-row speculative verify).
+static bool wide_rows(int M) { return M >= 64; }
 static int choose_split(int M, int N, int K, size_t split_ws_bytes) {
   const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+  const long target = wide_rows(M) ? 128 : 256;
   int S = 1;
-  while (tiles * S < 256 && S < 16 && (K / MF_BK) % (2 * S) == 0 &&
+  while ((tiles * S < target || (S == 1 && tiles < 256)) && S < 16 && (K / MF_BK) % (2 * S) == 0 &&
          (size_t)(2 * S) * M * N * sizeof(float) <= split_ws_bytes)
     S *= 2;
   return S;
@@ -383,9 +391,10 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {
       const int mt = (M + 127) / 128, nt = (N + 127) / 128;
-      // a long K range per workgroup streams its weights through a 4-stage ring (3 k-tiles in
-      // flight, one workgroup per CU); short ranges keep 2 stages, so two workgroups share a CU
-      if (K / S / MF_BK >= 16)
+      // a long K range (16 k-tiles, or 6 from 64 rows on) streams its weights through a 4-stage
+      // ring (3 k-tiles in flight, one workgroup per CU); shorter ranges keep 2 stages, so two
+      // workgroups share a CU
+      if (K / S / MF_BK >= (wide_rows(M) ? 6 : 16))
         DORY_LAUNCH((k_gemm_tile<128, 128, 2, 4, false, 4>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
                     (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
       else
