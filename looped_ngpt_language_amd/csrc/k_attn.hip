@@ -515,7 +515,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(
 #undef DORY_DEC_FETCH
 
 // VALU variant, used for many rows (batched decode): its lighter register use keeps
-// more waves, hence more pages, in flight per CU.
+// more waves, hence more pages, in flight per CU. This running-maximum form serves
+// attention scales above kFixedMaxScale; k_attn_decode_valu_fx below is the usual one.
 // grid (rows, H_kv, splits), 256 threads. Each workgroup attends the G query
 // heads of KV head g for one row over a page-aligned share of the row's keys.
 // Lane l of a wave reads key (l >> 2) of a page, dims 32*(l & 3) .. +32 for the
