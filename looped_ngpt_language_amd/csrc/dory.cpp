@@ -35,7 +35,10 @@ constexpr int kPage = 16;
 // back (rejected speculative tokens, at most 16) and a chunk's first key block (32 keys, aligned
 // down) never touches a recycled page.
 constexpr int kSwaReserve = 64;
-constexpr int kMaxSplits = 64;
+// Key splits per (row, KV head) at most: one decode row with 8 KV heads then fills the 256 CUs
+// with one round of the one-workgroup-per-CU MFMA decode kernel (131072-token context: 32 splits
+// 125 tok/s at k = 4, 64 splits 119, 128 splits 115).
+constexpr int kMaxSplits = 32;
 constexpr int kMaxGamma = 16;  // speculative draft length limit
 constexpr int kStageSlots = 4;
 constexpr size_t kAlign = 256;
