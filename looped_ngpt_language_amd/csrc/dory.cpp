@@ -393,6 +393,7 @@ const int32_t* slot_ptab(dory_ctx* c, int j) {
 
 // Copy the host upload image to the device upload area (pinned ring, async).
 bool stage_upload(dory_ctx* c, int n_ints) {
+  if (n_ints > c->L.upload_ints) { c->herr = hipErrorInvalidValue; return false; }  // sized at create
   if (c->dry || n_ints == 0) return true;
   const size_t bytes = (size_t)n_ints * 4;
   const int s = c->stage_cur;

@@ -250,3 +250,17 @@ def test_swa_recycling_off_keeps_every_slot_page():
     st = m.stats()
     assert st["swa_pages_total"] == 0 and st["swa_pages_in_use"] == 0
     assert m.kv_bytes_in_use() == st["pages_in_use"] * 8 * (2 * s.n_kv_heads * 16 * s.head_dim * 4)
+
+
+def test_batched_decode_upload_fits():
+    """One decode call for 128 sequences uploads their (seq, pos) rows, the page-table updates of
+    both tables (every sequence at a page boundary, sliding-window recycling on) and the rows'
+    longest-first order: all of it fits the upload area sized at create."""
+    s = synth.TINY
+    n = 128
+    m = dry(s, mode="last_loop", max_model_len=256, max_tokens=n, max_seqs=n, swa_recycle=True)
+    for q in range(n):
+        m.prefill(q, list(range(16 * (1 + q % 5))), 1)     # whole pages: the decode opens a new one
+    m.decode(list(range(n)), [1] * n)
+    assert all(m.seq_len(q) == 16 * (1 + q % 5) + 1 for q in range(n))
+    assert m.stats()["pages_in_use"] == sum(1 + q % 5 + 1 for q in range(n))
