@@ -15,7 +15,9 @@
 // logit (four 8-bit digits, most significant first), with histograms of mass
 // rather than counts; the draw scans 16 contiguous id spans (one per wave),
 // then walks the span that holds r 64 ids at a time. Every pass reads the row
-// from L2 (a 131072-token row is 512 KB).
+// from L2 (a 131072-token row is 512 KB), eight loads per thread in flight; the
+// passes are then bound by the ~30 VALU operations per element of the integer mass
+// on the row's one CU (about 26 us per pass at 131072 logits).
 #include "common.h"
 #include "kernels.h"
 
@@ -40,6 +42,27 @@ DORY_DEV unsigned long long wave_sum_u64(unsigned long long v) {
   return v;
 }
 
+// Calls f(i, l[i]) for the indices i = tid + SAMPLE_THREADS k of a row, loading SAMPLE_UNROLL
+// values per thread before using them, so that each thread keeps that many L2 loads in flight
+// (one load at a time left every pass waiting on L2 latency).
+constexpr int SAMPLE_UNROLL = 8;
+template <typename F>
+DORY_DEV void for_each_logit(const float* __restrict__ l, int V, int tid, F&& f) {
+  for (int base = tid; base < V; base += SAMPLE_THREADS * SAMPLE_UNROLL) {
+    float v[SAMPLE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+      const int i = base + u * SAMPLE_THREADS;
+      v[u] = i < V ? l[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+      const int i = base + u * SAMPLE_THREADS;
+      if (i < V) f(i, v[u]);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(SAMPLE_THREADS) k_sample(const float* __restrict__ logits, int V, float inv_t,
                                                            float top_p, const float* __restrict__ uniforms,
                                                            int32_t* __restrict__ ids) {
@@ -56,10 +79,9 @@ __global__ void __launch_bounds__(SAMPLE_THREADS) k_sample(const float* __restri
   // row maximum (and, for greedy, the lowest id holding it)
   float mx = -INFINITY;
   int mi = 0x7fffffff;
-  for (int i = tid; i < V; i += SAMPLE_THREADS) {
-    const float v = l[i];
+  for_each_logit(l, V, tid, [&](int i, float v) __attribute__((always_inline)) {
     if (v > mx) { mx = v; mi = i; }
-  }
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(mx, o, 64);
@@ -79,7 +101,7 @@ __global__ void __launch_bounds__(SAMPLE_THREADS) k_sample(const float* __restri
 
   // total mass
   unsigned long long part = 0;
-  for (int i = tid; i < V; i += SAMPLE_THREADS) part += token_mass(l[i], mx, inv_t);
+  for_each_logit(l, V, tid, [&](int, float v) __attribute__((always_inline)) { part += token_mass(v, mx, inv_t); });
   part = wave_sum_u64(part);
   if (lane == 0) wred[w] = part;
   __syncthreads();
@@ -99,12 +121,11 @@ __global__ void __launch_bounds__(SAMPLE_THREADS) k_sample(const float* __restri
       if (tid < 256) hist[tid] = 0;
       __syncthreads();
       const uint32_t prefix = s_prefix;
-      for (int i = tid; i < V; i += SAMPLE_THREADS) {
-        const float v = l[i];
+      for_each_logit(l, V, tid, [&](int, float v) __attribute__((always_inline)) {
         const uint32_t k = logit_key(v);
         if (pass == 0 || (k >> (shift + 8)) == (prefix >> (shift + 8)))
           atomicAdd(&hist[(k >> shift) & 255u], token_mass(v, mx, inv_t));
-      }
+      });
       __syncthreads();
       if (tid == 0) {
         unsigned long long cum = s_above;
@@ -131,9 +152,13 @@ __global__ void __launch_bounds__(SAMPLE_THREADS) k_sample(const float* __restri
   const int span = ((V + SAMPLE_WAVES - 1) / SAMPLE_WAVES + 63) & ~63;
   const int s0 = w * span, s1 = min(V, s0 + span);
   unsigned long long wm = 0;
-  for (int i = s0 + lane; i < s1; i += 64) {
-    const float v = l[i];
-    if (logit_key(v) >= kstar) wm += token_mass(v, mx, inv_t);
+  for (int b = s0 + lane; b < s1; b += 64 * SAMPLE_UNROLL) {
+    float v[SAMPLE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SAMPLE_UNROLL; ++u) v[u] = b + 64 * u < s1 ? l[b + 64 * u] : 0.f;
+#pragma unroll
+    for (int u = 0; u < SAMPLE_UNROLL; ++u)
+      if (b + 64 * u < s1 && logit_key(v[u]) >= kstar) wm += token_mass(v[u], mx, inv_t);
   }
   wm = wave_sum_u64(wm);
   if (lane == 0) wred[w] = wm;
@@ -152,29 +177,37 @@ __global__ void __launch_bounds__(SAMPLE_THREADS) k_sample(const float* __restri
   if (w != s_wave) return;
   unsigned long long rem = s_rem;
   int last = -1;  // last nucleus id seen: the answer if rounding leaves r unreached
-  for (int g = s0; g < s1; g += 64) {
-    const int i = g + lane;
-    unsigned long long q = 0;
-    if (i < s1) {
-      const float v = l[i];
-      if (logit_key(v) >= kstar) q = token_mass(v, mx, inv_t);
-    }
-    // inclusive scan of q over the 64 lanes
-    unsigned long long incl = q;
+  // groups of 64 ids in id order; SAMPLE_UNROLL groups' logits are loaded before they are walked
+  for (int gb = s0; gb < s1; gb += 64 * SAMPLE_UNROLL) {
+    float v[SAMPLE_UNROLL];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned long long t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
+    for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+      const int i = gb + 64 * u + lane;
+      v[u] = i < s1 ? l[i] : 0.f;
     }
-    const unsigned long long gtot = __shfl(incl, 63, 64);
-    if (rem < gtot) {
-      const unsigned long long hit = __ballot(incl > rem && q > 0);
-      if (lane == 0) ids[blockIdx.x] = g + (int)__builtin_ctzll(hit);
-      return;
+#pragma unroll
+    for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+      const int g = gb + 64 * u;
+      if (g >= s1) break;
+      const int i = g + lane;
+      const unsigned long long q = i < s1 && logit_key(v[u]) >= kstar ? token_mass(v[u], mx, inv_t) : 0ull;
+      // inclusive scan of q over the 64 lanes
+      unsigned long long incl = q;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const unsigned long long gtot = __shfl(incl, 63, 64);
+      if (rem < gtot) {
+        const unsigned long long hit = __ballot(incl > rem && q > 0);
+        if (lane == 0) ids[blockIdx.x] = g + (int)__builtin_ctzll(hit);
+        return;
+      }
+      rem -= gtot;
+      const unsigned long long seen = __ballot(q > 0);
+      if (seen) last = g + 63 - (int)__builtin_clzll(seen);
     }
-    rem -= gtot;
-    const unsigned long long seen = __ballot(q > 0);
-    if (seen) last = g + 63 - (int)__builtin_clzll(seen);
   }
   if (lane == 0) ids[blockIdx.x] = last >= 0 ? last : 0;
 }
