@@ -254,18 +254,22 @@ def test_mid_bf16_self_speculative_reuse_matches_plain():
 # inside the prompts
 NARROW = dataclasses.replace(synth.MID, d_model=256, n_heads=2, n_kv_heads=1, d_ff=512, vocab=2048, n_in=2, n_rec=4,
                              n_out=2, window=192)
+# attention scale above the fixed-offset limit (40): the running-maximum prefill and batched
+# decode kernels
+NARROW60 = dataclasses.replace(NARROW, attn_scale=60.0)
 
 
 @pytest.mark.parametrize("shape_name,mode,n_seq,min_len,max_len",
                          [("mid", "per_loop", 6, 17, 300), ("mid", "last_loop", 6, 17, 300),
-                          ("narrow", "last_loop", 20, 257, 360), ("narrow", "per_loop", 20, 257, 360)])
+                          ("narrow", "last_loop", 20, 257, 360), ("narrow", "per_loop", 20, 257, 360),
+                          ("narrow60", "last_loop", 20, 257, 360)])
 def test_bf16_batched_decode(shape_name, mode, n_seq, min_len, max_len):
     """Serving-style batched decode: sequences with ragged prompt lengths decode together
     (one call per step, rows = sequences); every sequence against its own oracle run,
     teacher-forced. Exercises the split-K small-M GEMM and multi-row split attention (the
     MFMA kernel up to 16 rows, the VALU kernel above; prompts over 256 tokens give it two
     key splits per row)."""
-    shape = synth.MID if shape_name == "mid" else NARROW
+    shape = {"mid": synth.MID, "narrow": NARROW, "narrow60": NARROW60}[shape_name]
     w = synth.make_weights(shape, seed=0)
     m = dory.Model(shape, w, kv_mode=mode, max_loops=2, max_seqs=n_seq, max_model_len=512, max_tokens=512)
     m.set_loops(2)
