@@ -479,11 +479,13 @@ bool fused_residual_ok(const dory_ctx* c, int M, bool decode) {
 double wbytes(const dory_ctx* c, int M) { return c->mx && M <= 2 ? 1.0 + 1.0 / 32 : (double)esize(c->cfg); }
 
 // C = A . W^T through the MXFP8 GEMV (calls of <= 2 rows when the context holds MX weights) or launch_gemm.
+// parts (may be NULL): as in launch_gemm, the split-K partials may be left in the split workspace.
 hipError_t project(dory_ctx* c, bool dual, const void* A, const void* W, const dory_ctx::MxMat& mx, void* out, int M,
-                   int N, int K) {
+                   int N, int K, int* parts = nullptr) {
+  if (parts) *parts = 0;
   if (c->mx && M <= 2 && dory::gemv_supported(K))
     return dory::launch_gemv(dual, A, mx.codes, mx.scales, out, M, N, K, c->stream);
-  return dory::launch_gemm(c->cfg.dtype, dual, A, W, out, M, N, K, SPLITK, c->stream);
+  return dory::launch_gemm(c->cfg.dtype, dual, A, W, out, M, N, K, SPLITK, c->stream, parts);
 }
 
 // One block application on M rows (hidden state per Flow; storage copy in hb when materialised).
@@ -555,9 +557,13 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
                              st));
     }
   }
+  // without the fused GEMV path, a split-K o / down product leaves its partials for the residual
+  // kernel to sum (one launch and one y round trip fewer)
+  int parts = 0;
   {
     Span sp(c, R_OPROJ, (double)d * hd * wb + Md * hd * es + Md * d * 4, 2.0 * Md * d * hd);
-    ok(c, project(c, false, c->W(c->L.o), c->wo[j], gmx ? c->mo[j] : dory_ctx::MxMat{}, y, M, d, hd));
+    ok(c, project(c, false, c->W(c->L.o), c->wo[j], gmx ? c->mo[j] : dory_ctx::MxMat{}, y, M, d, hd,
+                  fres ? nullptr : &parts));
   }
   if (fres) {
     Span sp(c, R_GU, 2.0 * F * d * wb + Md * d * 12 + 4.0 * d + Md * F * es, 2.0 * Md * 2 * F * d);
@@ -567,21 +573,22 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   } else {
     {
       Span sp(c, R_RESID, resid_bytes, 0);
-      ok(c, launch_residual(dt, f.h, y, c->aa[j], hb, M, d, st));
+      ok(c, launch_residual(dt, f.h, parts > 1 ? c->W<float>(c->L.splitk) : y, c->aa[j], hb, M, d, st, parts));
     }
     Span sp(c, R_GU, 2.0 * F * d * wb + Md * d * es + Md * F * es, 2.0 * Md * 2 * F * d);
     ok(c, project(c, true, hb, c->wgu[j], gmx ? c->mgu[j] : dory_ctx::MxMat{}, c->W(c->L.z), M, 2 * F, d));
   }
   {
     Span sp(c, R_DOWN, (double)d * F * wb + Md * F * es + Md * d * 4, 2.0 * Md * d * F);
-    ok(c, project(c, false, c->W(c->L.z), c->wd[j], gmx ? c->md[j] : dory_ctx::MxMat{}, y, M, d, F));
+    ok(c, project(c, false, c->W(c->L.z), c->wd[j], gmx ? c->md[j] : dory_ctx::MxMat{}, y, M, d, F,
+                  fres ? nullptr : &parts));
   }
   if (fres) {
     f.py = y;
     f.pa = c->am[j];
   } else {
     Span sp(c, R_RESID, resid_bytes, 0);
-    ok(c, launch_residual(dt, f.h, y, c->am[j], hb, M, d, st));
+    ok(c, launch_residual(dt, f.h, parts > 1 ? c->W<float>(c->L.splitk) : y, c->am[j], hb, M, d, st, parts));
   }
 }
 

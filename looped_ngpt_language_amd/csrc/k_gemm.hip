@@ -369,7 +369,8 @@ static int choose_split(int M, int N, int K, size_t split_ws_bytes) {
 }
 
 hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
-                       float* split_ws, size_t split_ws_bytes, hipStream_t st) {
+                       float* split_ws, size_t split_ws_bytes, hipStream_t st, int* parts) {
+  if (parts) *parts = 0;
   if (M <= 0) return hipSuccess;
   const int F = dual ? N / 2 : 0;
   if (dtype == 0) {
@@ -400,6 +401,10 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
       else
         DORY_LAUNCH((k_gemm_tile<128, 128, 2, 4, false, 2>), dim3(mt * nt, S), dim3(512), 0, st, (const bf16_t*)A,
                     (const bf16_t*)B, (void*)split_ws, M, N, K, 0, mt, nt, K / S);
+      if (parts && !dual) {
+        *parts = S;
+        return hipGetLastError();
+      }
       const size_t outs = (size_t)M * (dual ? F : N);
       if (dual)
         DORY_LAUNCH(k_splitk_reduce<true>, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st,

@@ -71,6 +71,62 @@ __global__ void __launch_bounds__(ROW_THREADS) k_residual(float* __restrict__ h,
   }
 }
 
+// The same step with y the sum of S split-K partial slices y[s][M][d] (slice = M * d floats), summed
+// in slice order from zero exactly as the split-K reduce kernel sums them, so the result equals
+// reduce-then-residual bit for bit while skipping that kernel and its y round trip. U slices are
+// loaded per trip (every load unconditional: indices past the last slice or the row re-read it).
+template <typename T, int U>
+__global__ void __launch_bounds__(ROW_THREADS) k_residual_parts(float* __restrict__ h, const float* __restrict__ y,
+                                                                int S, size_t slice, const float* __restrict__ alpha,
+                                                                T* __restrict__ hb, int d) {
+  __shared__ float red[ROW_THREADS / 64];
+  const size_t base = (size_t)blockIdx.x * d;
+  float yv[ROW_EPT], hv[ROW_EPT];
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    yv[e] = 0.f;
+    hv[e] = h[base + min((int)threadIdx.x + e * ROW_THREADS, d - 1)];
+  }
+  for (int s0 = 0; s0 < S; s0 += U) {
+    float t[U][ROW_EPT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < ROW_EPT; ++e)
+        t[u][e] = y[(size_t)min(s0 + u, S - 1) * slice + base + min((int)threadIdx.x + e * ROW_THREADS, d - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < ROW_EPT; ++e)
+        if (s0 + u < S) yv[e] += t[u][e];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    if ((int)threadIdx.x + e * ROW_THREADS >= d) yv[e] = hv[e] = 0.f;
+    ss += yv[e] * yv[e];
+  }
+  const float ry = rsqrtf(fmaxf(block_sum(ss, red, ROW_THREADS / 64), DORY_TINY_SS));
+  float st = 0.f;
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    const float a = i < d ? alpha[i] : 0.f;
+    hv[e] = hv[e] + a * (yv[e] * ry - hv[e]);
+    st += hv[e] * hv[e];
+  }
+  const float rh = rsqrtf(fmaxf(block_sum(st, red, ROW_THREADS / 64), DORY_TINY_SS));
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    if (i < d) {
+      const float v = hv[e] * rh;
+      h[base + i] = v;
+      St<T>::st(hb, base + i, v);
+    }
+  }
+}
+
 // out = N(a + b) written to h (fp32) and hb (storage); a and b may alias.
 // With b == nullptr: out = N(a), also written to s when s != nullptr.
 template <typename T>
@@ -186,7 +242,21 @@ hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int V, 
 }
 
 hipError_t launch_residual(int dtype, float* h, const float* y, const float* alpha, void* hb, int M, int d,
-                           hipStream_t st) {
+                           hipStream_t st, int parts) {
+  if (parts > 1) {
+    if (dtype != 1 || parts > 64) return hipErrorInvalidValue;
+    const size_t slice = (size_t)M * d;
+    if (parts >= 8)
+      DORY_LAUNCH((k_residual_parts<bf16_t, 8>), dim3(M), dim3(ROW_THREADS), 0, st, h, y, parts, slice, alpha,
+                  (bf16_t*)hb, d);
+    else if (parts >= 4)
+      DORY_LAUNCH((k_residual_parts<bf16_t, 4>), dim3(M), dim3(ROW_THREADS), 0, st, h, y, parts, slice, alpha,
+                  (bf16_t*)hb, d);
+    else
+      DORY_LAUNCH((k_residual_parts<bf16_t, 2>), dim3(M), dim3(ROW_THREADS), 0, st, h, y, parts, slice, alpha,
+                  (bf16_t*)hb, d);
+    return hipGetLastError();
+  }
   if (dtype == 0)
     DORY_LAUNCH(k_residual<float>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (float*)hb, d);
   else

@@ -34,8 +34,10 @@ namespace dory {
 
 hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int V, int d, int M, float* h, void* hb,
                         int32_t* err, hipStream_t st);
+// h <- N(h + alpha (N(y) - h)) on M rows of d; with parts > 1 (bf16 model) y holds that many split-K
+// partial slices [parts][M][d] left by launch_gemm (see below), summed here.
 hipError_t launch_residual(int dtype, float* h, const float* y, const float* alpha, void* hb, int M, int d,
-                           hipStream_t st);
+                           hipStream_t st, int parts = 0);
 hipError_t launch_norm_sum(int dtype, const float* a, const float* b, float* h, float* s, void* hb, int M, int d,
                            hipStream_t st);
 constexpr int kArgmaxParts = 64;  // partial (max, index) pairs per row in the argmax scratch
@@ -87,7 +89,9 @@ int mx_scale_row_bytes(int K);
 hipError_t launch_sample(const float* logits, int rows, int V, float temperature, float top_p, const float* uniforms,
                          int32_t* ids, hipStream_t st);
 // C = A . B^T (bf16 or fp32 model). split_ws (may be NULL) holds split-K partials for 3..256 rows.
+// parts (may be NULL; plain products only): when the product is split over K, the partial slices
+// [S][M][N] are left in split_ws unsummed, out is not written and *parts = S; otherwise *parts = 0.
 hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void* out, int M, int N, int K,
-                       float* split_ws, size_t split_ws_bytes, hipStream_t st);
+                       float* split_ws, size_t split_ws_bytes, hipStream_t st, int* parts = nullptr);
 
 }  // namespace dory
