@@ -64,8 +64,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the forward pass shards by sequence with no exchange; see DESIGN.md).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward pass would shard by sequence, with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
     import torch
 
