@@ -101,6 +101,9 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 // (global_load_lds_dwordx4; M0 holds the wave's LDS base). Issued from inline assembly so that
 // the compiler, which cannot tell LDS stages apart, does not wait for it before unrelated LDS
 // reads; the caller waits with s_waitcnt vmcnt before the barrier that publishes the data.
+// The compiler warns that m0 is a reserved register it will not preserve around the asm: in the
+// gfx950 code of k_gemm.hip and k_attn.hip every instruction that reads or writes m0 is one of
+// these asm blocks (the compiler itself keeps nothing in m0 there), so no value is lost.
 DORY_DEV void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_byte) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
                :: "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(voff), "s"(gbase)
