@@ -40,3 +40,18 @@ def test_native_sources_do_not_reference_the_oracle():
     for name in os.listdir(csrc):
         text = open(os.path.join(csrc, name)).read()
         assert "oracle" not in text.lower(), name
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With the HIP library absent the binding raises instead of computing anything another way
+    (run in a child process so the library this test session loaded stays as it is)."""
+    import subprocess
+    import sys
+    code = ("import looped_ngpt_language_amd.dory as d\n"
+            f"d.LIB_PATH = {str(tmp_path / 'absent' / 'libdory.so')!r}\n"
+            "try:\n"
+            "    d.lib()\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0 and r.stdout.startswith("raised"), (r.stdout, r.stderr)
