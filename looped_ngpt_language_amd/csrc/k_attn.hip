@@ -747,6 +747,7 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
   __shared__ __attribute__((aligned(16))) bf16_t vnew[DH];
   __shared__ float wm[4][G], wl[4][G];
   __shared__ float wacc[4][G][DH];
+  __shared__ __attribute__((aligned(16))) float pbuf[4][G][16];  // per wave: one page's probabilities
   const int m = order ? order[blockIdx.x] : (int)blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = rows[2 * m], pos = rows[2 * m + 1];
@@ -875,15 +876,24 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
         s += __shfl_xor(s, 1, 64);
         s += __shfl_xor(s, 2, 64);
         const float pr = valid ? __builtin_amdgcn_exp2f(s * k2 - k2) : 0.f;
-        if (db == 0) lrun[gi] += pr;
+        if (db == 0) {
+          lrun[gi] += pr;
+          pbuf[wv][gi][r] = pr;  // the page's 16 probabilities, by token; read back by every lane
+        }
+        // (one wave's LDS operations complete in order, so the reads below see these writes, and
+        // the next page's writes land after these reads)
+        float pv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 q4 = *reinterpret_cast<const float4*>(&pbuf[wv][gi][4 * i]);
+          pv[4 * i] = q4.x; pv[4 * i + 1] = q4.y; pv[4 * i + 2] = q4.z; pv[4 * i + 3] = q4.w;
+        }
         float a0 = acc[gi][0], a1 = acc[gi][1];
 #pragma unroll
         for (int w = 0; w < 8; ++w) {  // value word w holds the tokens vperm(2w), vperm(2w + 1)
-          const float pa = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), 4 * vperm(2 * w)));
-          const float pb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), 4 * vperm(2 * w + 1)));
-          const uint32_t pw = (uint32_t)f32_to_bf16(pa) | ((uint32_t)f32_to_bf16(pb) << 16);
-          a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v0w[w]), as_bf16x2(pw), a0, false);
-          a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v1w[w]), as_bf16x2(pw), a1, false);
+          const bf16x2_t pw = {(__bf16)pv[vperm(2 * w)], (__bf16)pv[vperm(2 * w + 1)]};
+          a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v0w[w]), pw, a0, false);
+          a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v1w[w]), pw, a1, false);
         }
         acc[gi][0] = a0;
         acc[gi][1] = a1;
