@@ -731,9 +731,10 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
 // Fixed-offset form of the VALU kernel (attention scale <= kFixedMaxScale): q^ and k^ are unit
 // vectors, so the probabilities are exp(scale (q^.k^ - 1)) with no running maximum, no rescaling
 // and a lane-local row sum. Scores are packed-bf16 dot products (v_dot2_f32_bf16) of the query
-// with the key words as loaded; each key's probability is the same for every lane and is taken
-// with readlane, rounded to bf16 in pairs (as the MFMA kernels feed P) and dotted with the
-// packed value words. Partials carry max = scale, so the wave combine and k_attn_merge apply.
+// with the key words as loaded; each page's 16 probabilities are written to LDS once by the
+// lanes that hold them and read back by every lane, rounded to bf16 in pairs (as the MFMA
+// kernels feed P) and dotted with the packed value words. Partials carry max = scale, so the
+// wave combine and k_attn_merge apply.
 template <int G>
 __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
     const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
