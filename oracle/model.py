@@ -109,18 +109,19 @@ def attend(q, K, V, positions, window, n_heads, n_kv_heads, scale) -> np.ndarray
     """
     T = q.shape[0]
     group = n_heads // n_kv_heads
-    kv_of_head = np.arange(n_heads) // group
     out = np.empty((T, n_heads, V.shape[-1]), dtype=np.float64)
     for i in range(T):
         p = int(positions[i])
         lo = 0 if window is None else max(0, p - window + 1)
-        k = K[lo:p + 1][:, kv_of_head, :]          # [n, H, dh]
-        v = V[lo:p + 1][:, kv_of_head, :]
-        s = scale * np.einsum("nhd,hd->hn", k, q[i])
-        s = s - s.max(axis=1, keepdims=True)
-        w = np.exp(s)
-        w = w / w.sum(axis=1, keepdims=True)
-        out[i] = np.einsum("hn,nhd->hd", w, v)
+        for g in range(n_kv_heads):
+            heads = slice(g * group, (g + 1) * group)   # the query heads that read KV head g
+            k = K[lo:p + 1, g, :]                        # [n, dh]
+            v = V[lo:p + 1, g, :]
+            s = scale * (q[i, heads] @ k.T)              # [group, n]
+            s = s - s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            w = w / w.sum(axis=1, keepdims=True)
+            out[i, heads] = w @ v
     return out
 
 
