@@ -141,6 +141,7 @@ typedef struct dory_stats {
   int32_t live_seqs;
   int32_t swa_pages_total;  /* sliding-window pages (SWA recycling; else 0) */
   int32_t swa_pages_in_use;
+  int32_t max_attn_splits;  /* most key splits per (row, KV head) any split-attention launch took */
 } dory_stats;
 
 /* Bytes the caller must allocate. kv_tokens: KV capacity in tokens summed over
@@ -159,9 +160,15 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t k
                         size_t workspace_bytes, void* stream, dory_ctx** out);
 void dory_destroy(dory_ctx* ctx);
 
-/* Loop count k for the following calls: 1..cfg->max_loops (the pages allow
- * 1..4). In per-loop mode, a live sequence whose cache lacks loops 1..k for
- * some of its positions makes a later call on it fail with DORY_E_STATE. */
+/* Loop count k for the following calls: 1..cfg->max_loops. The recurrent core
+ * runs k times per token; the released model takes 1..4 loops, chosen at run
+ * time (lucasainews article "NVIDIA, 루프 구조 4B 모델 Dory1.0-4B 4가지 정밀도로
+ * 공개", section "실행 방법": n_recurrent_loops / dory.num_loops; trawling.dev
+ * digest "NVIDIA, 반복 연산형 4B 언어 모델 Dory 공개", section "AI 요약"), and
+ * a pass applies 16 + 20k blocks: 36 / 56 / 96 at k = 1 / 2 / 4 (onedev.kr
+ * summary, section "어떻게 동작하나"). k outside 1..max_loops: DORY_E_INVALID.
+ * In per-loop mode, a live sequence whose cache lacks loops 1..k for some of
+ * its positions makes a later call on it fail with DORY_E_STATE. */
 dory_status dory_set_loops(dory_ctx* ctx, int32_t k);
 dory_status dory_get_loops(const dory_ctx* ctx, int32_t* k);
 
@@ -169,7 +176,11 @@ dory_status dory_get_loops(const dory_ctx* ctx, int32_t* k);
  * page capacity is recomputed for the new slot count. */
 dory_status dory_kv_mode(dory_ctx* ctx, int32_t mode);
 
-/* Append one chunk of n_tokens tokens (device int32 ids) to sequence seq_id,
+/* Prefill: the forward pass of the loop equation s_0 = x, u_t = N(s_{t-1} + x),
+ * s_t = N(F(u_t)) over a chunk of consecutive positions (onedev.kr summary,
+ * section "어떻게 동작하나"), with the KV writes of the configured mode (trawling.dev
+ * digest, section "KV 캐시와 실행 환경"; onedev.kr summary, section "전제와 한계").
+ * Append one chunk of n_tokens tokens (device int32 ids) to sequence seq_id,
  * creating it if it is not live, and run the forward pass on the chunk: in
  * every block application the chunk's keys/values are written to the block's
  * cache slot first, then every query of the chunk attends over its masked
@@ -181,11 +192,20 @@ dory_status dory_prefill(dory_ctx* ctx, int32_t seq_id, const int32_t* tokens_de
                          int32_t n_tokens, int32_t logits_rows, float* logits_dev,
                          int32_t* ids_dev);
 
-/* One decode step for n_seqs distinct live sequences: token tokens_dev[i]
- * (device) is appended to sequence seq_ids_host[i] (host). Writes logits
+/* Decode: the same forward pass on one new position of each of n_seqs distinct
+ * live sequences (onedev.kr summary, section "어떻게 동작하나"), batched the way
+ * the serving setup runs up to 128 sequences at once (lucasainews article,
+ * section "실행 방법": max-num-seqs 128); in last-loop mode every loop's queries
+ * read the keys/values the final loop of earlier steps left (onedev.kr summary,
+ * section "전제와 한계"). Token tokens_dev[i] (device) is appended to sequence
+ * seq_ids_host[i] (host: the scheduler needs the ids to build page tables and
+ * the row order before anything is enqueued, and the list is small). Writes logits
  * [n_seqs, V] to logits_dev (may be NULL: then only ids are produced, using
  * workspace memory) and the greedy next ids [n_seqs] to next_ids_dev (may be
- * NULL). next_ids_dev may be passed as the next call's tokens_dev. */
+ * NULL). next_ids_dev may be passed as the next call's tokens_dev. Errors: a
+ * sequence not live or listed twice, n_seqs outside 1..min(max_tokens,
+ * max_seqs) -> DORY_E_INVALID; per-loop cache lacking loops -> DORY_E_STATE;
+ * pool exhausted -> DORY_E_NOMEM. */
 dory_status dory_decode(dory_ctx* ctx, int32_t n_seqs, const int32_t* seq_ids_host,
                         const int32_t* tokens_dev, float* logits_dev, int32_t* next_ids_dev);
 

@@ -507,6 +507,7 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   const bool fused_decode = decode && paged;
   const bool flash = !decode && dt == DORY_BF16 && dh == 128 && M > c->L.part_rows;
   const int splits = flash ? 1 : choose_splits(c, M, keys_max, paged);
+  c->stats.max_attn_splits = std::max(c->stats.max_attn_splits, splits);
   const bool fres = fused_residual_ok(c, M, decode);
   if (c->dry) {
     c->stats.kernel_launches += (fres ? 4 : 6) + (fused_decode ? 1 : 2) + (splits > 1);

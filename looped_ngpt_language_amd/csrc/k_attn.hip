@@ -881,14 +881,19 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
           lrun[gi] += pr;
           pbuf[wv][gi][r] = pr;  // the page's 16 probabilities, by token; read back by every lane
         }
-        // (one wave's LDS operations complete in order, so the reads below see these writes, and
-        // the next page's writes land after these reads)
+        // One wave's LDS operations complete in issue order, so no s_barrier is needed; the
+        // wavefront-scope fence and wave barrier keep the compiler from moving the reads below
+        // above these writes, or the next page's writes above these reads.
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
         float pv[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float4 q4 = *reinterpret_cast<const float4*>(&pbuf[wv][gi][4 * i]);
           pv[4 * i] = q4.x; pv[4 * i + 1] = q4.y; pv[4 * i + 2] = q4.z; pv[4 * i + 3] = q4.w;
         }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
         float a0 = acc[gi][0], a1 = acc[gi][1];
 #pragma unroll
         for (int w = 0; w < 8; ++w) {  // value word w holds the tokens vperm(2w), vperm(2w + 1)

@@ -48,7 +48,7 @@ class Stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("calls", "block_apps", "sublayer_apps", "full_apps", "swa_apps",
                                          "kernel_launches")] + \
               [(n, C.c_int32) for n in ("n_slots", "pages_total", "pages_in_use", "live_seqs", "swa_pages_total",
-                                        "swa_pages_in_use")]
+                                        "swa_pages_in_use", "max_attn_splits")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -48,8 +48,14 @@ def test_4b_prefill_and_decode_vs_oracle(big):
     o_h = [om.last_hidden[-1]]
     lg, ids = m.prefill(0, prompt[:40], 40)
     g_h = [m.last_hidden(1)[0].cpu().numpy()]
-    errs = [float(np.max(np.abs(lg.cpu().numpy() - olg)))]
-    assert np.mean(ids.cpu().numpy() == oids) >= 0.9
+    g_lg, g_ids = lg.cpu().numpy(), ids.cpu().numpy()
+    errs = [float(np.max(np.abs(g_lg - olg)))]
+    near = 0
+    for i in range(40):       # every differing id must be a near-tie of the oracle's logits
+        if g_ids[i] != oids[i]:
+            near += 1
+            assert olg[i][oids[i]] - olg[i][g_ids[i]] < 2 * np.max(np.abs(g_lg[i] - olg[i])), i
+    say(f"  prefill ids {40 - near}/40 equal, {near} near-ties")
     tok = int(oids[-1])
     for step in range(2):
         l1, i1 = m.decode([0], torch.tensor([tok], dtype=torch.int32, device=m.device))
@@ -99,11 +105,15 @@ def test_4b_width_2048_token_prefill_vs_oracle():
     g_h = m.last_hidden(1)[0].cpu().numpy()
     om = OracleModel(shape, w, "per_loop", 1)
     olg, oids = om.prefill(0, prompt, 8)
-    err = float(np.max(np.abs(lg.cpu().numpy() - olg)))
+    g_lg, g_ids = lg.cpu().numpy(), ids.cpu().numpy()
+    err = float(np.max(np.abs(g_lg - olg)))
     err_h = float(np.max(np.abs(g_h - om.last_hidden[-1])))
-    agree = int(np.sum(ids.cpu().numpy() == oids))
+    agree = int(np.sum(g_ids == oids))
     say(f"  logits max-abs {err:.3e}, hidden max-abs {err_h:.3e}, ids {agree}/8")
     assert err <= 5e-2 and err_h <= 3e-2
+    for i in range(8):        # a differing id must be a near-tie of the oracle's logits
+        if g_ids[i] != oids[i]:
+            assert olg[i][oids[i]] - olg[i][g_ids[i]] < 2 * np.max(np.abs(g_lg[i] - olg[i])), i
     m.close()
 
 
