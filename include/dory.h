@@ -231,12 +231,35 @@ dory_status dory_get_stats(const dory_ctx* ctx, dory_stats* out);
  * hold at least top_p of the total mass (ties at that value all kept; top_p >= 1
  * keeps every token, top_p <= 0 the top logit and its ties); the id is the first
  * nucleus token in id order whose running mass exceeds floor(u * nucleus mass).
- * temperature <= 0 is greedy (lowest id among the largest logits). Nothing is
- * allocated; the call is queued on `stream` (a hipStream_t, NULL for the
+ * temperature <= 0 is greedy (lowest id among the largest logits); a positive
+ * temperature so small that 1/T overflows keeps only the largest logit and its
+ * ties, as the rule does. Each row is spread over several workgroups that pass
+ * partial results through a scratch buffer of dory_sample_scratch_bytes(rows,
+ * vocab) bytes, which the library allocates on the current device at the first
+ * call that needs it (and grows for a larger call; hipFree of the old buffer
+ * waits for the device), keeping it until the process ends; every call on one
+ * device shares it, so calls that overlap on one GPU (other streams or host
+ * threads) race. The call is queued on `stream` (a hipStream_t, NULL for the
  * default stream). DORY_E_INVALID: rows < 0, vocab outside 1..2^23, NULL
- * buffers with rows > 0, NaN temperature or top_p. */
+ * buffers with rows > 0, NaN or infinite temperature, NaN top_p;
+ * DORY_E_NOMEM: the scratch could not be allocated. */
 dory_status dory_sample(const float* logits_dev, int32_t rows, int32_t vocab, float temperature, float top_p,
                         const float* uniforms_dev, int32_t* ids_dev, void* stream);
+
+/* Bytes of scratch a dory_sample call of `rows` rows of `vocab` logits uses (0 for invalid
+ * sizes): about 8.3 KB per row. */
+size_t dory_sample_scratch_bytes(int32_t rows, int32_t vocab);
+
+/* dory_sample for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that forbid allocation): the same draw and the same kernels, with the scratch
+ * in a fixed 4 MiB device array of the library (one copy per GPU, held until the process ends)
+ * instead of an allocation. Calls no hipMalloc, hipFree or other allocating routine; the
+ * array's address is looked up once per device at the first call on it. Every call on one GPU
+ * shares the array (each call clears what must start at zero): calls that overlap on one GPU
+ * race. DORY_E_INVALID as dory_sample, and when dory_sample_scratch_bytes(rows, vocab) exceeds
+ * 4 MiB (rows <= 256 always fit, for any vocab). */
+dory_status dory_sample_static(const float* logits_dev, int32_t rows, int32_t vocab, float temperature,
+                               float top_p, const float* uniforms_dev, int32_t* ids_dev, void* stream);
 
 /* MXFP8 quantisation (OCP Microscaling Formats v1.0, MXFP8 with E4M3 elements)
  * of a bf16 matrix src_dev [rows, cols] (device, row-major, 16-byte aligned,
@@ -277,6 +300,23 @@ dory_status dory_last_hidden(dory_ctx* ctx, float* dst_dev, int32_t rows);
 dory_status dory_spec_decode(dory_ctx* ctx, int32_t seq_id, int32_t last_host, int32_t n_new,
                              int32_t gamma, int32_t k_draft, int32_t k_verify, int32_t reuse,
                              int32_t* out_ids_host, int32_t* n_out);
+
+/* Counters of the dory_spec_decode calls since the last reset, for its cost model: rounds
+ * (draft + verify steps), tokens drafted, drafted tokens the verifier accepted, ids produced
+ * (accepted + one per round), and the GPU time of the draft phases and of the verify phases
+ * (HIP events recorded on the context's stream at each phase boundary; the verify phase runs
+ * from the end of the last draft step to the end of the verify chunk's LM head and argmax). */
+typedef struct dory_spec_stats {
+  int64_t rounds;
+  int64_t drafted;
+  int64_t accepted;
+  int64_t produced;
+  double draft_ms;
+  double verify_ms;
+} dory_spec_stats;
+
+/* Copy the counters to *out; with reset != 0 restart them from zero afterwards. */
+dory_status dory_get_spec_stats(dory_ctx* ctx, dory_spec_stats* out, int32_t reset);
 
 /* Per-kernel accounting, one entry per kernel role of the forward pass
  * ("qkv_proj", "rope_qknorm_kvwrite", "attention", "o_proj", "ngpt_residual",

@@ -276,6 +276,9 @@ struct dory_ctx {
   std::vector<TimedRec> recs;
   std::string err;
   hipError_t herr = hipSuccess;
+  // self-speculative decoding: counters and the phase-boundary events of one round
+  dory_spec_stats spec{};
+  hipEvent_t spec_ev[3] = {};
 
   template <typename P = char>
   P* W(size_t off) const { return reinterpret_cast<P*>(ws + off); }
@@ -1061,6 +1064,8 @@ void dory_destroy(dory_ctx* c) {
   if (!c->dry) {
     (void)hipStreamSynchronize(c->stream);
     for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->spec_ev)
+      if (e) (void)hipEventDestroy(e);
     for (int i = 0; i < kStageSlots; ++i) {
       if (c->stage[i]) (void)hipHostFree(c->stage[i]);
       if (c->stage_ev[i]) (void)hipEventDestroy(c->stage_ev[i]);
@@ -1156,13 +1161,46 @@ dory_status dory_get_stats(const dory_ctx* c, dory_stats* out) {
   return DORY_OK;
 }
 
+namespace {
+dory_status sample_args_ok(const float* logits_dev, int32_t rows, int32_t vocab, float temperature, float top_p,
+                           const float* uniforms_dev, const int32_t* ids_dev) {
+  if (rows < 0 || vocab < 1 || vocab > (1 << 23)) return DORY_E_INVALID;
+  if (std::isnan(temperature) || std::isinf(temperature) || std::isnan(top_p)) return DORY_E_INVALID;
+  if (rows > 0 && (!logits_dev || !uniforms_dev || !ids_dev)) return DORY_E_INVALID;
+  return DORY_OK;
+}
+}  // namespace
+
 dory_status dory_sample(const float* logits_dev, int32_t rows, int32_t vocab, float temperature, float top_p,
                         const float* uniforms_dev, int32_t* ids_dev, void* stream) {
-  if (rows < 0 || vocab < 1 || vocab > (1 << 23) || std::isnan(temperature) || std::isnan(top_p)) return DORY_E_INVALID;
-  if (rows > 0 && (!logits_dev || !uniforms_dev || !ids_dev)) return DORY_E_INVALID;
-  const hipError_t e =
-      dory::launch_sample(logits_dev, rows, vocab, temperature, top_p, uniforms_dev, ids_dev, static_cast<hipStream_t>(stream));
+  const dory_status a = sample_args_ok(logits_dev, rows, vocab, temperature, top_p, uniforms_dev, ids_dev);
+  if (a != DORY_OK || rows == 0) return a;
+  void* scratch = nullptr;
+  size_t bytes = 0;
+  hipError_t e = dory::sample_library_scratch(rows, vocab, &scratch, &bytes);
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return DORY_E_NOMEM;
+  if (e == hipSuccess)
+    e = dory::launch_sample(logits_dev, rows, vocab, temperature, top_p, uniforms_dev, ids_dev, scratch, bytes,
+                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DORY_OK : DORY_E_HIP;
+}
+
+dory_status dory_sample_static(const float* logits_dev, int32_t rows, int32_t vocab, float temperature, float top_p,
+                               const float* uniforms_dev, int32_t* ids_dev, void* stream) {
+  const dory_status a = sample_args_ok(logits_dev, rows, vocab, temperature, top_p, uniforms_dev, ids_dev);
+  if (a != DORY_OK || rows == 0) return a;
+  if (dory::sample_scratch_bytes(rows, vocab) > dory::kSampleStaticScratchBytes) return DORY_E_INVALID;
+  void* scratch = nullptr;
+  hipError_t e = dory::sample_static_scratch(&scratch);
+  if (e == hipSuccess)
+    e = dory::launch_sample(logits_dev, rows, vocab, temperature, top_p, uniforms_dev, ids_dev, scratch,
+                            dory::kSampleStaticScratchBytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DORY_OK : DORY_E_HIP;
+}
+
+size_t dory_sample_scratch_bytes(int32_t rows, int32_t vocab) {
+  if (rows < 0 || vocab < 1 || vocab > (1 << 23)) return 0;
+  return dory::sample_scratch_bytes(rows, vocab);
 }
 
 dory_status dory_quantize_mxfp8(const void* src_dev, int64_t rows, int32_t cols, void* codes_dev, void* scales_dev,
@@ -1196,6 +1234,13 @@ dory_status dory_last_hidden(dory_ctx* c, float* dst, int32_t rows) {
   hipError_t e = hipMemcpyAsync(dst, c->last_h + (size_t)(c->last_rows - rows) * d, (size_t)rows * d * 4,
                                 hipMemcpyDeviceToDevice, c->stream);
   return e == hipSuccess ? DORY_OK : fail(c, DORY_E_HIP, "%s", hipGetErrorString(e));
+}
+
+dory_status dory_get_spec_stats(dory_ctx* c, dory_spec_stats* out, int32_t reset) {
+  if (!c || !out) return DORY_E_INVALID;
+  *out = c->spec;
+  if (reset) c->spec = dory_spec_stats{};
+  return DORY_OK;
 }
 
 dory_status dory_set_timing(dory_ctx* c, int32_t enable) {
@@ -1251,6 +1296,8 @@ dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_n
   if (gamma + 1 > c->cfg.max_tokens || gamma + 1 > c->L.logit_rows)
     return fail(c, DORY_E_INVALID, "gamma + 1 exceeds max_tokens or the logits scratch");
   if (c->dry) return fail(c, DORY_E_STATE, "self-speculative decoding needs the GPU");
+  for (hipEvent_t& e : c->spec_ev)
+    if (!e && hipEventCreate(&e) != hipSuccess) return fail(c, DORY_E_HIP, "hipEventCreate failed");
   const int k_saved = c->k;
   int32_t* toks = c->W<int32_t>(c->L.spec);   // [last, d1..d_gamma]
   int32_t* vids = toks + 32;                  // verifier ids [gamma+1]
@@ -1264,6 +1311,7 @@ dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_n
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);  // `last` lives on this host stack frame
     if (e != hipSuccess) { st = fail(c, DORY_E_HIP, "%s", hipGetErrorString(e)); break; }
     c->k = k_draft;
+    (void)hipEventRecord(c->spec_ev[0], c->stream);
     const size_t dm = (size_t)c->cfg.d_model;
     float* sx = c->W<float>(c->L.spec_x);
     float* ss = c->W<float>(c->L.spec_s1);
@@ -1273,6 +1321,7 @@ dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_n
       st = decode_impl(c, 1, &sid, toks + i, nullptr, toks + i + 1, o);
     }
     if (st != DORY_OK) break;
+    (void)hipEventRecord(c->spec_ev[1], c->stream);
     if (reuse) {
       // the draft's cache stays: input stack and loop 1 for d_gamma only, then loops 2..k_verify,
       // the output stack and the LM head for all gamma + 1 rows
@@ -1288,6 +1337,7 @@ dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_n
       c->k = k_verify;
       if ((st = dory_prefill(c, sid, toks, gamma + 1, gamma + 1, logits, vids)) != DORY_OK) break;
     }
+    (void)hipEventRecord(c->spec_ev[2], c->stream);
     e = hipMemcpyAsync(host.data(), toks, (gamma + 1) * 4, hipMemcpyDeviceToHost, c->stream);
     if (e == hipSuccess) e = hipMemcpyAsync(host.data() + gamma + 1, vids, (gamma + 1) * 4, hipMemcpyDeviceToHost, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
@@ -1296,6 +1346,13 @@ dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_n
     const int32_t* v = host.data() + gamma + 1;  // verifier ids after last, d1, ..., d_gamma
     int acc = 0;
     while (acc < gamma && d[acc] == v[acc]) ++acc;
+    float t_draft = 0.f, t_verify = 0.f;
+    if (hipEventElapsedTime(&t_draft, c->spec_ev[0], c->spec_ev[1]) == hipSuccess) c->spec.draft_ms += t_draft;
+    if (hipEventElapsedTime(&t_verify, c->spec_ev[1], c->spec_ev[2]) == hipSuccess) c->spec.verify_ms += t_verify;
+    c->spec.rounds++;
+    c->spec.drafted += gamma;
+    c->spec.accepted += acc;
+    c->spec.produced += acc + 1;
     for (int i = 0; i < acc; ++i) out_ids[count++] = d[i];
     out_ids[count++] = v[acc];
     last = v[acc];

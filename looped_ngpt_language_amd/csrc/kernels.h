@@ -85,9 +85,18 @@ hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* c
 // bytes per weight row of the lane-major MXFP8 scale layout the GEMV reads (0: K unsupported)
 int mx_scale_row_bytes(int K);
 // Temperature / top-p draw per row of fp32 logits [rows, V] with the caller's uniforms [rows]
-// (k_sample.hip); temperature <= 0 is greedy. 1 <= V <= 2^23.
+// (k_sample.hip); temperature <= 0 is greedy. 1 <= V <= 2^23. Each row is spread over several
+// workgroups that hand partial results to each other through `scratch` (device memory of at
+// least sample_scratch_bytes(rows, V) bytes; the call clears what must start at zero).
+size_t sample_scratch_bytes(int rows, int V);
 hipError_t launch_sample(const float* logits, int rows, int V, float temperature, float top_p, const float* uniforms,
-                         int32_t* ids, hipStream_t st);
+                         int32_t* ids, void* scratch, size_t scratch_bytes, hipStream_t st);
+// dory_sample's scratch: allocated on the current device at first use, grown when needed.
+hipError_t sample_library_scratch(int rows, int V, void** ptr, size_t* bytes);
+// dory_sample_static's scratch: the current device's copy of a fixed device array of
+// kSampleStaticScratchBytes bytes (its address is looked up once per device).
+constexpr size_t kSampleStaticScratchBytes = (size_t)4 << 20;
+hipError_t sample_static_scratch(void** ptr);
 // C = A . B^T (bf16 or fp32 model). split_ws (may be NULL) holds split-K partials for 3..256 rows.
 // parts (may be NULL; plain products only): when the product is split over K, the partial slices
 // [S][M][N] are left in split_ws unsummed, out is not written and *parts = S; otherwise *parts = 0.

@@ -59,6 +59,14 @@ class KernelTime(C.Structure):
                 ("timed_launches", C.c_int64), ("total_ms", C.c_double)]
 
 
+class SpecStats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("rounds", "drafted", "accepted", "produced")] + \
+              [(n, C.c_double) for n in ("draft_ms", "verify_ms")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
 EXPORTS = {
     "dory_query_sizes": (C.c_int, [C.POINTER(Config), C.c_int32, C.c_int64, C.POINTER(C.c_size_t),
                                    C.POINTER(C.c_size_t)]),
@@ -80,8 +88,12 @@ EXPORTS = {
     "dory_quantize_mxfp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dory_sample": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p, C.c_void_p,
                               C.c_void_p]),
+    "dory_sample_static": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p,
+                                     C.c_void_p, C.c_void_p]),
+    "dory_sample_scratch_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
     "dory_spec_decode": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                    C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+    "dory_get_spec_stats": (C.c_int, [C.c_void_p, C.POINTER(SpecStats), C.c_int32]),
     "dory_set_timing": (C.c_int, [C.c_void_p, C.c_int32]),
     "dory_get_timing": (C.c_int, [C.c_void_p, C.POINTER(KernelTime), C.c_int32, C.POINTER(C.c_int32), C.c_int32]),
     "dory_last_error": (C.c_char_p, [C.c_void_p]),
@@ -142,18 +154,22 @@ def quantize_mxfp8(w, stream=None):
     return codes, scales
 
 
-def sample(logits, uniforms, temperature=1.0, top_p=0.95, stream=None):
-    """fp32 device logits [rows, V] and uniforms [rows] -> int32 ids [rows] (temperature / top-p draw)."""
+def sample(logits, uniforms, temperature=1.0, top_p=0.95, stream=None, static_scratch=False, ids=None):
+    """fp32 device logits [rows, V] and uniforms [rows] -> int32 ids [rows] (temperature / top-p draw).
+    static_scratch=True calls dory_sample_static (no allocation inside the library); `ids` may be
+    a preallocated int32 device tensor [rows]."""
     import torch
     rows, vocab = logits.shape
     if logits.dtype != torch.float32 or uniforms.dtype != torch.float32 or not logits.is_contiguous():
         raise DoryError(DORY_E_INVALID, "sample needs contiguous fp32 logits and fp32 uniforms")
     if uniforms.numel() != rows or uniforms.device != logits.device:
         raise DoryError(DORY_E_INVALID, "one uniform per row, on the logits' device")
-    ids = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    if ids is None:
+        ids = torch.empty(rows, dtype=torch.int32, device=logits.device)
     st = stream if stream is not None else torch.cuda.current_stream(logits.device)
-    r = lib().dory_sample(_ptr(logits), int(rows), int(vocab), float(temperature), float(top_p),
-                          _ptr(uniforms.contiguous()), _ptr(ids), C.c_void_p(st.cuda_stream))
+    fn = lib().dory_sample_static if static_scratch else lib().dory_sample
+    r = fn(_ptr(logits), int(rows), int(vocab), float(temperature), float(top_p), _ptr(uniforms.contiguous()),
+           _ptr(ids), C.c_void_p(st.cuda_stream))
     if r != DORY_OK:
         raise DoryError(r, "dory_sample rejected its arguments")
     return ids
@@ -360,6 +376,13 @@ class Model:
             out[e.name.decode()] = {"launches": e.launches, "bytes": e.bytes, "flops": e.flops,
                                     "timed_launches": e.timed_launches, "ms": e.total_ms}
         return out
+
+    def spec_stats(self, reset: bool = False) -> dict:
+        """Counters of spec_decode since the last reset: rounds, drafted, accepted, produced,
+        draft_ms and verify_ms (GPU time of the two phases)."""
+        s = SpecStats()
+        self._check(lib().dory_get_spec_stats(self.ctx, C.byref(s), 1 if reset else 0), "dory_get_spec_stats")
+        return s.as_dict()
 
     def spec_decode(self, seq_id: int, last: int, n_new: int, gamma=4, k_draft=1, k_verify=4, reuse=False):
         """reuse=True (k_draft 1): the verify pass reuses the draft's input-stack output, loop-1

@@ -129,3 +129,36 @@ def test_sampled_decode_on_device_logits():
         tok = s
     say(f"[sample] mid decode, 8 sampled steps: {near} near-tie")
     assert near <= 1
+
+
+def test_tiny_temperature_draws_among_the_tied_maxima():
+    """T = 1e-40 (1/T overflows fp32): only the largest logit and its ties keep mass, shared
+    evenly; the device draws among them by u exactly as the oracle does."""
+    rng = np.random.default_rng(23)
+    v, rows = 32768, 64
+    l = rng.integers(-3, 4, (rows, v)).astype(np.float32)     # many ties at the maximum 3
+    us = rng.random(rows).astype(np.float32)
+    for p in (0.95, 1.0):
+        gid = run(l, us, 1e-40, p)
+        for r in range(rows):
+            assert gid[r] == sample_row(l[r].astype(np.float64), 1e-40, p, float(us[r])), (r, p)
+    say(f"[sample] T=1e-40: {rows} rows equal the oracle")
+
+
+def test_sampler_wide_batch_and_single_row():
+    """The chunked sampler at the row counts serving uses (1, 3, 128 rows) over the ~4B vocabulary,
+    against the oracle on every row."""
+    rng = np.random.default_rng(31)
+    v = 131072
+    for rows in (1, 3, 128):
+        l = (rng.standard_normal((rows, v)) * 2).astype(np.float32)
+        us = rng.random(rows).astype(np.float32)
+        gid = run(l, us, 1.0, 0.95)
+        near = 0
+        for r in range(rows):
+            oid = sample_row(l[r].astype(np.float64), 1.0, 0.95, float(us[r]))
+            if gid[r] != oid:
+                assert near_tie_ok(l[r].astype(np.float64), 1.0, 0.95, float(us[r]), gid[r])
+                near += 1
+        say(f"[sample] {rows} rows x {v}: {near} near-tie")
+        assert near <= 1

@@ -1,14 +1,15 @@
 """Decode-attention parity at the key-split depths the benchmark runs, against the oracle.
 
-The ~4B benchmark decodes at batch 1 with a 2560-token context: the split-key MFMA kernel then
-takes 20 splits per (row, KV head), and the split merge runs two groups (16 + 4). Batched decode
-of 128 ragged sequences and 131072-token contexts take up to 32 splits, on the VALU kernel
-(longest row first) and on the MFMA kernel respectively. A narrow bf16 model with the ~4B
+The ~4B benchmark decodes at batch 1 after a 2560-token prompt: the split-key MFMA kernel then
+takes 21..23 splits per (row, KV head) (128 keys per split), and the split merge runs two groups
+(16 + the rest). Batched decode of 128 ragged sequences and 131072-token contexts take up to 32
+splits, on the VALU kernel (longest row first) and on the MFMA kernel respectively. A narrow bf16 model with the ~4B
 attention geometry per KV head (128-wide heads, 3 query heads per KV head, scale sqrt(128)) and
 a window of 1000 (not a page multiple) reaches those depths at sizes the oracle computes in
 about a minute:
 
-  * batch 1 at 2560 and 4400 keys: 20 and 32 splits (MFMA kernel, both merge groups);
+  * batch 1 after 2560- and 4400-token prompts: 21 and 32 splits (MFMA kernel, both merge
+    groups);
   * 20 rows of 300..6000 keys decoded together: up to 24 splits (VALU kernel), ragged rows,
     empty trailing splits for the short rows, window edges inside pages.
 
@@ -91,14 +92,15 @@ def check_rows(tag, g_lg, g_ids, o_lg, o_ids, g_h=None, o_h=None):
         assert near_tie_ok(int(g_ids[i]), int(o_ids[i]), g_lg[i], o_lg[i]), (tag, i)
 
 
-def test_bs1_decode_20_and_32_splits(narrow):
-    """Batch-1 decode (split-key MFMA kernel) at 2560 keys (20 splits, merge groups 16 + 4) and
-    at 4400 keys (32 splits, two full merge groups), k = 2, last-loop, 3 teacher-forced steps."""
+def test_bs1_decode_21_and_32_splits(narrow):
+    """Batch-1 decode (split-key MFMA kernel) after a 2560-token prompt (2561..2563 keys: 21
+    splits, merge groups 16 + 5) and after a 4400-token prompt (32 splits, two full merge
+    groups), k = 2, last-loop, 3 teacher-forced steps."""
     w, prompt, om, hidden = narrow
     n_dec = 3
     m = dory.Model(NARROW3, w, kv_mode="last_loop", max_loops=K, max_seqs=2, max_model_len=4600, max_tokens=4400)
     m.set_loops(K)
-    for sid, (L, want_splits) in enumerate(((2560, 20), (4400, 32))):
+    for sid, (L, want_splits) in enumerate(((2560, 21), (4400, 32))):
         say(f"[narrow3 bf16] bs1 decode at {L} keys, expect {want_splits} splits")
         fork(om, 0, 10 + sid, L)
         o_lg0, o_id0 = om.lm_head(hidden[L - 1:L])

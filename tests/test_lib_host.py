@@ -191,6 +191,33 @@ def test_sample_argument_errors():
     assert lib.dory_sample(None, 0, 100, nan, 0.95, None, None, None) == dory.DORY_E_INVALID
     assert lib.dory_sample(None, 0, 100, 1.0, nan, None, None, None) == dory.DORY_E_INVALID
     assert lib.dory_sample(None, 0, 100, 1.0, 0.95, None, None, None) == dory.DORY_OK               # nothing to do
+    inf = float("inf")
+    assert lib.dory_sample(None, 0, 100, inf, 0.95, None, None, None) == dory.DORY_E_INVALID
+    assert lib.dory_sample(None, 0, 100, -inf, 0.95, None, None, None) == dory.DORY_E_INVALID
+    for fn in (lib.dory_sample_static,):
+        assert fn(None, -1, 100, 1.0, 0.95, None, None, None) == dory.DORY_E_INVALID
+        assert fn(None, 2, 100, 1.0, 0.95, None, None, None) == dory.DORY_E_INVALID      # NULL buffers
+        assert fn(None, 0, 100, inf, 0.95, None, None, None) == dory.DORY_E_INVALID
+        assert fn(None, 0, 100, 1.0, nan, None, None, None) == dory.DORY_E_INVALID
+        assert fn(None, 0, 100, 1.0, 0.95, None, None, None) == dory.DORY_OK
+
+
+def test_sample_scratch_sizes():
+    """Scratch per call: about 8.3 KB per row plus the chunk partials; every call of at most 256
+    rows fits the static 4 MiB array, and a larger one that does not is refused before any GPU work
+    (the NULL buffers would otherwise be the error)."""
+    lib = dory.lib()
+    assert lib.dory_sample_scratch_bytes(0, 100) == 0
+    assert lib.dory_sample_scratch_bytes(1, 0) == 0
+    one = lib.dory_sample_scratch_bytes(1, 131072)
+    assert 8256 <= one <= 16384
+    for rows in (1, 7, 128, 256):
+        for v in (1, 1000, 131072, 1 << 23):
+            assert lib.dory_sample_scratch_bytes(rows, v) <= 4 << 20
+    big = 1024
+    assert lib.dory_sample_scratch_bytes(big, 131072) > 4 << 20
+    dummy = 256   # non-NULL pointers: the size check must refuse before anything is launched
+    assert lib.dory_sample_static(dummy, big, 131072, 1.0, 0.95, dummy, dummy, None) == dory.DORY_E_INVALID
 
 
 def test_swa_recycling_pool_size_4b_long_context():

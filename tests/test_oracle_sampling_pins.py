@@ -101,3 +101,15 @@ def test_mass_reaching_top_p_exactly_is_enough():
     np.testing.assert_array_equal(nucleus(l, 1.0, 0.75), [False, True])
     assert all(sample_row(l, 1.0, 0.75, u) == 1 for u in [0.0, 0.2, 0.9])
     np.testing.assert_array_equal(nucleus(l, 1.0, 0.76), [True, True])
+
+
+def test_tiny_temperature_keeps_only_the_maximum_and_its_ties():
+    """A positive temperature so small that (l - max) / T overflows: every logit below the maximum
+    gets probability 0, and the tied maxima share the mass evenly (the T -> 0+ limit of the
+    softmax), so the draw picks among them by u in id order."""
+    l = np.array([0.5, 2.0, -1.0, 2.0, 1.999])
+    for u, want in ((0.0, 1), (0.49, 1), (0.5, 3), (0.99, 3)):
+        assert sample_row(l, 1e-40, 0.95, u) == want
+        assert sample_row(l, 1e-40, 1.0, u) == want
+    assert sample_row(l, 0.0, 0.95, 0.99) == 1      # T = 0 is greedy: the lowest tied id
+
