@@ -264,6 +264,8 @@ struct dory_ctx {
   // the running call: a chunk of consecutive positions of one sequence (prefill, resume), or -1
   int chunk_seq = -1, chunk_pos0 = -1;
   const int32_t* row_order = nullptr;  // device: batched decode rows, longest context first (this call only)
+  // the running call's rows are positions run_pos, run_pos + 1, ... of sequence run_seq (else -1)
+  int run_seq = -1, run_pos = -1;
   // last call
   int last_rows = 0;
   float* last_h = nullptr;
@@ -550,7 +552,7 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
     if (paged && (decode || !flash)) {
       ok(c, launch_attn_decode(qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), kv, c->page_el, M, H, Hk,
                                win, g.attn_scale, splits, fused_decode ? 1 : 0, c->W(c->L.o), c->W<float>(c->L.part_ml),
-                               c->W<float>(c->L.part_o), c->row_order, st));
+                               c->W<float>(c->L.part_o), c->row_order, c->run_seq, c->run_pos, st));
     } else if (flash) {
       ok(c, launch_attn_prefill(c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, win,
                                 g.attn_scale, c->W(c->L.o), st));
@@ -622,8 +624,26 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, con
     if (c->dry) { c->stats.kernel_launches++; return; }
     ok(c, launch_copy_f32(dst, src, (size_t)M * d, c->stream));
   };
+  // One launch per loop boundary: the pending sublayer step of the stack that just ended (if the
+  // last block left one), s_t = N(.) and u_{t+1} = N(s_t + x) (launch_loop_step).
+  auto loop_step = [&](Flow& fl, const float* xin, float* sout, float* hout, int mode) {
+    const double bytes = Md * d * ((fl.py ? 12 : 4) + (mode == 1 ? 12 : mode == 2 ? 8 : 4) + es) + (fl.py ? 4.0 * d : 0);
+    if (!c->dry) {
+      Span sp(c, R_LOOPN, bytes, 0);
+      ok(c, launch_loop_step(dt, fl.h, fl.py, fl.pa, xin, sout, hout, hb, M, d, mode, c->stream));
+    } else {
+      c->stats.kernel_launches++;
+    }
+    fl.py = fl.pa = nullptr;
+  };
   float* x;
   Flow f{b[0], b[3]};
+  float* rest[3];
+  auto split_rest = [&]() {
+    int nr = 0;
+    for (float* p : b)
+      if (p != x) rest[nr++] = p;
+  };
   if (o.phase != FwdOpts::RESUME) {
     if (!c->dry) {
       Span sp(c, R_EMBED, Md * d * (2 * es + 4) + Md * 4, 0);
@@ -632,40 +652,35 @@ void run_forward(dory_ctx* c, const int32_t* tokens_dev, int M, bool decode, con
       c->stats.kernel_launches++;
     }
     for (int j = 0; j < g.n_in; ++j) run_block(c, j, 1, M, f, decode, geo);
-    flush(c, f, M);
-    x = f.h;  // input-stack output
+    x = f.h;  // input-stack output (its last sublayer step may still be pending)
+    split_rest();
+    // x materialised in place; u_1 = N(s_0 + x) with s_0 = x
+    loop_step(f, nullptr, nullptr, rest[0], 0);
     if (o.cap_x) copy_rows(o.cap_x, x);
   } else {
     x = b[0];
     copy_rows(x, o.res_x);
+    split_rest();
   }
   // the other three buffers hold h, s and the spare
-  float* rest[3];
-  int nr = 0;
-  for (float* p : b)
-    if (p != x) rest[nr++] = p;
   float* s = rest[1];
   f = Flow{rest[0], rest[2]};
-  if (o.phase == FwdOpts::RESUME) copy_rows(s, o.res_s1);
+  if (o.phase == FwdOpts::RESUME) {
+    copy_rows(s, o.res_s1);
+    // u_2 = N(s_1 + x)
+    if (!c->dry) {
+      Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
+      ok(c, launch_norm_sum(dt, s, x, f.h, nullptr, hb, M, d, c->stream));
+    } else {
+      c->stats.kernel_launches++;
+    }
+  }
   const int t_first = o.phase == FwdOpts::RESUME ? 2 : 1;
   const int t_last = o.phase == FwdOpts::HEAD ? 1 : c->k;
   for (int t = t_first; t <= t_last; ++t) {
-    // u_t = N(s_{t-1} + x), with s_0 = x
-    if (!c->dry) {
-      Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
-      ok(c, launch_norm_sum(dt, t == 1 ? x : s, x, f.h, nullptr, hb, M, d, c->stream));
-    } else {
-      c->stats.kernel_launches++;
-    }
     for (int j = g.n_in; j < g.n_in + g.n_rec; ++j) run_block(c, j, t, M, f, decode, geo);
-    flush(c, f, M);
-    // s_t = N(F(u_t)); h continues as s_t
-    if (!c->dry) {
-      Span sp(c, R_LOOPN, Md * d * (12 + es), 0);
-      ok(c, launch_norm_sum(dt, f.h, nullptr, f.h, s, hb, M, d, c->stream));
-    } else {
-      c->stats.kernel_launches++;
-    }
+    // s_t = N(F(u_t)); then u_{t+1} = N(s_t + x), or h continues as s_k after the last loop
+    loop_step(f, x, s, f.h, t < t_last ? 1 : 2);
     if (t == 1 && o.cap_s1) copy_rows(o.cap_s1, s);
   }
   if (o.phase == FwdOpts::HEAD) {
@@ -809,10 +824,10 @@ dory_status prefill_impl(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, in
   s.append_run(s.len, k_run);
   Geom geo;
   geo.add_chunk(len, n, c->cfg.window);
-  c->chunk_seq = sid;
-  c->chunk_pos0 = len;
+  c->chunk_seq = c->run_seq = sid;
+  c->chunk_pos0 = c->run_pos = len;
   run_forward(c, tokens_dev, n, false, geo, o);
-  c->chunk_seq = c->chunk_pos0 = -1;
+  c->chunk_seq = c->chunk_pos0 = c->run_seq = c->run_pos = -1;
   if (!head) lm_head(c, n, logits_rows, logits_dev, ids_dev);
   c->stats.calls++;
   if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
@@ -877,8 +892,13 @@ dory_status decode_impl(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
     s.append_run(s.len, c->k);
   }
   c->row_order = ordered ? c->W<int32_t>(c->L.upload) + n_rows_ints + 2 * n_upd : nullptr;
+  if (n == 1) {  // one row: its sequence and position are passed to the attention kernel directly
+    c->run_seq = seq_ids[0];
+    c->run_pos = c->seqs[seq_ids[0]].len - 1;
+  }
   run_forward(c, tokens_dev, n, true, geo, o);
   c->row_order = nullptr;
+  c->run_seq = c->run_pos = -1;
   float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
   lm_head(c, n, n, logits, next_ids_dev);
   c->stats.calls++;
@@ -915,10 +935,10 @@ dory_status resume_impl(dory_ctx* c, int32_t sid, int32_t n, const float* res_x,
   o.phase = FwdOpts::RESUME;
   o.res_x = res_x;
   o.res_s1 = res_s1;
-  c->chunk_seq = sid;
-  c->chunk_pos0 = pos0;
+  c->chunk_seq = c->run_seq = sid;
+  c->chunk_pos0 = c->run_pos = pos0;
   run_forward(c, nullptr, n, false, geo, o);
-  c->chunk_seq = c->chunk_pos0 = -1;
+  c->chunk_seq = c->chunk_pos0 = c->run_seq = c->run_pos = -1;
   lm_head(c, n, n, logits_dev, ids_dev);
   c->stats.calls++;
   if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));

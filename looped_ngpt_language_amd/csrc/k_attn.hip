@@ -338,7 +338,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(
     const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
     const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window,
     float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
-    float* __restrict__ part_o) {
+    float* __restrict__ part_o, int2 run) {
   constexpr int DH = 128;
   __shared__ __attribute__((aligned(16))) bf16_t qs[G][DH];
   __shared__ float wm[4][G], wl[4][G];
@@ -346,7 +346,10 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   const int m = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = lane & 31, hh = lane >> 5;
-  const int seq = rows[2 * m], pos = rows[2 * m + 1];
+  // run.x >= 0: the rows are the consecutive positions run.y, run.y + 1, ... of sequence run.x
+  // (one decode row, or a short prefill chunk), known to the host, so the page-table loads do
+  // not wait for a load of the row list
+  const int seq = run.x >= 0 ? run.x : rows[2 * m], pos = run.x >= 0 ? run.y + m : rows[2 * m + 1];
   const int lo = window > 0 ? max(0, pos - window + 1) : 0;
   const int pf = lo >> 4, pl = pos >> 4;
   const int pps = (pl - pf + 1 + splits - 1) / splits;
@@ -1284,7 +1287,8 @@ bool attn_decode_supported(int dtype, int H, int Hkv, int dh) {
 hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                               const float2* rope, void* kv, size_t page_elems, int M, int H, int Hkv, int window,
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
-                              const int32_t* order, hipStream_t st) {
+                              const int32_t* order, int run_seq, int run_pos, hipStream_t st) {
+  const int2 run = make_int2(M <= kDecodeMfmaRows ? run_seq : -1, run_pos);
   dim3 grid(M, Hkv, splits);
 #define DORY_DEC(GV)                                                                                             \
   if (M > kDecodeMfmaRows && scale <= kFixedMaxScale)                                                          \
@@ -1296,7 +1300,7 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
                 page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o);           \
   else                                                                                                         \
     DORY_LAUNCH(k_attn_decode<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv,      \
-                page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o)
+                page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o, run)
   switch (H / Hkv) {
     case 1: DORY_DEC(1); break;
     case 2: DORY_DEC(2); break;

@@ -387,7 +387,7 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
   if (K % MF_BK != 0) return hipErrorNotSupported;
   // 32-bit byte offsets inside the tile kernels
   if ((size_t)M * K * 2 > 0xFFFFFFFFull || (size_t)N * K * 2 > 0xFFFFFFFFull) return hipErrorNotSupported;
-  if (M <= 2 && gemv_supported(K)) return launch_gemv(dual, A, B, nullptr, out, M, N, K, st);
+  if (M <= kGemvMaxRows && gemv_supported(K)) return launch_gemv(dual, A, B, nullptr, out, M, N, K, st);
   if (M <= 256 && split_ws) {
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {

@@ -1,4 +1,4 @@
-// Weight-streaming GEMV for decode (M <= 2 rows): C[M,N] = X[M,K] . W[N,K]^T
+// Weight-streaming GEMV for decode (M <= 8 rows): C[M,N] = X[M,K] . W[N,K]^T
 // with every weight byte read once. Epilogues as in the GEMM: fp32 store, or
 // the SwiGLU of the fused gate/up weight (z = silu(X.Wg^T) * (X.Wu^T), Wg = rows
 // 0..F-1 and Wu = rows F..2F-1 of W) stored as bf16.
@@ -50,7 +50,11 @@ int mx_scale_row_bytes(int K) {
 // of each weight row (KCH chunks per lane, K = 64 * EPC * KCH). The small loads
 // of the residual prologue (h, y, alpha) are issued before the weight stream, so
 // that the prologue's arithmetic and reductions run while the weights arrive
-// (loads complete in issue order).
+// (loads complete in issue order). Up to 2 input rows live in registers; with
+// MR > 2 (3..8 rows: a speculative verify chunk, a few decode rows) the M input
+// rows go global -> LDS directly (global_load_lds_dwordx4, no registers), in
+// flight together with the weight stream; each 16-byte input chunk read from LDS
+// then serves the wave's R rows.
 template <int KCH, int R, int MR, bool DUAL, bool RES, bool MX>
 __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, const void* __restrict__ Wv,
                                               const uint8_t* __restrict__ Sc, void* __restrict__ Y, int M, int N,
@@ -58,6 +62,8 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
                                               const float* __restrict__ ralpha, float* __restrict__ hout) {
   constexpr int EPC = MX ? 16 : 8;
   constexpr int K = KCH * 64 * EPC;
+  constexpr bool XL = MR > 2;                // input rows staged in LDS (bf16, no residual prologue)
+  static_assert(!XL || (!RES && !MX), "3..8 input rows: bf16 weights, no prologue");
   constexpr int RB = K * (MX ? 1 : 2);       // bytes per weight row
   constexpr int XU = EPC / 8;                // 16-byte x pieces per chunk
   constexpr int EPT = RES ? K / 256 : 1;     // prologue elements per thread
@@ -83,6 +89,7 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
       }
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight stream
   }
+  __shared__ __attribute__((aligned(16))) bf16_t xl[XL ? MR * K : 8];
   // Unconditional (the row index is clamped, so idle tail waves re-read the last
   // row): a branch here would make the in-order load counter wait for the weight
   // stream before the prologue.
@@ -113,7 +120,66 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
         }
       }
   }
-  uint4 xr[MR][KCH][XU];
+  if constexpr (XL) {
+    // The M input rows, 1 KB per wave instruction, dealt over the 4 waves. Issued from inline
+    // assembly with a memory clobber, after the weight loads: the compiler keeps those loads
+    // ahead of it, so both streams are in flight together. The wait is for every load the wave
+    // issued; the barrier then publishes every wave's share of the rows.
+    const int nblk = M * K * 2 / 1024;
+    const uint32_t lds0 = (uint32_t)(size_t)&xl[0];
+    for (int blk = tid >> 6; blk < nblk; blk += 4) lds_dma16(X, (uint32_t)blk * 1024 + lane * 16, lds0 + blk * 1024);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (!active) return;
+    float acc[NB][R][MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float sacc[NB][R];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < R; ++r) sacc[b][r] = 0.f;
+      if (m < M) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+          const uint4 x = *reinterpret_cast<const uint4*>(&xl[m * K + (c * 64 + lane) * 8]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const u32x4_t w = wr[b][r][c];
+              float t = sacc[b][r];
+              t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), t, false);
+              t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), t, false);
+              t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), t, false);
+              t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), t, false);
+              sacc[b][r] = t;
+            }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[b][r][m] = wave_sum(sacc[b][r]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int n = r0 + r;
+        if (n >= nrows_out) continue;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          if (m >= M) continue;
+          if (DUAL)
+            reinterpret_cast<bf16_t*>(Y)[(size_t)m * F + n] = f32_to_bf16(silu(acc[0][r][m]) * acc[NB - 1][r][m]);
+          else
+            reinterpret_cast<float*>(Y)[(size_t)m * N + n] = acc[0][r][m];
+        }
+      }
+    }
+    return;
+  }
+  uint4 xr[XL ? 1 : MR][KCH][XU];
   if constexpr (RES) {
     __shared__ __attribute__((aligned(16))) bf16_t xs[MR][K];
     __shared__ float red[4];
@@ -283,9 +349,26 @@ static hipError_t gemv_k(const bf16_t* X, const void* W, const uint8_t* Sc, void
   if (M == 1)
     DORY_LAUNCH((k_gemv<KCH, R, 1, DUAL, RES, MX>), grid, dim3(256), 0, st, X, W, Sc, Y, M, N, F, ra.h, ra.y,
                 ra.alpha, ra.hout);
-  else
+  else if (M == 2)
     DORY_LAUNCH((k_gemv<KCH, R, 2, DUAL, RES, MX>), grid, dim3(256), 0, st, X, W, Sc, Y, M, N, F, ra.h, ra.y,
                 ra.alpha, ra.hout);
+  else if constexpr (!RES && !MX) {
+    // 3..8 rows, staged in LDS (M rows of K bf16: at most 128 KB); two weight rows per wave, so
+    // each staged input chunk serves both
+    constexpr int R2 = 2;
+    const dim3 grid2((rows_out + 4 * R2 - 1) / (4 * R2));
+    if (M <= 4)
+      DORY_LAUNCH((k_gemv<KCH, R2, 4, DUAL, false, false>), grid2, dim3(256), 0, st, X, W, Sc, Y, M, N, F, ra.h,
+                  ra.y, ra.alpha, ra.hout);
+    else if (M == 5)
+      DORY_LAUNCH((k_gemv<KCH, R2, 5, DUAL, false, false>), grid2, dim3(256), 0, st, X, W, Sc, Y, M, N, F, ra.h,
+                  ra.y, ra.alpha, ra.hout);
+    else
+      DORY_LAUNCH((k_gemv<KCH, R2, 8, DUAL, false, false>), grid2, dim3(256), 0, st, X, W, Sc, Y, M, N, F, ra.h,
+                  ra.y, ra.alpha, ra.hout);
+  } else {
+    return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 
@@ -309,7 +392,7 @@ bool gemv_residual_supported(int K) { return K == 1024 || K == 3072 || K == 4096
 
 hipError_t launch_gemv(bool dual, const void* X, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
                        hipStream_t st) {
-  if (M < 1 || M > 2 || !gemv_supported(K)) return hipErrorNotSupported;
+  if (M < 1 || M > (scales ? 2 : kGemvMaxRows) || !gemv_supported(K)) return hipErrorNotSupported;
   const int F = dual ? N / 2 : 0;
   const ResArgs none{nullptr, nullptr, nullptr, nullptr};
   const bf16_t* x = (const bf16_t*)X;

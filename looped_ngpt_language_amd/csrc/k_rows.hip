@@ -155,6 +155,95 @@ __global__ void __launch_bounds__(ROW_THREADS) k_norm_sum(const float* a, const 
   }
 }
 
+// Loop boundary of the recurrent core in one pass over each row (onedev.kr summary
+// "Dory1.0-4B는 반복 횟수로 추론 연산과 정확도를 조절한다", section "어떻게 동작하나":
+// s_0 = x, u_t = N(s_{t-1} + x), s_t = N(F(u_t))). v is the row of h, first advanced by the
+// pending sublayer step N(v + alpha (N(y) - v)) when y != nullptr (that result is written back
+// to h). Then, by mode:
+//   LOOP_START (end of the input stack, h = x): u_1 = N(v + v) -> hout, hb;
+//   LOOP_NEXT  (end of loop t < k): s_t = N(v) -> s; u_{t+1} = N(s_t + x) -> hout, hb;
+//   LOOP_LAST  (end of loop k): s_k = N(v) -> s, hout, hb.
+// Each step is computed exactly as the separate residual and norm kernels compute it (same
+// reductions, same order), so results are bit-identical to launching them one after another.
+// hout may alias h (the row is read whole before anything is written).
+enum { LOOP_START = 0, LOOP_NEXT = 1, LOOP_LAST = 2 };
+template <typename T>
+__global__ void __launch_bounds__(ROW_THREADS) k_loop_step(float* h, const float* __restrict__ y,
+                                                           const float* __restrict__ alpha,
+                                                           const float* __restrict__ x, float* __restrict__ s,
+                                                           float* hout, T* __restrict__ hb, int d, int mode) {
+  __shared__ float red[ROW_THREADS / 64];
+  const size_t base = (size_t)blockIdx.x * d;
+  float hv[ROW_EPT];
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    hv[e] = i < d ? h[base + i] : 0.f;
+  }
+  if (y) {  // the pending sublayer step, as k_residual
+    float yv[ROW_EPT];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < ROW_EPT; ++e) {
+      const int i = threadIdx.x + e * ROW_THREADS;
+      yv[e] = i < d ? y[base + i] : 0.f;
+      ss += yv[e] * yv[e];
+    }
+    const float ry = rsqrtf(fmaxf(block_sum(ss, red, ROW_THREADS / 64), DORY_TINY_SS));
+    float st = 0.f;
+#pragma unroll
+    for (int e = 0; e < ROW_EPT; ++e) {
+      const int i = threadIdx.x + e * ROW_THREADS;
+      const float a = i < d ? alpha[i] : 0.f;
+      hv[e] = hv[e] + a * (yv[e] * ry - hv[e]);
+      st += hv[e] * hv[e];
+    }
+    const float rh = rsqrtf(fmaxf(block_sum(st, red, ROW_THREADS / 64), DORY_TINY_SS));
+#pragma unroll
+    for (int e = 0; e < ROW_EPT; ++e) hv[e] *= rh;
+    if (mode == LOOP_START) {
+#pragma unroll
+      for (int e = 0; e < ROW_EPT; ++e) {
+        const int i = threadIdx.x + e * ROW_THREADS;
+        if (i < d) h[base + i] = hv[e];
+      }
+    }
+  }
+  if (mode != LOOP_START) {  // s_t = N(v), as k_norm_sum with one operand
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < ROW_EPT; ++e) ss += hv[e] * hv[e];
+    const float r = rsqrtf(fmaxf(block_sum(ss, red, ROW_THREADS / 64), DORY_TINY_SS));
+#pragma unroll
+    for (int e = 0; e < ROW_EPT; ++e) {
+      const int i = threadIdx.x + e * ROW_THREADS;
+      hv[e] *= r;
+      if (i < d) s[base + i] = hv[e];
+    }
+  }
+  if (mode != LOOP_LAST) {  // u = N(a + b), as k_norm_sum with two operands
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < ROW_EPT; ++e) {
+      const int i = threadIdx.x + e * ROW_THREADS;
+      const float b = mode == LOOP_START ? hv[e] : (i < d ? x[base + i] : 0.f);
+      hv[e] = i < d ? hv[e] + b : 0.f;
+      ss += hv[e] * hv[e];
+    }
+    const float r = rsqrtf(fmaxf(block_sum(ss, red, ROW_THREADS / 64), DORY_TINY_SS));
+#pragma unroll
+    for (int e = 0; e < ROW_EPT; ++e) hv[e] *= r;
+  }
+#pragma unroll
+  for (int e = 0; e < ROW_EPT; ++e) {
+    const int i = threadIdx.x + e * ROW_THREADS;
+    if (i < d) {
+      hout[base + i] = hv[e];
+      St<T>::st(hb, base + i, hv[e]);
+    }
+  }
+}
+
 // ids[r] = argmax_j logits[r, j], lowest j on ties. Two passes: grid (rows,
 // ARGMAX_PARTS) workgroups each reduce a contiguous slice to (max, index), then
 // one workgroup per row reduces the slices. Ties keep the lower index.
@@ -261,6 +350,16 @@ hipError_t launch_residual(int dtype, float* h, const float* y, const float* alp
     DORY_LAUNCH(k_residual<float>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (float*)hb, d);
   else
     DORY_LAUNCH(k_residual<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, (bf16_t*)hb, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_loop_step(int dtype, float* h, const float* y, const float* alpha, const float* x, float* s,
+                            float* hout, void* hb, int M, int d, int mode, hipStream_t st) {
+  if (dtype == 0)
+    DORY_LAUNCH(k_loop_step<float>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, x, s, hout, (float*)hb, d, mode);
+  else
+    DORY_LAUNCH(k_loop_step<bf16_t>, dim3(M), dim3(ROW_THREADS), 0, st, h, y, alpha, x, s, hout, (bf16_t*)hb, d,
+                mode);
   return hipGetLastError();
 }
 

@@ -40,6 +40,12 @@ hipError_t launch_residual(int dtype, float* h, const float* y, const float* alp
                            hipStream_t st, int parts = 0);
 hipError_t launch_norm_sum(int dtype, const float* a, const float* b, float* h, float* s, void* hb, int M, int d,
                            hipStream_t st);
+// Loop boundary in one launch (k_rows.hip): optional pending residual step on h (y != nullptr),
+// then mode 0 (end of the input stack): u_1 = N(2 v) -> hout, the stepped v written back to h;
+// mode 1 (end of loop t < k): s_t = N(v) -> s, u_{t+1} = N(s_t + x) -> hout; mode 2 (end of
+// loop k): s_k = N(v) -> s and hout. hb gets the storage copy of hout. hout may alias h.
+hipError_t launch_loop_step(int dtype, float* h, const float* y, const float* alpha, const float* x, float* s,
+                            float* hout, void* hb, int M, int d, int mode, hipStream_t st);
 constexpr int kArgmaxParts = 64;  // partial (max, index) pairs per row in the argmax scratch
 hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, void* scratch, hipStream_t st);
 hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, hipStream_t st);
@@ -62,14 +68,17 @@ constexpr int kDecodeMfmaRows = 16;  // split-key attention: MFMA kernel up to t
 hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                               const float2* rope, void* kv, size_t page_elems, int M, int H, int Hkv, int window,
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
-                              const int32_t* order, hipStream_t st);
+                              const int32_t* order, int run_seq, int run_pos, hipStream_t st);
+// (run_seq >= 0: the M <= kDecodeMfmaRows rows are positions run_pos, run_pos + 1, ... of sequence
+// run_seq, so the kernel takes them from its arguments instead of loading the row list.)
 hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
                                hipStream_t st);
 
 bool gemv_supported(int K);
 bool gemv_residual_supported(int K);
-// GEMV for M <= 2 bf16 rows (k_gemv.hip). W is bf16 [N, K], or with `scales` != NULL
+constexpr int kGemvMaxRows = 8;
+// GEMV for M <= 8 bf16 rows (k_gemv.hip). W is bf16 [N, K], or with `scales` != NULL (M <= 2)
 // MXFP8 element codes [N, K] (uint8) with E8M0 block scales in the lane-major layout
 // (mx_scale_row_bytes(K) bytes per row, as written by launch_mx_quantize with lane_major).
 hipError_t launch_gemv(bool dual, const void* X, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
