@@ -170,9 +170,10 @@ class OracleModel:
     """
 
     def __init__(self, shape, weights, kv_mode: str = PER_LOOP, loops: int = 1, gemv_weights: str = "bf16"):
-        """gemv_weights = "mxfp8": calls that process at most 2 rows (decode of one or two
-        sequences, prefill chunks of one or two tokens) use the projection and LM-head weights
-        quantised to MXFP8 and dequantised (oracle.mx); other calls use the weights as given."""
+        """gemv_weights = "mxfp8" / "mxfp4": calls that process at most 2 rows (decode of one or
+        two sequences, prefill chunks of one or two tokens) use the projection and LM-head weights
+        quantised to MXFP8 / MXFP4 and dequantised (oracle.mx); other calls use the weights as
+        given."""
         self.s = shape
         self.bf16 = shape.dtype == "bf16"
         self.E = np.asarray(weights.embed, dtype=np.float64)
@@ -180,13 +181,16 @@ class OracleModel:
         self.blocks = []
         for blk in weights.blocks:
             self.blocks.append({k: np.asarray(v, dtype=np.float64) for k, v in blk.items()})
-        if gemv_weights not in ("bf16", "mxfp8"):
+        if gemv_weights not in ("bf16", "mxfp8", "mxfp4"):
             raise ValueError(gemv_weights)
-        self.mx = gemv_weights == "mxfp8"
+        self.mx = gemv_weights != "bf16"
         self.blocks_mx, self.Wlm_mx = [], None
         if self.mx:
-            from .mx import dequantize_mxfp8, quantize_mxfp8
-            dq = lambda w: dequantize_mxfp8(*quantize_mxfp8(w))  # noqa: E731
+            from .mx import dequantize_mxfp4, dequantize_mxfp8, quantize_mxfp4, quantize_mxfp8
+            if gemv_weights == "mxfp8":
+                dq = lambda w: dequantize_mxfp8(*quantize_mxfp8(w))  # noqa: E731
+            else:
+                dq = lambda w: dequantize_mxfp4(*quantize_mxfp4(w))  # noqa: E731
             for blk in self.blocks:
                 self.blocks_mx.append({k: (dq(v) if k.startswith("w") else v) for k, v in blk.items()})
             self.Wlm_mx = dq(self.Wlm)

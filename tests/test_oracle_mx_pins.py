@@ -75,3 +75,85 @@ def test_oracle_model_uses_mx_weights_only_for_calls_of_at_most_two_rows():
     d1, _ = mx.decode([0], [5])
     assert 0 < np.max(np.abs(d0 - d1)) < 0.5        # one row: quantised weights, close but different
     np.testing.assert_array_equal(mx.blocks_mx[0]["alpha_attn"], base.blocks[0]["alpha_attn"])
+
+
+# ---------------------------------------------------------------- MXFP4 (FP4 E2M1 elements)
+
+from oracle.mx import E2M1_TABLE, dequantize_mxfp4, quantize_mxfp4, round_e2m1  # noqa: E402
+
+
+def test_e2m1_table_closed_forms():
+    """FP4 E2M1 (OCP MX v1.0): bias 1, one mantissa bit; the eight magnitudes are
+    0, 0.5 (the subnormal), 1, 1.5, 2, 3, 4, 6; the sign bit mirrors them."""
+    np.testing.assert_array_equal(E2M1_TABLE[:8], [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    assert E2M1_TABLE[8] == 0.0 and np.signbit(E2M1_TABLE[8])
+    np.testing.assert_array_equal(E2M1_TABLE[8:], -E2M1_TABLE[:8])
+
+
+def test_e2m1_rounding_ties_and_saturation():
+    np.testing.assert_array_equal(round_e2m1(E2M1_TABLE[:8]), np.arange(8))
+    # midpoints, hand-derived: the even code (mantissa bit 0) wins
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    want = [0, 2, 2, 4, 4, 6, 6]     # 0, 1, 1, 2, 2, 4, 4
+    np.testing.assert_array_equal(round_e2m1(mids), want)
+    np.testing.assert_array_equal(round_e2m1([-m for m in mids]), [w | 0x8 for w in want])
+    np.testing.assert_array_equal(round_e2m1([0.26, 0.74, 2.51, 5.01]), [1, 1, 5, 7])
+    np.testing.assert_array_equal(round_e2m1([6.0, 7.0, 100.0, -1e9]), [7, 7, 7, 15])   # saturate at 6
+
+
+def test_mxfp4_scale_rule_hand_values():
+    rows = np.zeros((4, 32))
+    rows[0, :] = 1.0                  # max 1   -> X = 2^(0 - 2),  code 125; element 4 -> code 6
+    rows[1, 5] = 6.0                  # max 6   -> X = 2^(2 - 2),  code 127; element 6 -> code 7
+    rows[1, 6] = 0.2                  #             0.2 -> nearest of 0 / 0.5 is 0 -> code 0
+    rows[2, 0] = -0.3                 # max 0.3 -> X = 2^(-2 - 2), code 123; -0.3 / X = -4.8 -> -4 (code 0xE)
+    codes, sc = quantize_mxfp4(rows)  # row 3: all zero -> code 0, zero elements
+    np.testing.assert_array_equal(sc[:, 0], [125, 127, 123, 0])
+    assert np.all(codes[0] == 6)
+    assert codes[1, 5] == 7 and codes[1, 6] == 0 and codes[1, 0] == 0
+    assert codes[2, 0] == 0xE and codes[2, 1] == 0
+    assert np.all(codes[3] == 0)
+    deq = dequantize_mxfp4(codes, sc)
+    assert deq[0, 0] == 1.0 and deq[1, 5] == 6.0 and deq[2, 0] == -0.25
+
+
+def test_mxfp4_error_bound_and_idempotence():
+    """|v - dq(q(v))| <= half an E2M1 step at v's magnitude times X, except above the largest
+    element value 6, where the spec saturates (the block maximum over X lies in [4, 8), so the
+    top elements may lose up to 2 X): there the error is exactly (|v| / X - 6) X. Re-quantising
+    the dequantised values changes nothing."""
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((16, 256)) * np.exp(rng.uniform(-6, 6, (16, 1)))
+    codes, sc = quantize_mxfp4(w)
+    deq = dequantize_mxfp4(codes, sc)
+    X = np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+    q = np.abs(w) / X
+    step = np.select([q < 2, q < 4], [0.5, 1.0], 2.0)    # spacing of E2M1 values around q
+    inside = q <= 6.0
+    assert np.all(np.abs(w - deq)[inside] <= (0.5 * step * X)[inside] + 1e-300)
+    np.testing.assert_allclose(np.abs(w - deq)[~inside], ((q - 6.0) * X)[~inside], rtol=1e-12)
+    assert np.any(~inside)
+    c2, s2 = quantize_mxfp4(deq)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(s2, sc)
+
+
+def test_oracle_model_uses_mxfp4_weights_only_for_calls_of_at_most_two_rows():
+    """As for MXFP8: 12-row calls use the weights as given; one-row calls the MXFP4 copies, whose
+    logits differ more than MXFP8's (4-bit elements) but stay close."""
+    w = synth.make_weights(synth.TINY, seed=0)
+    base = OracleModel(synth.TINY, w, "per_loop", 2)
+    m8 = OracleModel(synth.TINY, w, "per_loop", 2, gemv_weights="mxfp8")
+    m4 = OracleModel(synth.TINY, w, "per_loop", 2, gemv_weights="mxfp4")
+    prompt = synth.prompt_tokens(synth.TINY, 12)
+    l0, _ = base.prefill(0, prompt, 3)
+    m8.prefill(0, prompt, 3)
+    l4, _ = m4.prefill(0, prompt, 3)
+    np.testing.assert_array_equal(l0, l4)
+    d0, _ = base.decode([0], [5])
+    d8, _ = m8.decode([0], [5])
+    d4, _ = m4.decode([0], [5])
+    e8, e4 = np.max(np.abs(d0 - d8)), np.max(np.abs(d0 - d4))
+    assert 0 < e8 < e4 < 0.5
+    q, sc = quantize_mxfp4(w.blocks[0]["wq"])
+    np.testing.assert_array_equal(m4.blocks_mx[0]["wq"], dequantize_mxfp4(q, sc))
