@@ -269,15 +269,17 @@ def main():
                                for k in loops}
     m.set_kv_mode("last_loop")
     if not args.no_mx:
-        # the same steps streaming MXFP8 copies of the weights (OCP MX, E4M3 + E8M0 per 32)
-        mm = dory.Model(shape, None, kv_mode="last_loop", max_loops=4, max_seqs=1, max_model_len=max_len,
-                        max_tokens=max(args.prompt, args.prefill_len), device="cuda:0", share_weights_from=m,
-                        gemv_weights="mxfp8")
-        log(f"[bench] MXFP8 context: workspace {mm.ws_bytes / 2**30:.2f} GiB")
-        res["decode_mx"] = {k: decode_run(mm, k, "last_loop", ptoks, min(args.steps, 100), args.warmup, "mxfp8")
-                            for k in loops}
-        mm.close()
-        del mm
+        # the same steps streaming MXFP8 / MXFP4 copies of the weights (OCP MX: E4M3 or E2M1
+        # elements, E8M0 scale per 32)
+        for fmt in ("mxfp8", "mxfp4"):
+            mm = dory.Model(shape, None, kv_mode="last_loop", max_loops=4, max_seqs=1, max_model_len=max_len,
+                            max_tokens=max(args.prompt, args.prefill_len), device="cuda:0", share_weights_from=m,
+                            gemv_weights=fmt)
+            log(f"[bench] {fmt} context: workspace {mm.ws_bytes / 2**30:.2f} GiB")
+            res[f"decode_{fmt}"] = {k: decode_run(mm, k, "last_loop", ptoks, min(args.steps, 100), args.warmup, fmt)
+                                    for k in loops}
+            mm.close()
+            del mm
 
     if not args.no_sampling:
         res["sampling"] = bench_sampling(shape)
@@ -316,7 +318,8 @@ def main():
         "decode_bs1": {str(k): short(v) for k, v in res["decode"].items()},
         "decode_bs1_per_loop": {str(k): short(v) for k, v in res.get("decode_per_loop", {}).items()},
         "decode_bs1_128_prompt_1024_steps": {str(k): short(v) for k, v in res.get("decode_short", {}).items()},
-        "decode_bs1_mxfp8": {str(k): short(v) for k, v in res.get("decode_mx", {}).items()},
+        "decode_bs1_mxfp8": {str(k): short(v) for k, v in res.get("decode_mxfp8", {}).items()},
+        "decode_bs1_mxfp4": {str(k): short(v) for k, v in res.get("decode_mxfp4", {}).items()},
         "prefill": {str(k): {"tokens": v["tokens"], "tok_s": round(v["tok_s"], 1), "ms": round(v["ms"], 3),
                              "tflop_s": round(v["tflop_s"], 1), "mfma_frac": round(v["mfma_frac"], 4)}
                     for k, v in res["prefill"].items()},

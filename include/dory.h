@@ -70,6 +70,15 @@ typedef enum { DORY_F32 = 0, DORY_BF16 = 1 } dory_dtype_t;
  * with d_model, n_heads*head_dim and d_ff in {1024, 3072, 4096, 8192}. The
  * workspace grows by about 1.03 bytes per weight (dory_query_sizes). */
 #define DORY_FLAG_MXFP8_GEMV 4u
+/* Context flag: as DORY_FLAG_MXFP8_GEMV with MXFP4 copies (OCP Microscaling
+ * Formats v1.0: FP4 E2M1 elements, two per byte, one E8M0 scale per 32
+ * consecutive elements of a row, by the rule of dory_quantize_mxfp4): about a
+ * quarter of the bf16 weight bytes per decode step (lucasainews article "NVIDIA,
+ * 루프 구조 4B 모델 Dory1.0-4B 4가지 정밀도로 공개", section "학습 방식과 변형",
+ * names 4-bit weights among the released formats). Excludes
+ * DORY_FLAG_MXFP8_GEMV; same shape conditions; the workspace grows by about
+ * 0.53 bytes per weight. */
+#define DORY_FLAG_MXFP4_GEMV 16u
 /* Context flag: sliding-window page recycling. A sliding-window layer reads
  * only the last `window` keys (trawling.dev digest "NVIDIA, 반복 연산형 4B
  * 언어 모델 Dory 공개", section "Reddit 반응", on the hybrid attention's cache
@@ -270,6 +279,18 @@ dory_status dory_sample_static(const float* logits_dev, int32_t rows, int32_t vo
  * sign kept) to codes_dev [rows, cols] (16-byte aligned). Enqueued on `stream`
  * (a hipStream_t, NULL = default stream); caller-owned buffers. */
 dory_status dory_quantize_mxfp8(const void* src_dev, int64_t rows, int32_t cols, void* codes_dev, void* scales_dev,
+                                void* stream);
+
+/* MXFP4 quantisation (OCP Microscaling Formats v1.0, MXFP4 with FP4 E2M1
+ * elements) of a bf16 matrix src_dev [rows, cols] (device, row-major, 16-byte
+ * aligned, cols % 32 == 0): per 32 consecutive elements of a row, the E8M0
+ * scale code e + 127 with e = floor(log2(max |v|)) - 2 clamped to [-127, 127]
+ * (-127 for an all-zero block) goes to scales_dev [rows, cols/32], and each
+ * element's E2M1 code (v / 2^e rounded to the nearest of 0, 0.5, 1, 1.5, 2, 3,
+ * 4, 6 with ties to the even code, magnitudes above 6 saturating to 6, sign
+ * kept) to codes_dev [rows, cols/2] (16-byte aligned), two codes per byte with
+ * element 2i in the low nibble. Enqueued on `stream`; caller-owned buffers. */
+dory_status dory_quantize_mxfp4(const void* src_dev, int64_t rows, int32_t cols, void* codes_dev, void* scales_dev,
                                 void* stream);
 
 /* Device-side error flags raised since the last reset (synchronises the

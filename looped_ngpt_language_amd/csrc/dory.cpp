@@ -95,7 +95,7 @@ Layout make_layout(const dory_config& c) {
   L.spec_s1 = take((size_t)(kMaxGamma + 1) * d * 4);
   // MXFP8 copies of every projection and of the LM head (codes, then scales per matrix)
   L.mx_bytes = 0;
-  if (c.flags & DORY_FLAG_MXFP8_GEMV) {
+  if (c.flags & (DORY_FLAG_MXFP8_GEMV | DORY_FLAG_MXFP4_GEMV)) {
     const size_t nb = (size_t)(c.n_in + c.n_rec + c.n_out);
     const size_t hd = (size_t)c.n_heads * c.head_dim;
     const size_t block_params = (size_t)qkv_cols(c) * d + d * hd + 2 * (size_t)c.d_ff * d + d * (size_t)c.d_ff;
@@ -105,7 +105,8 @@ Layout make_layout(const dory_config& c) {
     const size_t block_scales = (size_t)qkv_cols(c) * srb(d) + d * srb((int)hd) + 2 * (size_t)c.d_ff * srb(d) +
                                 d * srb(c.d_ff);
     const size_t scales = nb * block_scales + (size_t)c.vocab * srb(d);
-    L.mx_bytes = params + scales + 16 * kAlign * (4 * nb + 1);
+    const size_t codes = (c.flags & DORY_FLAG_MXFP4_GEMV) ? params / 2 : params;  // MXFP4: two codes per byte
+    L.mx_bytes = codes + scales + 16 * kAlign * (4 * nb + 1);
   }
   L.mx = take(L.mx_bytes);
   L.total = off;
@@ -173,11 +174,13 @@ std::string check_config(const dory_config* c) {
     if (c->d_model % 64 || c->d_ff % 64 || hd % 64) return "bf16 model: d_model, d_ff and n_heads*head_dim must be multiples of 64";
   }
   if (!(c->rope_theta > 0.f) || !(c->attn_scale > 0.f)) return "rope_theta and attn_scale must be positive";
-  if (c->flags & DORY_FLAG_MXFP8_GEMV) {
-    if (c->dtype != DORY_BF16) return "MXFP8 weights need the bf16 model";
+  if ((c->flags & DORY_FLAG_MXFP8_GEMV) && (c->flags & DORY_FLAG_MXFP4_GEMV))
+    return "DORY_FLAG_MXFP8_GEMV and DORY_FLAG_MXFP4_GEMV exclude each other";
+  if (c->flags & (DORY_FLAG_MXFP8_GEMV | DORY_FLAG_MXFP4_GEMV)) {
+    if (c->dtype != DORY_BF16) return "MX weights need the bf16 model";
     if (!dory::gemv_supported(c->d_model) || !dory::gemv_supported(c->n_heads * c->head_dim) ||
         !dory::gemv_supported(c->d_ff))
-      return "MXFP8 weights need d_model, n_heads*head_dim and d_ff in {1024, 3072, 4096, 8192}";
+      return "MX weights need d_model, n_heads*head_dim and d_ff in {1024, 3072, 4096, 8192}";
   }
   return "";
 }
@@ -246,8 +249,9 @@ struct dory_ctx {
   const void* lm = nullptr;
   std::vector<const void*> wqkv, wo, wgu, wd;
   std::vector<const float*> aa, am;
-  // MXFP8 copies (workspace) used by the weight-streaming GEMV (calls of <= 2 rows)
+  // MXFP8 / MXFP4 copies (workspace) used by the weight-streaming GEMV (calls of <= 2 rows)
   bool mx = false;
+  int mx_fmt = 0;  // 1: MXFP8, 2: MXFP4
   struct MxMat { const void* codes = nullptr; const uint8_t* scales = nullptr; };
   std::vector<MxMat> mqkv, mo, mgu, md;
   MxMat mlm;
@@ -481,7 +485,10 @@ bool fused_residual_ok(const dory_ctx* c, int M, bool decode) {
 }
 
 // Weight bytes per parameter a launch streams: MXFP8 (1 + 1/32) on the GEMV path, else the storage size.
-double wbytes(const dory_ctx* c, int M) { return c->mx && M <= 2 ? 1.0 + 1.0 / 32 : (double)esize(c->cfg); }
+double wbytes(const dory_ctx* c, int M) {
+  if (c->mx && M <= 2) return (c->mx_fmt == 2 ? 0.5 : 1.0) + 1.0 / 32;
+  return (double)esize(c->cfg);
+}
 
 // C = A . W^T through the MXFP8 GEMV (calls of <= 2 rows when the context holds MX weights) or launch_gemm.
 // parts (may be NULL): as in launch_gemm, the split-K partials may be left in the split workspace.
@@ -489,7 +496,7 @@ hipError_t project(dory_ctx* c, bool dual, const void* A, const void* W, const d
                    int N, int K, int* parts = nullptr) {
   if (parts) *parts = 0;
   if (c->mx && M <= 2 && dory::gemv_supported(K))
-    return dory::launch_gemv(dual, A, mx.codes, mx.scales, out, M, N, K, c->stream);
+    return dory::launch_gemv(dual, A, mx.codes, mx.scales, out, M, N, K, c->stream, c->mx_fmt);
   return dory::launch_gemm(c->cfg.dtype, dual, A, W, out, M, N, K, SPLITK, c->stream, parts);
 }
 
@@ -527,11 +534,11 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   char* kv = slot_base(c, j, t);
   hipStream_t st = c->stream;
   const double wb = wbytes(c, M);
-  const bool gmx = c->mx && M <= 2;  // this call streams the MXFP8 weights
+  const bool gmx = c->mx && M <= 2;  // this call streams the MX weights
   if (f.py && fres) {
     Span sp(c, R_QKV, (double)nq * d * wb + Md * d * 12 + 4.0 * d + Md * nq * 4, 2.0 * Md * nq * d);
     ok(c, launch_gemv_residual(false, gmx ? c->mqkv[j].codes : c->wqkv[j], gmx ? c->mqkv[j].scales : nullptr, qkv, M,
-                               nq, d, f.h, f.py, f.pa, f.spare, st));
+                               nq, d, f.h, f.py, f.pa, f.spare, st, c->mx_fmt));
     std::swap(f.h, f.spare);
     f.py = f.pa = nullptr;
   } else {
@@ -574,7 +581,7 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   if (fres) {
     Span sp(c, R_GU, 2.0 * F * d * wb + Md * d * 12 + 4.0 * d + Md * F * es, 2.0 * Md * 2 * F * d);
     ok(c, launch_gemv_residual(true, gmx ? c->mgu[j].codes : c->wgu[j], gmx ? c->mgu[j].scales : nullptr,
-                               c->W(c->L.z), M, 2 * F, d, f.h, y, c->aa[j], f.spare, st));
+                               c->W(c->L.z), M, 2 * F, d, f.h, y, c->aa[j], f.spare, st, c->mx_fmt));
     std::swap(f.h, f.spare);
   } else {
     {
@@ -899,8 +906,10 @@ dory_status decode_impl(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
   run_forward(c, tokens_dev, n, true, geo, o);
   c->row_order = nullptr;
   c->run_seq = c->run_pos = -1;
-  float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
-  lm_head(c, n, n, logits, next_ids_dev);
+  if (o.phase != FwdOpts::HEAD) {  // HEAD: input stack and loop 1 only, no logits
+    float* logits = logits_dev ? logits_dev : c->W<float>(c->L.logits);
+    lm_head(c, n, n, logits, next_ids_dev);
+  }
   c->stats.calls++;
   if (c->herr != hipSuccess) return fail(c, DORY_E_HIP, "kernel launch failed: %s", hipGetErrorString(c->herr));
   return DORY_OK;
@@ -1008,7 +1017,8 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t k
   c->cfg = *cfg;
   c->L = L;
   c->dry = dry;
-  c->mx = (cfg->flags & DORY_FLAG_MXFP8_GEMV) != 0;
+  c->mx = (cfg->flags & (DORY_FLAG_MXFP8_GEMV | DORY_FLAG_MXFP4_GEMV)) != 0;
+  c->mx_fmt = (cfg->flags & DORY_FLAG_MXFP4_GEMV) ? 2 : c->mx ? 1 : 0;
   c->kv_mode = kv_mode;
   c->n_blocks = nb;
   c->pool = static_cast<char*>(kv_pool);
@@ -1044,19 +1054,19 @@ dory_status dory_create(const dory_config* cfg, const dory_weights* w, int32_t k
     // unwritten cache slots hold zeros, never NaN bit patterns, so masked keys contribute 0 * v = 0
     if (e == hipSuccess) e = hipMemsetAsync(c->pool, 0, c->pool_bytes, c->stream);
     if (e == hipSuccess && c->mx) {
-      // quantise every projection and the LM head into the workspace's MXFP8 area
+      // quantise every projection and the LM head into the workspace's MX area
       char* p = c->W(L.mx);
       auto quant = [&](const void* src, size_t rows, int cols) -> dory_ctx::MxMat {
         dory_ctx::MxMat m;
         m.codes = p;
-        p += align_up(rows * cols);
+        p += align_up(c->mx_fmt == 2 ? rows * cols / 2 : rows * cols);
         m.scales = reinterpret_cast<const uint8_t*>(p);
         const size_t sbytes = rows * (size_t)dory::mx_scale_row_bytes(cols);
         p += align_up(sbytes);
         if (e == hipSuccess) e = hipMemsetAsync(const_cast<uint8_t*>(m.scales), 0, sbytes, c->stream);
         if (e == hipSuccess)
           e = dory::launch_mx_quantize(src, (long long)rows, cols, const_cast<void*>(m.codes),
-                                       const_cast<uint8_t*>(m.scales), true, c->stream);
+                                       const_cast<uint8_t*>(m.scales), true, c->stream, c->mx_fmt);
         return m;
       };
       const int d = cfg->d_model, hd = cfg->n_heads * cfg->head_dim, F = cfg->d_ff, nq = qkv_cols(*cfg);
@@ -1233,6 +1243,16 @@ dory_status dory_quantize_mxfp8(const void* src_dev, int64_t rows, int32_t cols,
   return e == hipSuccess ? DORY_OK : DORY_E_HIP;
 }
 
+dory_status dory_quantize_mxfp4(const void* src_dev, int64_t rows, int32_t cols, void* codes_dev, void* scales_dev,
+                                void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 || (rows > 0 && (!src_dev || !codes_dev || !scales_dev)))
+    return DORY_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(src_dev) % 16 || reinterpret_cast<uintptr_t>(codes_dev) % 16) return DORY_E_INVALID;
+  hipError_t e = dory::launch_mx_quantize(src_dev, rows, cols, codes_dev, scales_dev, false,
+                                          static_cast<hipStream_t>(stream), 2);
+  return e == hipSuccess ? DORY_OK : DORY_E_HIP;
+}
+
 dory_status dory_device_flags(dory_ctx* c, int32_t* flags, int32_t reset) {
   if (!c || !flags) return DORY_E_INVALID;
   *flags = 0;
@@ -1349,7 +1369,9 @@ dory_status dory_spec_decode(dory_ctx* c, int32_t sid, int32_t last, int32_t n_n
       o.phase = FwdOpts::HEAD;
       o.cap_x = sx + gamma * dm;
       o.cap_s1 = ss + gamma * dm;
-      if ((st = prefill_impl(c, sid, toks + gamma, 1, 1, nullptr, nullptr, o)) != DORY_OK) break;
+      // a one-token chunk is a decode step: the decode kernels (residual in the GEMV prologue,
+      // RoPE in the attention kernel) run it, at the draft's loop count 1
+      if ((st = decode_impl(c, 1, &sid, toks + gamma, nullptr, nullptr, o)) != DORY_OK) break;
       c->k = k_verify;
       if ((st = resume_impl(c, sid, gamma + 1, sx, ss, logits, vids)) != DORY_OK) break;
     } else {

@@ -323,43 +323,52 @@ DORY_DEV float bf16r(float v) { return bf16_to_f32(f32_to_bf16(v)); }
     }                                                                                                         \
   } while (0)
 
-// grid (rows, H_kv, splits), 256 threads. Each workgroup attends the G <= 4
-// query heads of KV head g for one row over a page-aligned share of the row's
-// keys, on MFMA: the G queries are columns of a 32-wide S^T = K . Q^T tile
-// (v_mfma_f32_32x32x16_bf16; the other columns are zero), and the tile's
-// probabilities feed O^T = V^T . P^T directly (same scheme as the prefill
-// kernel). Each wave takes 32-key blocks round-robin with the next block's
-// operands in flight. With write_kv the split holding the row's own position
-// first writes that position's k^ and v (decode: every row is the newest token
-// of its sequence; splits never share a page). With splits > 1 each workgroup
-// stores a partial (max, sum, unnormalised output) and k_attn_merge combines them.
-template <int G>
+// grid (row groups, H_kv, splits), 256 threads. Each workgroup attends the query heads of KV
+// head g for RW rows over a page-aligned share of the rows' keys, on MFMA: the queries are the
+// columns of a 32-wide S^T = K . Q^T tile (v_mfma_f32_32x32x16_bf16; unused columns are zero),
+// and the tile's probabilities feed O^T = V^T . P^T directly (same scheme as the prefill kernel).
+// C is the column capacity: C = G for one row per workgroup (rows of different sequences, or
+// one decode row); C = 32 for RW = floor(32 / G) consecutive positions of one sequence per
+// workgroup (run.x >= 0: a short prefill chunk, a speculative verify), which then read each key
+// once for all their queries, column r * G + gi masking keys past its own row's position.
+// Each wave takes 32-key blocks round-robin with the next block's operands in flight. With
+// write_kv (decode, C = G) the split holding the row's own position first writes that
+// position's k^ and v (every row is the newest token of its sequence; splits never share a
+// page). With splits > 1 each workgroup stores a partial (max, sum, unnormalised output) per
+// column and k_attn_merge combines them.
+template <int G, int C>
 __global__ void __launch_bounds__(256) k_attn_decode(
     const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
-    const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window,
-    float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
+    const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int M, int H, int Hkv,
+    int window, float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
     float* __restrict__ part_o, int2 run) {
   constexpr int DH = 128;
-  __shared__ __attribute__((aligned(16))) bf16_t qs[G][DH];
-  __shared__ float wm[4][G], wl[4][G];
-  __shared__ float wacc[4][G][DH];
-  const int m = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  constexpr int RWMAX = C / G;  // rows per workgroup at most
+  static_assert(C == G || C == 32, "column capacity");
+  __shared__ __attribute__((aligned(16))) bf16_t qs[C][DH];
+  __shared__ float wm[4][C], wl[4][C];
+  __shared__ float wacc[4][C][DH];
+  const int m0 = blockIdx.x * RWMAX, g = blockIdx.y, sp = blockIdx.z;
+  const int RW = min(RWMAX, M - m0);  // rows of this workgroup
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = lane & 31, hh = lane >> 5;
   // run.x >= 0: the rows are the consecutive positions run.y, run.y + 1, ... of sequence run.x
   // (one decode row, or a short prefill chunk), known to the host, so the page-table loads do
   // not wait for a load of the row list
-  const int seq = run.x >= 0 ? run.x : rows[2 * m], pos = run.x >= 0 ? run.y + m : rows[2 * m + 1];
-  const int lo = window > 0 ? max(0, pos - window + 1) : 0;
+  const int seq = run.x >= 0 ? run.x : rows[2 * m0];
+  const int pos_first = run.x >= 0 ? run.y + m0 : rows[2 * m0 + 1];
+  const int pos = pos_first + RW - 1;  // the workgroup's last row (C == G: its only row)
+  const int lo = window > 0 ? max(0, pos_first - window + 1) : 0;
   const int pf = lo >> 4, pl = pos >> 4;
+  // this lane's column: row r_c = qi / G of the group (rows past RW repeat the last one)
+  const int pos_c = pos_first + min(qi / G, RW - 1);
+  const int lo_c = window > 0 ? max(0, pos_c - window + 1) : 0;
   const int pps = (pl - pf + 1 + splits - 1) / splits;
   const int sp_first = pf + sp * pps;
   const int sp_last = min(pl, sp_first + pps - 1);
-  const float* src = qkv + (size_t)m * (size_t)((H + 2 * Hkv) * DH);
   const int32_t* prow = ptab + (size_t)seq * max_pages;
   const size_t vbase = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16;
-  const float2 cs = rope[(size_t)pos * 64 + lane];
-  const bool writer = write_kv && sp_first <= pl && pl <= sp_last;
+  const bool writer = C == G && write_kv && sp_first <= pl && pl <= sp_last;
   const int npair = sp_last >= sp_first ? (sp_last - sp_first + 2) / 2 : 0;
   const int nw = npair > wv ? (npair - wv + 3) / 4 : 0;  // blocks of this wave: pairs wv, wv+4, ...
   bf16x8_t kA[8], vA[8], kB[8], vB[8];
@@ -379,17 +388,21 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   // writer split fetches after writing the new key/value)
   if (!writer && nw > 0) DORY_DEC_FETCH(kA, vA, 0);
 
-  // queries of the group: q^ = N(RoPE(q)) in bf16
-  for (int gi = wv; gi < G; gi += 4) {
-    const float* x = src + (size_t)(g * G + gi) * DH;
+  // queries of the group: q^ = N(RoPE(q)) in bf16, column r * G + gi
+  for (int col = wv; col < RW * G; col += 4) {
+    const int r = col / G, gi = col % G;
+    const float2 cs = rope[(size_t)(pos_first + r) * 64 + lane];
+    const float* x = qkv + (size_t)(m0 + r) * (size_t)((H + 2 * Hkv) * DH) + (size_t)(g * G + gi) * DH;
     const float x1 = x[lane], x2 = x[lane + 64];
     const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
-    const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
-    qs[gi][lane] = f32_to_bf16(a0 * r);
-    qs[gi][lane + 64] = f32_to_bf16(a1 * r);
+    const float rn = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    qs[col][lane] = f32_to_bf16(a0 * rn);
+    qs[col][lane + 64] = f32_to_bf16(a1 * rn);
   }
   // the split holding the row's own position writes its key/value first
   if (writer && wv < 2) {
+    const float* src = qkv + (size_t)m0 * (size_t)((H + 2 * Hkv) * DH);
+    const float2 cs = rope[(size_t)pos * 64 + lane];
     bf16_t* pg = kv_slot + (size_t)prow[pl] * page_elems;
     const int tok = pos & 15;
     if (wv == 0) {
@@ -409,10 +422,11 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   }
   __syncthreads();
 
+  const int ncol = RW * G;
   bf16x8_t qb[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    if (qi < G) qb[ks] = *reinterpret_cast<const bf16x8_t*>(&qs[qi < G ? qi : 0][16 * ks + 8 * hh]);
+    if (qi < ncol) qb[ks] = *reinterpret_cast<const bf16x8_t*>(&qs[qi < ncol ? qi : 0][16 * ks + 8 * hh]);
     else
 #pragma unroll
       for (int e = 0; e < 8; ++e) qb[ks][e] = (__bf16)0.f;
@@ -449,7 +463,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int kp = 16 * p0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-      const bool ok = kp >= lo && kp <= pos && (kp >> 4) <= sp_last;
+      const bool ok = kp >= lo_c && kp <= pos_c && (kp >> 4) <= sp_last;
       sv[v] = ok ? st[v] * scale : -INFINITY;
       mb = fmaxf(mb, sv[v]);
     }
@@ -484,8 +498,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(
     prefetch(kA, vA, it + 2);
     block(kB, vB, it + 1);
   }
-  // waves -> LDS: lanes of query qi < G hold O[qi][32dt + 8(v/4) + 4hh + v%4]
-  if (qi < G) {
+  // waves -> LDS: lanes of column qi < ncol hold O[qi][32dt + 8(v/4) + 4hh + v%4]
+  if (qi < ncol) {
     if (hh == 0) { wm[wv][qi] = mrun; wl[wv][qi] = lrun; }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -493,25 +507,25 @@ __global__ void __launch_bounds__(256) k_attn_decode(
       for (int v = 0; v < 16; ++v) wacc[wv][qi][32 * dt + 8 * (v >> 2) + 4 * hh + (v & 3)] = acc[dt][v];
   }
   __syncthreads();
-  for (int idx = tid; idx < G * DH; idx += 256) {
-    const int gi = idx / DH, e = idx % DH;
-    float M = -INFINITY;
+  for (int idx = tid; idx < ncol * DH; idx += 256) {
+    const int col = idx / DH, e = idx % DH;
+    float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][gi]);
+    for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, wm[w][col]);
     float L = 0.f, A = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float cw = safe_scale(wm[w][gi], M);
-      L += wl[w][gi] * cw;
-      A += wacc[w][gi][e] * cw;
+      const float cw = safe_scale(wm[w][col], Mx);
+      L += wl[w][col] * cw;
+      A += wacc[w][col][e] * cw;
     }
-    const int hq = g * G + gi;
+    const int m = m0 + col / G, hq = g * G + col % G;
     if (splits == 1) {
       out[((size_t)m * H + hq) * DH + e] = f32_to_bf16(L > 0.f ? A / L : 0.f);
     } else {
       const size_t pi = ((size_t)m * H + hq) * splits + sp;
       part_o[pi * DH + e] = A;
-      if (e == 0) { part_ml[2 * pi] = M; part_ml[2 * pi + 1] = L; }
+      if (e == 0) { part_ml[2 * pi] = Mx; part_ml[2 * pi + 1] = L; }
     }
   }
 }
@@ -1289,6 +1303,9 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
                               const int32_t* order, int run_seq, int run_pos, hipStream_t st) {
   const int2 run = make_int2(M <= kDecodeMfmaRows ? run_seq : -1, run_pos);
+  // consecutive positions of one sequence whose keys are already in the cache (no key/value
+  // writes here): several rows per workgroup share every key load
+  const bool multi = run.x >= 0 && M > 1 && !write_kv;
   dim3 grid(M, Hkv, splits);
 #define DORY_DEC(GV)                                                                                             \
   if (M > kDecodeMfmaRows && scale <= kFixedMaxScale)                                                          \
@@ -1298,9 +1315,13 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
   else if (M > kDecodeMfmaRows)                                                                                \
     DORY_LAUNCH(k_attn_decode_valu<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv, \
                 page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o);           \
+  else if (multi)                                                                                              \
+    DORY_LAUNCH((k_attn_decode<GV, 32>), dim3((M + 32 / GV - 1) / (32 / GV), Hkv, splits), dim3(256), 0, st, qkv, \
+                rows, ptab, max_pages, rope, (bf16_t*)kv, page_elems, M, H, Hkv, window, scale, splits, write_kv,  \
+                (bf16_t*)out, part_ml, part_o, run);                                                            \
   else                                                                                                         \
-    DORY_LAUNCH(k_attn_decode<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv,      \
-                page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o, run)
+    DORY_LAUNCH((k_attn_decode<GV, GV>), grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv, \
+                page_elems, M, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o, run)
   switch (H / Hkv) {
     case 1: DORY_DEC(1); break;
     case 2: DORY_DEC(2); break;

@@ -15,12 +15,15 @@
 
 namespace dory {
 
-// Weights either bf16 [N, K] or (MX) MXFP8 [N, K] (OCP Microscaling Formats
-// v1.0: FP8 E4M3 element codes, one E8M0 scale 2^(code - 127) per 32 consecutive
-// elements of a row); an MX element pair is turned into the exact bf16 pair
-// value * scale by v_cvt_scalef32_pk_bf16_fp8 and fed to the same
-// v_dot2_f32_bf16 as the bf16 path, so MXFP8 halves the weight bytes.
-// A 16-byte lane chunk holds EPC = 8 (bf16) or 16 (MX) elements of a row.
+// Weights either bf16 [N, K] (MX = 0), MXFP8 [N, K] (MX = 1: OCP Microscaling
+// Formats v1.0, FP8 E4M3 element codes, one E8M0 scale 2^(code - 127) per 32
+// consecutive elements of a row) or MXFP4 [N, K / 2] (MX = 2: FP4 E2M1 element
+// codes, two per byte, element 2i in the low nibble, the same scales); an MX
+// element pair is turned into the exact bf16 pair value * scale by
+// v_cvt_scalef32_pk_bf16_fp8 / _fp4 and fed to the same v_dot2_f32_bf16 as the
+// bf16 path, so MXFP8 halves and MXFP4 quarters the weight bytes.
+// A lane chunk holds EPC = 8 (bf16, 16 bytes) or 16 (MXFP8: 16 bytes; MXFP4: 8
+// bytes) elements of a row.
 //
 // MX scales are stored lane-major: lane l's chunk c of a row covers scale block
 // j = 32 c + l / 2, and the row's scale bytes are laid out as [32][KCHP] (byte
@@ -55,7 +58,7 @@ int mx_scale_row_bytes(int K) {
 // rows go global -> LDS directly (global_load_lds_dwordx4, no registers), in
 // flight together with the weight stream; each 16-byte input chunk read from LDS
 // then serves the wave's R rows.
-template <int KCH, int R, int MR, bool DUAL, bool RES, bool MX>
+template <int KCH, int R, int MR, bool DUAL, bool RES, int MX>
 __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, const void* __restrict__ Wv,
                                               const uint8_t* __restrict__ Sc, void* __restrict__ Y, int M, int N,
                                               int F, const float* __restrict__ rh, const float* __restrict__ ry,
@@ -64,7 +67,8 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
   constexpr int K = KCH * 64 * EPC;
   constexpr bool XL = MR > 2;                // input rows staged in LDS (bf16, no residual prologue)
   static_assert(!XL || (!RES && !MX), "3..8 input rows: bf16 weights, no prologue");
-  constexpr int RB = K * (MX ? 1 : 2);       // bytes per weight row
+  constexpr int RB = MX == 2 ? K / 2 : MX ? K : 2 * K;   // bytes per weight row
+  constexpr int CB = MX == 2 ? 8 : 16;                     // bytes per lane chunk
   constexpr int XU = EPC / 8;                // 16-byte x pieces per chunk
   constexpr int EPT = RES ? K / 256 : 1;     // prologue elements per thread
   using SR = MxScaleRow<KCH>;
@@ -93,7 +97,8 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
   // Unconditional (the row index is clamped, so idle tail waves re-read the last
   // row): a branch here would make the in-order load counter wait for the weight
   // stream before the prologue.
-  u32x4_t wr[NB][R][KCH];
+  u32x4_t wr[NB][R][MX == 2 ? 1 : KCH];
+  uint2 wr4[NB][R][MX == 2 ? KCH : 1];
   uint32_t sw[NB][R][SR::WORDS];
   {
 #pragma unroll
@@ -101,9 +106,12 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int n = min(r0 + r, nrows_out - 1) + b * F;
-        const char* wp = W + (size_t)n * RB + (size_t)lane * 16;
+        const char* wp = W + (size_t)n * RB + (size_t)lane * CB;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) wr[b][r][c] = *reinterpret_cast<const u32x4_t*>(wp + c * 1024);
+        for (int c = 0; c < KCH; ++c) {
+          if constexpr (MX == 2) wr4[b][r][c] = *reinterpret_cast<const uint2*>(wp + c * 64 * CB);
+          else wr[b][r][c] = *reinterpret_cast<const u32x4_t*>(wp + c * 64 * CB);
+        }
         if constexpr (MX) {
           const uint8_t* sp = Sc + (size_t)n * SR::BYTES + (lane >> 1) * SR::P;
           if constexpr (SR::P == 8) {
@@ -237,8 +245,31 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
-          const u32x4_t w = wr[b][r][c];
-          if constexpr (MX) {
+          const u32x4_t w = wr[b][r][MX == 2 ? 0 : c];
+          if constexpr (MX == 2) {
+            // byte i of the chunk holds elements 2i (low nibble) and 2i + 1; x word k holds
+            // elements 2k, 2k + 1
+            const float scale = e8m0_to_f32((sw[b][r][c >> 2] >> (8 * (c & 3))) & 0xFFu);
+            const uint2 w4 = wr4[b][r][c];
+            const uint4 x0 = xr[m][c][0], x1 = xr[m][c][1];
+            const uint32_t xx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4.x, scale, 0);
+            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4.x, scale, 1);
+            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4.x, scale, 2);
+            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4.x, scale, 3);
+            const bf16x2_t p4 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4.y, scale, 0);
+            const bf16x2_t p5 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4.y, scale, 1);
+            const bf16x2_t p6 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4.y, scale, 2);
+            const bf16x2_t p7 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4.y, scale, 3);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p0, as_bf16x2(xx[0]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p1, as_bf16x2(xx[1]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p2, as_bf16x2(xx[2]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p3, as_bf16x2(xx[3]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p4, as_bf16x2(xx[4]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p5, as_bf16x2(xx[5]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p6, as_bf16x2(xx[6]), s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(p7, as_bf16x2(xx[7]), s, false);
+          } else if constexpr (MX) {
             // word j holds elements 4j .. 4j+3; x piece u holds elements 8u .. 8u+7
             const float scale = e8m0_to_f32((sw[b][r][c >> 2] >> (8 * (c & 3))) & 0xFFu);
             const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -285,6 +316,10 @@ __global__ void __launch_bounds__(256) k_gemv(const bf16_t* __restrict__ X, cons
 // step), magnitudes of 448 and above saturate to 448; the sign bit is kept.
 // With srb > 0 the scales are written lane-major (row stride srb bytes, see
 // above); srb = 0 gives the plain [rows, cols / 32] layout.
+// FMT = 2 (MXFP4): e = floor(log2 max|v|) - 2, each v / X rounded to FP4 E2M1 (0, 0.5, 1, 1.5,
+// 2, 3, 4, 6; nearest, ties to the even code, above 6 saturating to 6), two codes per byte
+// (element 2i in the low nibble), 16 bytes per block.
+template <int FMT>
 __global__ void __launch_bounds__(256) k_mx_quantize(const bf16_t* __restrict__ src, long long blocks, int nblk,
                                                      int srb, uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales) {
@@ -301,7 +336,7 @@ __global__ void __launch_bounds__(256) k_mx_quantize(const bf16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax_bits = max(amax_bits, max((u[i] << 16) & 0x7FFFFFFFu, u[i] & 0x7FFF0000u));
   const int ebits = (int)(amax_bits >> 23);
-  const int e = max(-127, min(127, (ebits ? ebits - 127 : -200) - 8));
+  const int e = max(-127, min(127, (ebits ? ebits - 127 : -200) - (FMT == 2 ? 2 : 8)));
   long long si = b;
   if (srb > 0) {
     const long long n = b / nblk;
@@ -309,6 +344,20 @@ __global__ void __launch_bounds__(256) k_mx_quantize(const bf16_t* __restrict__ 
     si = n * srb + (j & 31) * p + (j >> 5);
   }
   scales[si] = (uint8_t)(e + 127);
+  if constexpr (FMT == 2) {
+    uint32_t o4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t bits = (i & 1) ? (u[i >> 1] & 0xFFFF0000u) : (u[i >> 1] << 16);
+      const float q = ldexpf(__uint_as_float(bits & 0x7FFFFFFFu), -e);  // exact: power-of-two scaling
+      // midpoints between neighbours: a tie goes to the even code (mantissa bit 0)
+      const uint32_t mag = q <= 0.25f ? 0u : q < 0.75f ? 1u : q <= 1.25f ? 2u : q < 1.75f ? 3u
+                         : q <= 2.5f ? 4u : q < 3.5f ? 5u : q <= 5.f ? 6u : 7u;
+      o4[i >> 3] |= ((bits >> 31) << 3 | mag) << (4 * (i & 7));
+    }
+    *reinterpret_cast<uint4*>(codes + b * 16) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    return;
+  }
   uint32_t out[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = 0;
@@ -338,7 +387,7 @@ struct ResArgs {
   float* hout;
 };
 
-template <int KCH, bool DUAL, bool RES, bool MX>
+template <int KCH, bool DUAL, bool RES, int MX>
 static hipError_t gemv_k(const bf16_t* X, const void* W, const uint8_t* Sc, void* Y, int M, int N, int F,
                          const ResArgs& ra, hipStream_t st) {
   const int rows_out = DUAL ? F : N;
@@ -372,7 +421,7 @@ static hipError_t gemv_k(const bf16_t* X, const void* W, const uint8_t* Sc, void
   return hipGetLastError();
 }
 
-template <bool DUAL, bool RES, bool MX>
+template <bool DUAL, bool RES, int MX>
 static hipError_t gemv_dispatch(const bf16_t* X, const void* W, const uint8_t* Sc, void* Y, int M, int N, int K,
                                 int F, const ResArgs& ra, hipStream_t st) {
   constexpr int D = MX ? 1024 : 512;  // elements per lane chunk column (64 lanes x EPC)
@@ -391,39 +440,51 @@ bool gemv_supported(int K) { return K == 1024 || K == 3072 || K == 4096 || K == 
 bool gemv_residual_supported(int K) { return K == 1024 || K == 3072 || K == 4096; }
 
 hipError_t launch_gemv(bool dual, const void* X, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
-                       hipStream_t st) {
+                       hipStream_t st, int mx_fmt) {
   if (M < 1 || M > (scales ? 2 : kGemvMaxRows) || !gemv_supported(K)) return hipErrorNotSupported;
   const int F = dual ? N / 2 : 0;
   const ResArgs none{nullptr, nullptr, nullptr, nullptr};
   const bf16_t* x = (const bf16_t*)X;
+  if (scales && mx_fmt == 2)
+    return dual ? gemv_dispatch<true, false, 2>(x, W, scales, out, M, N, K, F, none, st)
+                : gemv_dispatch<false, false, 2>(x, W, scales, out, M, N, K, F, none, st);
   if (scales)
-    return dual ? gemv_dispatch<true, false, true>(x, W, scales, out, M, N, K, F, none, st)
-                : gemv_dispatch<false, false, true>(x, W, scales, out, M, N, K, F, none, st);
-  return dual ? gemv_dispatch<true, false, false>(x, W, nullptr, out, M, N, K, F, none, st)
-              : gemv_dispatch<false, false, false>(x, W, nullptr, out, M, N, K, F, none, st);
+    return dual ? gemv_dispatch<true, false, 1>(x, W, scales, out, M, N, K, F, none, st)
+                : gemv_dispatch<false, false, 1>(x, W, scales, out, M, N, K, F, none, st);
+  return dual ? gemv_dispatch<true, false, 0>(x, W, nullptr, out, M, N, K, F, none, st)
+              : gemv_dispatch<false, false, 0>(x, W, nullptr, out, M, N, K, F, none, st);
 }
 
 hipError_t launch_gemv_residual(bool dual, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
-                                const float* h, const float* y, const float* alpha, float* hout, hipStream_t st) {
+                                const float* h, const float* y, const float* alpha, float* hout, hipStream_t st,
+                                int mx_fmt) {
   if (M < 1 || M > 2 || !gemv_residual_supported(K)) return hipErrorNotSupported;
   const int F = dual ? N / 2 : 0;
   const ResArgs ra{h, y, alpha, hout};
+  if (scales && mx_fmt == 2)
+    return dual ? gemv_dispatch<true, true, 2>(nullptr, W, scales, out, M, N, K, F, ra, st)
+                : gemv_dispatch<false, true, 2>(nullptr, W, scales, out, M, N, K, F, ra, st);
   if (scales)
-    return dual ? gemv_dispatch<true, true, true>(nullptr, W, scales, out, M, N, K, F, ra, st)
-                : gemv_dispatch<false, true, true>(nullptr, W, scales, out, M, N, K, F, ra, st);
-  return dual ? gemv_dispatch<true, true, false>(nullptr, W, nullptr, out, M, N, K, F, ra, st)
-              : gemv_dispatch<false, true, false>(nullptr, W, nullptr, out, M, N, K, F, ra, st);
+    return dual ? gemv_dispatch<true, true, 1>(nullptr, W, scales, out, M, N, K, F, ra, st)
+                : gemv_dispatch<false, true, 1>(nullptr, W, scales, out, M, N, K, F, ra, st);
+  return dual ? gemv_dispatch<true, true, 0>(nullptr, W, nullptr, out, M, N, K, F, ra, st)
+              : gemv_dispatch<false, true, 0>(nullptr, W, nullptr, out, M, N, K, F, ra, st);
 }
 
 hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* codes, void* scales, bool lane_major,
-                              hipStream_t st) {
-  if (rows < 0 || cols <= 0 || cols % 32) return hipErrorInvalidValue;
+                              hipStream_t st, int fmt) {
+  if (rows < 0 || cols <= 0 || cols % 32 || (fmt != 1 && fmt != 2)) return hipErrorInvalidValue;
   const int srb = lane_major ? mx_scale_row_bytes(cols) : 0;
   if (lane_major && srb == 0) return hipErrorNotSupported;
   const long long blocks = rows * (cols / 32);
   if (blocks == 0) return hipSuccess;
-  DORY_LAUNCH(k_mx_quantize, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, st, (const bf16_t*)src, blocks,
-              cols / 32, srb, (uint8_t*)codes, (uint8_t*)scales);
+  const dim3 grid((unsigned)((blocks + 255) / 256));
+  if (fmt == 2)
+    DORY_LAUNCH(k_mx_quantize<2>, grid, dim3(256), 0, st, (const bf16_t*)src, blocks, cols / 32, srb, (uint8_t*)codes,
+                (uint8_t*)scales);
+  else
+    DORY_LAUNCH(k_mx_quantize<1>, grid, dim3(256), 0, st, (const bf16_t*)src, blocks, cols / 32, srb, (uint8_t*)codes,
+                (uint8_t*)scales);
   return hipGetLastError();
 }
 

@@ -81,16 +81,19 @@ constexpr int kGemvMaxRows = 8;
 // GEMV for M <= 8 bf16 rows (k_gemv.hip). W is bf16 [N, K], or with `scales` != NULL (M <= 2)
 // MXFP8 element codes [N, K] (uint8) with E8M0 block scales in the lane-major layout
 // (mx_scale_row_bytes(K) bytes per row, as written by launch_mx_quantize with lane_major).
+// mx_fmt (with scales): 1 = MXFP8 codes [N, K], 2 = MXFP4 codes [N, K / 2] (element 2i in the low nibble).
 hipError_t launch_gemv(bool dual, const void* X, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
-                       hipStream_t st);
+                       hipStream_t st, int mx_fmt = 1);
 // GEMV (M <= 2) whose input rows are N(h + alpha (N(y) - h)), computed in the prologue; the fp32
 // result is also written to hout (which must not alias h or y).
 hipError_t launch_gemv_residual(bool dual, const void* W, const uint8_t* scales, void* out, int M, int N, int K,
-                                const float* h, const float* y, const float* alpha, float* hout, hipStream_t st);
+                                const float* h, const float* y, const float* alpha, float* hout, hipStream_t st,
+                                int mx_fmt = 1);
 // bf16 [rows, cols] -> MXFP8 codes [rows, cols] + scales [rows, cols / 32] (cols % 32 == 0), or
 // with lane_major the GEMV's scale layout (rows * mx_scale_row_bytes(cols) bytes; padding untouched).
+// fmt 1: MXFP8 codes [rows, cols]; fmt 2: MXFP4 codes [rows, cols / 2] (element 2i in the low nibble).
 hipError_t launch_mx_quantize(const void* src, long long rows, int cols, void* codes, void* scales, bool lane_major,
-                              hipStream_t st);
+                              hipStream_t st, int fmt = 1);
 // bytes per weight row of the lane-major MXFP8 scale layout the GEMV reads (0: K unsupported)
 int mx_scale_row_bytes(int K);
 // Temperature / top-p draw per row of fp32 logits [rows, V] with the caller's uniforms [rows]

@@ -23,6 +23,7 @@ KV_MODES = {"per_loop": 0, "last_loop": 1}
 FLAG_DRY_RUN = 1
 FLAG_MXFP8_GEMV = 4
 FLAG_SWA_RECYCLE = 8
+FLAG_MXFP4_GEMV = 16
 
 
 class DoryError(RuntimeError):
@@ -86,6 +87,7 @@ EXPORTS = {
     "dory_last_hidden": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
     "dory_device_flags": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
     "dory_quantize_mxfp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dory_quantize_mxfp4": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dory_sample": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p, C.c_void_p,
                               C.c_void_p]),
     "dory_sample_static": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p,
@@ -120,7 +122,7 @@ def lib():
 
 def make_config(shape: synth.ModelShape, *, max_seqs=1, max_model_len=4096, max_loops=4, max_tokens=4096,
                 dry_run=False, gemv_weights="bf16", swa_recycle=False) -> Config:
-    if gemv_weights not in ("bf16", "mxfp8"):
+    if gemv_weights not in ("bf16", "mxfp8", "mxfp4"):
         raise ValueError(gemv_weights)
     return Config(d_model=shape.d_model, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
                   head_dim=shape.head_dim, d_ff=shape.d_ff, vocab=shape.vocab, n_in=shape.n_in, n_rec=shape.n_rec,
@@ -128,6 +130,7 @@ def make_config(shape: synth.ModelShape, *, max_seqs=1, max_model_len=4096, max_
                   dtype=0 if shape.dtype == synth.F32 else 1, page_size=shape.page_size, max_seqs=max_seqs,
                   max_model_len=max_model_len, max_loops=max_loops, max_tokens=max_tokens,
                   flags=(FLAG_DRY_RUN if dry_run else 0) | (FLAG_MXFP8_GEMV if gemv_weights == "mxfp8" else 0)
+                  | (FLAG_MXFP4_GEMV if gemv_weights == "mxfp4" else 0)
                   | (FLAG_SWA_RECYCLE if swa_recycle else 0),
                   rope_theta=shape.rope_theta, attn_scale=shape.scale)
 
@@ -151,6 +154,20 @@ def quantize_mxfp8(w, stream=None):
     r = lib().dory_quantize_mxfp8(_ptr(w), int(rows), int(cols), _ptr(codes), _ptr(scales), C.c_void_p(st.cuda_stream))
     if r != DORY_OK:
         raise DoryError(r, "dory_quantize_mxfp8 rejected its arguments")
+    return codes, scales
+
+
+def quantize_mxfp4(w, stream=None):
+    """bf16 device tensor [rows, cols] -> (codes uint8 [rows, cols/2], two per byte with element 2i in the
+    low nibble, scales uint8 [rows, cols/32]) on its device."""
+    import torch
+    rows, cols = w.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
+    st = stream if stream is not None else torch.cuda.current_stream(w.device)
+    r = lib().dory_quantize_mxfp4(_ptr(w), int(rows), int(cols), _ptr(codes), _ptr(scales), C.c_void_p(st.cuda_stream))
+    if r != DORY_OK:
+        raise DoryError(r, "dory_quantize_mxfp4 rejected its arguments")
     return codes, scales
 
 
@@ -193,7 +210,7 @@ class Model:
     def __init__(self, shape: synth.ModelShape, weights=None, *, kv_mode="per_loop", max_loops=4, max_seqs=1,
                  max_model_len=4096, max_tokens=None, kv_tokens=None, device="cuda:0", dry_run=False, stream=None,
                  share_weights_from=None, gemv_weights="bf16", swa_recycle=False):
-        """gemv_weights="mxfp8": calls of at most 2 rows stream MXFP8 copies of the weights.
+        """gemv_weights="mxfp8" / "mxfp4": calls of at most 2 rows stream MXFP8 / MXFP4 copies of the weights.
         swa_recycle: sliding-window layers keep only the pages their window (plus a 64-token
         rollback reserve) can reach; kv_tokens then sizes the full-attention pages."""
         self.shape = shape

@@ -173,6 +173,33 @@ def test_mxfp8_flag_sizes_and_validation():
         dory.query_sizes(dory.make_config(STACKS, dry_run=True, gemv_weights="mxfp8"), "per_loop", 64)
 
 
+def test_mxfp4_flag_sizes_and_validation():
+    """The MXFP4 flag adds ~0.53 bytes per weight (two codes per byte plus a scale per 32) and
+    cannot be combined with the MXFP8 flag."""
+    base = dory.make_config(synth.MID, dry_run=True)
+    mx4 = dory.make_config(synth.MID, dry_run=True, gemv_weights="mxfp4")
+    _, ws0 = dory.query_sizes(base, "per_loop", 4096)
+    _, ws1 = dory.query_sizes(mx4, "per_loop", 4096)
+    s = synth.MID
+    params = s.n_blocks * ((s.n_heads + 2 * s.n_kv_heads) * s.head_dim * s.d_model + s.d_model * s.n_heads * s.head_dim
+                           + 3 * s.d_ff * s.d_model) + s.vocab * s.d_model
+    assert params * 17 // 32 <= ws1 - ws0 <= params * 17 // 32 + (1 << 20)
+    both = dory.make_config(synth.MID, dry_run=True, gemv_weights="mxfp4")
+    both.flags |= dory.FLAG_MXFP8_GEMV
+    with pytest.raises(dory.DoryError):
+        dory.query_sizes(both, "per_loop", 64)
+    with pytest.raises(dory.DoryError):
+        dory.query_sizes(dory.make_config(synth.TINY, dry_run=True, gemv_weights="mxfp4"), "per_loop", 64)
+
+
+def test_quantize_mxfp4_argument_errors():
+    lib = dory.lib()
+    assert lib.dory_quantize_mxfp4(None, 4, 30, None, None, None) == dory.DORY_E_INVALID   # cols % 32
+    assert lib.dory_quantize_mxfp4(None, -1, 32, None, None, None) == dory.DORY_E_INVALID
+    assert lib.dory_quantize_mxfp4(None, 4, 32, None, None, None) == dory.DORY_E_INVALID    # NULL buffers
+    assert lib.dory_quantize_mxfp4(None, 0, 32, None, None, None) == dory.DORY_OK          # nothing to do
+
+
 def test_quantize_mxfp8_argument_errors():
     lib = dory.lib()
     assert lib.dory_quantize_mxfp8(None, 4, 30, None, None, None) == dory.DORY_E_INVALID   # cols % 32
