@@ -296,8 +296,31 @@ dory_status dory_quantize_mxfp4(const void* src_dev, int64_t rows, int32_t cols,
 /* Device-side error flags raised since the last reset (synchronises the
  * stream): bit 0 = a token id outside 0..V-1 reached the embedding (it was
  * clamped into range, so that call's outputs are not those of the given ids).
- * With reset != 0 the flags are cleared afterwards. */
+ * The checked build (dory_checked_build() == 1) also raises: bit 1 = a
+ * page-table read with a sequence or page index outside the table, bit 2 = a
+ * page id outside the pages of the cache region it indexes, bit 3 = a RoPE
+ * position outside 0..max_model_len-1; each offending read used index 0
+ * instead, so the access stayed inside its buffer but that call's outputs are
+ * meaningless. With reset != 0 the flags are cleared afterwards. */
 dory_status dory_device_flags(dory_ctx* ctx, int32_t* flags, int32_t reset);
+
+/* 1 for the checked (debug) build of this library, libdory_checked.so, whose
+ * attention kernels bounds-check every page-table entry, page id and RoPE row
+ * they read (see dory_device_flags) and whose host runtime checks that each
+ * layer slot's cache region lies inside the KV pool before its launches (else
+ * the call fails with DORY_E_HIP); 0 for the default build, which reads them
+ * as given. Both builds compute the same results on valid state. */
+int32_t dory_checked_build(void);
+
+/* Checked build only (else DORY_E_STATE): overwrite entry page_index of
+ * sequence seq_id's full-attention page table on the device with page_id and
+ * return the previous entry in *old_id (may be NULL). Synchronises the
+ * context's stream. A fault injection for testing the checked build's guards:
+ * the host's own record of the sequence's pages is not changed, so restore the
+ * entry before relying on the sequence's outputs again. DORY_E_INVALID:
+ * seq_id or page_index outside the table. */
+dory_status dory_debug_set_page(dory_ctx* ctx, int32_t seq_id, int32_t page_index, int32_t page_id,
+                                int32_t* old_id);
 
 /* Copy the final hidden states (output of the output stack, fp32 [rows, d]) of
  * the previous prefill/decode call's last `rows` rows to dst_dev. Enqueued. */

@@ -399,6 +399,21 @@ const int32_t* slot_ptab(dory_ctx* c, int j) {
   const int32_t* t = c->W<int32_t>(c->L.ptab);
   return (c->recycle && !full_block(c->cfg, j)) ? t + (size_t)c->cfg.max_seqs * c->L.max_pages : t;
 }
+// Entries of the page tables (the full-attention one, then the sliding-window one under recycling).
+int ptab_entries(const dory_ctx* c) {
+  return ((c->cfg.flags & DORY_FLAG_SWA_RECYCLE) ? 2 : 1) * c->cfg.max_seqs * c->L.max_pages;
+}
+
+// Index guard of block j's attention kernels: its page table's shape, the pages of the cache
+// region its ids index, the RoPE table's rows and the device flag word.
+dory::PageGuard slot_guard(dory_ctx* c, int j) {
+  dory::PageGuard gd;
+  gd.max_seqs = c->cfg.max_seqs;
+  gd.pool_pages = (c->recycle && !full_block(c->cfg, j)) ? c->swa_pages_total : c->pages_total;
+  gd.max_pos = c->cfg.max_model_len;
+  gd.flags = c->W<int32_t>(c->L.err);
+  return gd;
+}
 
 // Copy the host upload image to the device upload area (pinned ring, async).
 bool stage_upload(dory_ctx* c, int n_ints) {
@@ -532,6 +547,14 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   const int32_t* rows = c->W<int32_t>(c->L.upload);
   const int32_t* ptab = slot_ptab(c, j);
   char* kv = slot_base(c, j, t);
+  const dory::PageGuard gd = slot_guard(c, j);
+#if DORY_CHECKED
+  // the slot's whole cache region must lie inside the caller's pool
+  if (kv < c->pool || kv + (size_t)gd.pool_pages * c->page_bytes > c->pool + c->pool_bytes) {
+    ok(c, hipErrorInvalidValue);
+    return;
+  }
+#endif
   hipStream_t st = c->stream;
   const double wb = wbytes(c, M);
   const bool gmx = c->mx && M <= 2;  // this call streams the MX weights
@@ -549,7 +572,7 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   if (!fused_decode) {
     Span sp(c, R_ROPE, Md * nq * 4 + Md * (hd + 2.0 * Hk * dh) * es, 0);
     ok(c, launch_rope_qk_kv(dt, qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), c->W(c->L.q), kv, M, H,
-                            Hk, dh, c->page_el, decode ? -1 : c->chunk_seq, decode ? -1 : c->chunk_pos0, st));
+                            Hk, dh, c->page_el, decode ? -1 : c->chunk_seq, decode ? -1 : c->chunk_pos0, gd, st));
   }
   {
     // fused decode reads q/k/v from the projection output and writes the new key/value itself
@@ -559,15 +582,15 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
     if (paged && (decode || !flash)) {
       ok(c, launch_attn_decode(qkv, rows, ptab, c->L.max_pages, c->W<float2>(c->L.rope), kv, c->page_el, M, H, Hk,
                                win, g.attn_scale, splits, fused_decode ? 1 : 0, c->W(c->L.o), c->W<float>(c->L.part_ml),
-                               c->W<float>(c->L.part_o), c->row_order, c->run_seq, c->run_pos, st));
+                               c->W<float>(c->L.part_o), c->row_order, c->run_seq, c->run_pos, gd, st));
     } else if (flash) {
       ok(c, launch_attn_prefill(c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, win,
-                                g.attn_scale, c->W(c->L.o), st));
+                                g.attn_scale, c->W(c->L.o), gd, st));
     } else {
       if (splits > 1) c->stats.kernel_launches++;
       ok(c, launch_attn_rows(dt, c->W(c->L.q), rows, ptab, c->L.max_pages, kv, c->page_el, M, H, Hk, dh, win,
                              g.attn_scale, splits, c->W(c->L.o), c->W<float>(c->L.part_ml), c->W<float>(c->L.part_o),
-                             st));
+                             gd, st));
     }
   }
   // without the fused GEMV path, a split-K o / down product leaves its partials for the residual
@@ -825,7 +848,7 @@ dory_status prefill_impl(dory_ctx* c, int32_t sid, const int32_t* tokens_dev, in
   if (!c->dry && n_upd) {
     Span sp(c, R_PTAB, 12.0 * n_upd, 0);
     ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
-                                     c->stream));
+                                     ptab_entries(c), c->W<int32_t>(c->L.err), c->stream));
   }
   s.len = len + n;
   s.append_run(s.len, k_run);
@@ -889,7 +912,7 @@ dory_status decode_impl(dory_ctx* c, int32_t n, const int32_t* seq_ids, const in
   if (!c->dry && n_upd) {
     Span sp(c, R_PTAB, 12.0 * n_upd, 0);
     ok(c, dory::launch_apply_updates(c->W<int32_t>(c->L.ptab), c->W<int32_t>(c->L.upload) + n_rows_ints, n_upd,
-                                     c->stream));
+                                     ptab_entries(c), c->W<int32_t>(c->L.err), c->stream));
   }
   Geom geo;
   for (int i = 0; i < n; ++i) {
@@ -1263,6 +1286,26 @@ dory_status dory_device_flags(dory_ctx* c, int32_t* flags, int32_t reset) {
   if (e == hipSuccess && reset) e = hipMemsetAsync(c->W(c->L.err), 0, 4, c->stream);
   if (e != hipSuccess) return fail(c, DORY_E_HIP, "reading device flags: %s", hipGetErrorString(e));
   *flags = v;
+  return DORY_OK;
+}
+
+int32_t dory_checked_build(void) { return DORY_CHECKED ? 1 : 0; }
+
+dory_status dory_debug_set_page(dory_ctx* c, int32_t seq_id, int32_t page_index, int32_t page_id, int32_t* old_id) {
+  if (!c) return DORY_E_INVALID;
+  if (!DORY_CHECKED) return fail(c, DORY_E_STATE, "dory_debug_set_page exists only in the checked build");
+  if (c->dry) return fail(c, DORY_E_STATE, "dry-run context");
+  if (seq_id < 0 || seq_id >= c->cfg.max_seqs || page_index < 0 || page_index >= c->L.max_pages)
+    return fail(c, DORY_E_INVALID, "page-table entry (%d, %d) outside the table", seq_id, page_index);
+  int32_t* e = c->W<int32_t>(c->L.ptab) + (size_t)seq_id * c->L.max_pages + page_index;
+  int32_t v = 0;
+  const int32_t nv = page_id;
+  hipError_t h = hipMemcpyAsync(&v, e, 4, hipMemcpyDeviceToHost, c->stream);
+  if (h == hipSuccess) h = hipStreamSynchronize(c->stream);
+  if (h == hipSuccess) h = hipMemcpyAsync(e, &nv, 4, hipMemcpyHostToDevice, c->stream);
+  if (h == hipSuccess) h = hipStreamSynchronize(c->stream);
+  if (h != hipSuccess) return fail(c, DORY_E_HIP, "page-table write: %s", hipGetErrorString(h));
+  if (old_id) *old_id = v;
   return DORY_OK;
 }
 

@@ -25,6 +25,34 @@
 
 namespace dory {
 
+// Page-table and RoPE-row reads through the index guard (PageGuard, kernels.h): plain reads in
+// the default build; bounds-checked, flagged and clamped to index 0 in the DORY_CHECKED build.
+DORY_DEV int32_t page_at(const int32_t* __restrict__ tab, int max_pages, int seq, int pi, const PageGuard& gd) {
+#if DORY_CHECKED
+  if ((uint32_t)seq >= (uint32_t)gd.max_seqs || (uint32_t)pi >= (uint32_t)max_pages) {
+    atomicOr(gd.flags, kDevFlagPageIndex);
+    return 0;
+  }
+  const int32_t p = tab[(size_t)seq * max_pages + pi];
+  if ((uint32_t)p >= (uint32_t)gd.pool_pages) {
+    atomicOr(gd.flags, kDevFlagPageId);
+    return 0;
+  }
+  return p;
+#else
+  return tab[(size_t)seq * max_pages + pi];
+#endif
+}
+DORY_DEV int rope_row(int pos, const PageGuard& gd) {
+#if DORY_CHECKED
+  if ((uint32_t)pos >= (uint32_t)gd.max_pos) {
+    atomicOr(gd.flags, kDevFlagPosition);
+    return 0;
+  }
+#endif
+  return pos;
+}
+
 // ---------------------------------------------------------------- rotary + norm + KV write
 
 // One wave per (row, head). Heads 0..H-1 are queries: q^ = N(RoPE(q)) -> q_out.
@@ -35,7 +63,7 @@ __global__ void __launch_bounds__(64) k_rope_qk_kv(const float* __restrict__ qkv
                                                    const int32_t* __restrict__ ptab, int max_pages,
                                                    const float2* __restrict__ rope, T* __restrict__ q_out,
                                                    T* __restrict__ kv_slot, int H, int Hkv, int dh,
-                                                   size_t page_elems) {
+                                                   size_t page_elems, const PageGuard gd) {
   const int m = blockIdx.x, hd = blockIdx.y, lane = threadIdx.x;
   const int seq = rows[2 * m], pos = rows[2 * m + 1];
   const int half = dh >> 1;
@@ -45,7 +73,7 @@ __global__ void __launch_bounds__(64) k_rope_qk_kv(const float* __restrict__ qkv
   const bool act = lane < half;
   if (act) {
     const float x1 = src[lane], x2 = src[lane + half];
-    const float2 cs = rope[(size_t)pos * half + lane];
+    const float2 cs = rope[(size_t)rope_row(pos, gd) * half + lane];
     a0 = x1 * cs.x - x2 * cs.y;
     a1 = x1 * cs.y + x2 * cs.x;
   }
@@ -59,7 +87,7 @@ __global__ void __launch_bounds__(64) k_rope_qk_kv(const float* __restrict__ qkv
     return;
   }
   const int g = hd - H, tok = pos & 15;
-  const int page = ptab[(size_t)seq * max_pages + (pos >> 4)];
+  const int page = page_at(ptab, max_pages, seq, pos >> 4, gd);
   T* kp = kv_slot + (size_t)page * page_elems + ((size_t)g * 16 + tok) * dh;
   T* vt = kv_slot + (size_t)page * page_elems + (size_t)Hkv * 16 * dh + (size_t)g * dh * 16 + vperm(tok);
   const float* vsrc = src + (size_t)Hkv * dh;
@@ -82,7 +110,7 @@ __global__ void __launch_bounds__(1024) k_rope_page(const float* __restrict__ qk
                                                    const int32_t* __restrict__ ptab, int max_pages,
                                                    const float2* __restrict__ rope, bf16_t* __restrict__ q_out,
                                                    bf16_t* __restrict__ kv_slot, int H, int Hkv,
-                                                   size_t page_elems) {
+                                                   size_t page_elems, const PageGuard gd) {
   constexpr int DH = 128;
   __shared__ __attribute__((aligned(16))) bf16_t kt[16][DH];
   __shared__ __attribute__((aligned(16))) bf16_t vt[DH][16];
@@ -107,7 +135,7 @@ __global__ void __launch_bounds__(1024) k_rope_page(const float* __restrict__ qk
     const int head = hu < G ? g * G + hu : H + g;    // query head, or the key head
     const float* x = src + (size_t)head * DH;
     const float x1 = x[lane], x2 = x[lane + 64];
-    const float2 cs = rope[(size_t)pos * 64 + lane];
+    const float2 cs = rope[(size_t)rope_row(pos, gd) * 64 + lane];
     const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
     const float rn = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
     if (hu < G) {
@@ -120,7 +148,7 @@ __global__ void __launch_bounds__(1024) k_rope_page(const float* __restrict__ qk
     }
   }
   __syncthreads();
-  const int page = ptab[(size_t)seq * max_pages + pg];
+  const int page = page_at(ptab, max_pages, seq, pg, gd);
   bf16_t* kp = kv_slot + (size_t)page * page_elems + (size_t)g * 16 * DH;
   bf16_t* vp = kv_slot + (size_t)page * page_elems + (size_t)Hkv * 16 * DH + (size_t)g * DH * 16;
   const int t = threadIdx.x;
@@ -151,7 +179,7 @@ template <typename T, int DH>
 __global__ void __launch_bounds__(ATT_THREADS) k_attn_rows(
     const T* __restrict__ q, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
     const T* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window, float scale, int splits,
-    T* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_o) {
+    T* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_o, const PageGuard gd) {
   constexpr int LPK = DH / 8;
   constexpr int KPW = 64 / LPK;
   __shared__ float sm[ATT_WAVES][GMAX], sl[ATT_WAVES][GMAX];
@@ -186,7 +214,7 @@ __global__ void __launch_bounds__(ATT_THREADS) k_attn_rows(
     for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
   }
   for (int j = kbeg + wv * KPW + lane / LPK; j < kend; j += ATT_WAVES * KPW) {
-    const int page = ptab[(size_t)seq * max_pages + (j >> 4)];
+    const int page = page_at(ptab, max_pages, seq, j >> 4, gd);
     const T* pg = kv_slot + (size_t)page * page_elems;
     float kf[8], vf[8];
     load8(pg + ((size_t)g * 16 + (j & 15)) * DH + e0, kf);
@@ -341,7 +369,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(
     const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
     const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int M, int H, int Hkv,
     int window, float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
-    float* __restrict__ part_o, int2 run) {
+    float* __restrict__ part_o, int2 run, const PageGuard gd) {
   constexpr int DH = 128;
   constexpr int RWMAX = C / G;  // rows per workgroup at most
   static_assert(C == G || C == 32, "column capacity");
@@ -366,7 +394,6 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   const int pps = (pl - pf + 1 + splits - 1) / splits;
   const int sp_first = pf + sp * pps;
   const int sp_last = min(pl, sp_first + pps - 1);
-  const int32_t* prow = ptab + (size_t)seq * max_pages;
   const size_t vbase = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16;
   const bool writer = C == G && write_kv && sp_first <= pl && pl <= sp_last;
   const int npair = sp_last >= sp_first ? (sp_last - sp_first + 2) / 2 : 0;
@@ -379,8 +406,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(
     const int itl = it0 + lane;
     if (itl < nw) {
       const int p0 = sp_first + 2 * (wv + 4 * itl);
-      pid0 = prow[p0];
-      pid1 = p0 + 1 <= sp_last ? prow[p0 + 1] : pid0;
+      pid0 = page_at(ptab, max_pages, seq, p0, gd);
+      pid1 = p0 + 1 <= sp_last ? page_at(ptab, max_pages, seq, p0 + 1, gd) : pid0;
     }
   };
   load_pids(0);
@@ -391,7 +418,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   // queries of the group: q^ = N(RoPE(q)) in bf16, column r * G + gi
   for (int col = wv; col < RW * G; col += 4) {
     const int r = col / G, gi = col % G;
-    const float2 cs = rope[(size_t)(pos_first + r) * 64 + lane];
+    const float2 cs = rope[(size_t)rope_row(pos_first + r, gd) * 64 + lane];
     const float* x = qkv + (size_t)(m0 + r) * (size_t)((H + 2 * Hkv) * DH) + (size_t)(g * G + gi) * DH;
     const float x1 = x[lane], x2 = x[lane + 64];
     const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
@@ -402,8 +429,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   // the split holding the row's own position writes its key/value first
   if (writer && wv < 2) {
     const float* src = qkv + (size_t)m0 * (size_t)((H + 2 * Hkv) * DH);
-    const float2 cs = rope[(size_t)pos * 64 + lane];
-    bf16_t* pg = kv_slot + (size_t)prow[pl] * page_elems;
+    const float2 cs = rope[(size_t)rope_row(pos, gd) * 64 + lane];
+    bf16_t* pg = kv_slot + (size_t)page_at(ptab, max_pages, seq, pl, gd) * page_elems;
     const int tok = pos & 15;
     if (wv == 0) {
       const float* x = src + (size_t)(H + g) * DH;
@@ -547,7 +574,7 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
     const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
     const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window,
     float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
-    float* __restrict__ part_o) {
+    float* __restrict__ part_o, const PageGuard gd) {
   constexpr int DH = 128;
   __shared__ float qs[G][DH];
   __shared__ float knew[DH], vnew[DH];
@@ -562,7 +589,7 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
   const int kbeg = lo + sp * chunk;
   const int kend = min(pos + 1, kbeg + chunk);
   const float* src = qkv + (size_t)m * (size_t)((H + 2 * Hkv) * DH);
-  const float2 cs = rope[(size_t)pos * 64 + lane];
+  const float2 cs = rope[(size_t)rope_row(pos, gd) * 64 + lane];
 
   // queries of the group: q^ = N(RoPE(q)), rounded to bf16, times the scale
   for (int gi = wv; gi < G; gi += 4) {
@@ -577,7 +604,7 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
   // them in LDS: the key loop below takes that key from LDS, not from memory.
   const bool writer = write_kv && kbeg <= pos && pos < kend;
   if (writer && wv < 2) {
-    const int page = ptab[(size_t)seq * max_pages + (pos >> 4)];
+    const int page = page_at(ptab, max_pages, seq, pos >> 4, gd);
     bf16_t* pg = kv_slot + (size_t)page * page_elems;
     const int tok = pos & 15;
     if (wv == 0) {
@@ -618,9 +645,8 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
     const int np = p_first <= p_last ? (p_last - p_first) / 4 + 1 : 0;  // pages of this wave
     const size_t vofs = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16 + (size_t)lane * 32;
     const size_t kofs = ((size_t)g * 16 + r) * DH + db * 32;
-    const int32_t* prow = ptab + (size_t)seq * max_pages;
     // page ids of this wave's pages, 64 at a time, one per lane
-    int pid = lane < np ? prow[p_first + 4 * lane] : 0;
+    int pid = lane < np ? page_at(ptab, max_pages, seq, p_first + 4 * lane, gd) : 0;
     uint4 kr[4], vr[4];
     auto fetch = [&](int it) {
       const int page = __shfl(pid, it & 63, 64);
@@ -661,7 +687,8 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
       }
       // next page's loads are in flight while this page is computed
       if (it + 1 < np) {
-        if (((it + 1) & 63) == 0) pid = lane + it + 1 < np ? prow[p_first + 4 * (it + 1 + lane)] : 0;
+        if (((it + 1) & 63) == 0)
+          pid = lane + it + 1 < np ? page_at(ptab, max_pages, seq, p_first + 4 * (it + 1 + lane), gd) : 0;
         fetch(it + 1);
       }
       const int key = p * 16 + r;
@@ -757,7 +784,7 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
     const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
     const float2* __restrict__ rope, bf16_t* __restrict__ kv_slot, size_t page_elems, int H, int Hkv, int window,
     float scale, int splits, int write_kv, bf16_t* __restrict__ out, float* __restrict__ part_ml,
-    float* __restrict__ part_o, const int32_t* __restrict__ order) {
+    float* __restrict__ part_o, const int32_t* __restrict__ order, const PageGuard gd) {
   constexpr int DH = 128;
   constexpr float LOG2E = 1.4426950408889634f;
   __shared__ __attribute__((aligned(16))) bf16_t qh[G][DH];
@@ -775,7 +802,7 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
   const int kbeg = lo + sp * chunk;
   const int kend = min(pos + 1, kbeg + chunk);
   const float* src = qkv + (size_t)m * (size_t)((H + 2 * Hkv) * DH);
-  const float2 cs = rope[(size_t)pos * 64 + lane];
+  const float2 cs = rope[(size_t)rope_row(pos, gd) * 64 + lane];
 
   // queries of the group: q^ = N(RoPE(q)) in bf16
   for (int gi = wv; gi < G; gi += 4) {
@@ -791,7 +818,7 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
   const bool writer = write_kv && kbeg <= pos && pos < kend;
   const int tok = pos & 15;
   if (writer && wv < 2) {
-    const int page = ptab[(size_t)seq * max_pages + (pos >> 4)];
+    const int page = page_at(ptab, max_pages, seq, pos >> 4, gd);
     bf16_t* pg = kv_slot + (size_t)page * page_elems;
     if (wv == 0) {
       const float* x = src + (size_t)(H + g) * DH;
@@ -834,9 +861,8 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
     const int np = p_first <= p_last ? (p_last - p_first) / 4 + 1 : 0;  // pages of this wave
     const size_t vofs = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16 + (size_t)lane * 32;
     const size_t kofs = ((size_t)g * 16 + r) * DH + db * 32;
-    const int32_t* prow = ptab + (size_t)seq * max_pages;
     // page ids of this wave's pages, 64 at a time, one per lane
-    int pid = lane < np ? prow[p_first + 4 * lane] : 0;
+    int pid = lane < np ? page_at(ptab, max_pages, seq, p_first + 4 * lane, gd) : 0;
     uint4 kr[4], vr[4];
     auto fetch = [&](int it) __attribute__((always_inline)) {
       const int page = __builtin_amdgcn_readlane(pid, it & 63);
@@ -864,7 +890,8 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
       }
       // next page's loads are in flight while this page is computed
       if (it + 1 < np) {
-        if (((it + 1) & 63) == 0) pid = lane + it + 1 < np ? prow[p_first + 4 * (it + 1 + lane)] : 0;
+        if (((it + 1) & 63) == 0)
+          pid = lane + it + 1 < np ? page_at(ptab, max_pages, seq, p_first + 4 * (it + 1 + lane), gd) : 0;
         fetch(it + 1);
       }
       const int key = p * 16 + r;
@@ -990,7 +1017,7 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
                              const int32_t* __restrict__ ptab, int max_pages, const bf16_t* __restrict__ kv_slot,
                              size_t page_elems, int M, int H, int Hkv, int window, float scale,
                              bf16_t* __restrict__ out, int wrow0, bf16_t (*Ks)[KSPLIT][PF_KB * 128],
-                             bf16_t (*Vs)[KSPLIT][PF_KB * 128]) {
+                             bf16_t (*Vs)[KSPLIT][PF_KB * 128], const PageGuard& gd) {
   constexpr int DH = 128, KB = PF_KB, STEP = KB * KSPLIT;
   constexpr float LOG2E = 1.4426950408889634f;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1006,7 +1033,6 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
   const int wg_last = rows[2 * (min(wrow0 + 127, M - 1)) + 1];
   const int pos_first = nrow > 0 ? rows[2 * row0 + 1] : 0;
   const int pos_last = nrow > 0 ? rows[2 * (row0 + nrow - 1) + 1] : -1;
-  const int32_t* prow = ptab + (size_t)seq * max_pages;
   const int last_page = wg_last >> 4;
 
   // Q as the B operand of S^T: lane holds Q[query qi][dims 16ks + 8hh .. +8]
@@ -1046,7 +1072,7 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
   constexpr uint32_t kStageBytes = KSPLIT * PF_KB * 128 * 2;
   auto kv_dma = [&](int step0, int st_) __attribute__((always_inline)) {
     const int pidx = min(((step0 + kgu * KB) >> 4) + wqu, last_page);
-    const bf16_t* pg = kv_slot + (size_t)prow[pidx] * page_elems;
+    const bf16_t* pg = kv_slot + (size_t)page_at(ptab, max_pages, seq, pidx, gd) * page_elems;
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
       lds_dma16(pg, kofs[qt], lds_k + st_ * kStageBytes + qt * 4 * DH * 2);
@@ -1227,17 +1253,18 @@ __global__ void __launch_bounds__(256 * KSPLIT) k_attn_prefill(const bf16_t* __r
                                                                const int32_t* __restrict__ ptab, int max_pages,
                                                                const bf16_t* __restrict__ kv_slot, size_t page_elems,
                                                                int M, int H, int Hkv, int window, float scale,
-                                                               bf16_t* __restrict__ out, int paired) {
+                                                               bf16_t* __restrict__ out, int paired,
+                                                               const PageGuard gd) {
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][KSPLIT][PF_KB * 128];
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[2][KSPLIT][PF_KB * 128];
   const int nrb = (M + 127) / 128;
   const int hi = nrb - 1 - (int)blockIdx.x, lo = (int)blockIdx.x;
   attn_row_block<FIXED, KSPLIT>(q, rows, ptab, max_pages, kv_slot, page_elems, M, H, Hkv, window, scale, out,
-                                hi * 128, Ks, Vs);
+                                hi * 128, Ks, Vs, gd);
   if (paired && lo < hi) {
     __syncthreads();  // the first block's merge read the LDS
     attn_row_block<FIXED, KSPLIT>(q, rows, ptab, max_pages, kv_slot, page_elems, M, H, Hkv, window, scale, out,
-                                  lo * 128, Ks, Vs);
+                                  lo * 128, Ks, Vs, gd);
   }
 }
 
@@ -1245,31 +1272,31 @@ __global__ void __launch_bounds__(256 * KSPLIT) k_attn_prefill(const bf16_t* __r
 
 hipError_t launch_rope_qk_kv(int dtype, const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                              const float2* rope, void* q_out, void* kv_slot, int M, int H, int Hkv, int dh,
-                             size_t page_elems, int seq, int pos0, hipStream_t st) {
+                             size_t page_elems, int seq, int pos0, const PageGuard& gd, hipStream_t st) {
   if (dtype != 0 && dh == 128 && seq >= 0 && pos0 >= 0) {
     const int tiles = (pos0 + M - 1) / 16 - pos0 / 16 + 1;
     DORY_LAUNCH(k_rope_page, dim3(tiles, Hkv), dim3(1024), 0, st, qkv, seq, pos0, M, ptab, max_pages, rope,
-                (bf16_t*)q_out, (bf16_t*)kv_slot, H, Hkv, page_elems);
+                (bf16_t*)q_out, (bf16_t*)kv_slot, H, Hkv, page_elems, gd);
     return hipGetLastError();
   }
   dim3 grid(M, H + Hkv);
   if (dtype == 0)
     DORY_LAUNCH(k_rope_qk_kv<float>, grid, dim3(64), 0, st, qkv, rows, ptab, max_pages, rope,
-                       (float*)q_out, (float*)kv_slot, H, Hkv, dh, page_elems);
+                       (float*)q_out, (float*)kv_slot, H, Hkv, dh, page_elems, gd);
   else
     DORY_LAUNCH(k_rope_qk_kv<bf16_t>, grid, dim3(64), 0, st, qkv, rows, ptab, max_pages, rope,
-                       (bf16_t*)q_out, (bf16_t*)kv_slot, H, Hkv, dh, page_elems);
+                       (bf16_t*)q_out, (bf16_t*)kv_slot, H, Hkv, dh, page_elems, gd);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t attn_t(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                          size_t page_elems, int M, int H, int Hkv, int dh, int window, float scale, int splits,
-                         void* out, float* part_ml, float* part_o, hipStream_t st) {
+                         void* out, float* part_ml, float* part_o, const PageGuard& gd, hipStream_t st) {
   dim3 grid(M, Hkv, splits);
 #define DORY_ATT(DHV)                                                                                         \
   DORY_LAUNCH((k_attn_rows<T, DHV>), grid, dim3(ATT_THREADS), 0, st, (const T*)q, rows, ptab, max_pages, \
-                     (const T*)kv, page_elems, H, Hkv, window, scale, splits, (T*)out, part_ml, part_o)
+                     (const T*)kv, page_elems, H, Hkv, window, scale, splits, (T*)out, part_ml, part_o, gd)
   switch (dh) {
     case 32: DORY_ATT(32); break;
     case 64: DORY_ATT(64); break;
@@ -1286,12 +1313,13 @@ static hipError_t attn_t(const void* q, const int32_t* rows, const int32_t* ptab
 
 hipError_t launch_attn_rows(int dtype, const void* q, const int32_t* rows, const int32_t* ptab, int max_pages,
                             const void* kv, size_t page_elems, int M, int H, int Hkv, int dh, int window,
-                            float scale, int splits, void* out, float* part_ml, float* part_o, hipStream_t st) {
+                            float scale, int splits, void* out, float* part_ml, float* part_o, const PageGuard& gd,
+                            hipStream_t st) {
   if (H / Hkv > GMAX) return hipErrorInvalidValue;
   return dtype == 0 ? attn_t<float>(q, rows, ptab, max_pages, kv, page_elems, M, H, Hkv, dh, window, scale, splits,
-                                    out, part_ml, part_o, st)
+                                    out, part_ml, part_o, gd, st)
                     : attn_t<bf16_t>(q, rows, ptab, max_pages, kv, page_elems, M, H, Hkv, dh, window, scale, splits,
-                                     out, part_ml, part_o, st);
+                                     out, part_ml, part_o, gd, st);
 }
 
 bool attn_decode_supported(int dtype, int H, int Hkv, int dh) {
@@ -1301,7 +1329,7 @@ bool attn_decode_supported(int dtype, int H, int Hkv, int dh) {
 hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                               const float2* rope, void* kv, size_t page_elems, int M, int H, int Hkv, int window,
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
-                              const int32_t* order, int run_seq, int run_pos, hipStream_t st) {
+                              const int32_t* order, int run_seq, int run_pos, const PageGuard& gd, hipStream_t st) {
   const int2 run = make_int2(M <= kDecodeMfmaRows ? run_seq : -1, run_pos);
   // consecutive positions of one sequence whose keys are already in the cache (no key/value
   // writes here): several rows per workgroup share every key load
@@ -1311,17 +1339,17 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
   if (M > kDecodeMfmaRows && scale <= kFixedMaxScale)                                                          \
     DORY_LAUNCH(k_attn_decode_valu_fx<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope,           \
                 (bf16_t*)kv, page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o, \
-                order);                                                                                        \
+                order, gd);                                                                                    \
   else if (M > kDecodeMfmaRows)                                                                                \
     DORY_LAUNCH(k_attn_decode_valu<GV>, grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv, \
-                page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o);           \
+                page_elems, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o, gd);       \
   else if (multi)                                                                                              \
     DORY_LAUNCH((k_attn_decode<GV, 32>), dim3((M + 32 / GV - 1) / (32 / GV), Hkv, splits), dim3(256), 0, st, qkv, \
                 rows, ptab, max_pages, rope, (bf16_t*)kv, page_elems, M, H, Hkv, window, scale, splits, write_kv,  \
-                (bf16_t*)out, part_ml, part_o, run);                                                            \
+                (bf16_t*)out, part_ml, part_o, run, gd);                                                        \
   else                                                                                                         \
     DORY_LAUNCH((k_attn_decode<GV, GV>), grid, dim3(256), 0, st, qkv, rows, ptab, max_pages, rope, (bf16_t*)kv, \
-                page_elems, M, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o, run)
+                page_elems, M, H, Hkv, window, scale, splits, write_kv, (bf16_t*)out, part_ml, part_o, run, gd)
   switch (H / Hkv) {
     case 1: DORY_DEC(1); break;
     case 2: DORY_DEC(2); break;
@@ -1339,17 +1367,17 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
 
 hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
-                               hipStream_t st) {
+                               const PageGuard& gd, hipStream_t st) {
   // pair row blocks when that still leaves at least 128 workgroups
   const int nrb = (M + 127) / 128;
   const int paired = ((nrb + 1) / 2) * H >= 128 ? 1 : 0;
   dim3 grid(paired ? (nrb + 1) / 2 : nrb, H);
   if (scale <= kFixedMaxScale)
     DORY_LAUNCH((k_attn_prefill<true, 2>), grid, dim3(512), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
-                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, paired);
+                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, paired, gd);
   else
     DORY_LAUNCH((k_attn_prefill<false, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
-                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, paired);
+                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, paired, gd);
   return hipGetLastError();
 }
 

@@ -295,10 +295,20 @@ __global__ void __launch_bounds__(64) k_argmax_final(const float* __restrict__ p
   if (t == 0) ids[row] = bi == 0x7fffffff ? 0 : bi;
 }
 
-// Page-table scatter: table[upd[2i]] = upd[2i+1].
-__global__ void k_apply_updates(int32_t* __restrict__ table, const int32_t* __restrict__ upd, int n) {
+// Page-table scatter: table[upd[2i]] = upd[2i+1]. The checked build skips (and flags) an entry
+// index outside the table's `entries`.
+__global__ void k_apply_updates(int32_t* __restrict__ table, const int32_t* __restrict__ upd, int n, int entries,
+                                int32_t* __restrict__ flags) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) table[upd[2 * i]] = upd[2 * i + 1];
+  if (i >= n) return;
+  const int e = upd[2 * i];
+#if DORY_CHECKED
+  if ((uint32_t)e >= (uint32_t)entries) {
+    atomicOr(flags, kDevFlagPageIndex);
+    return;
+  }
+#endif
+  table[e] = upd[2 * i + 1];
 }
 
 // Rotary table: tab[p][i] = (cos, sin)(p * theta^(-2i/dh)), angle and cos/sin in fp64.
@@ -381,9 +391,10 @@ hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, voi
   return hipGetLastError();
 }
 
-hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, hipStream_t st) {
+hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, int entries, int32_t* flags,
+                                hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  DORY_LAUNCH(k_apply_updates, dim3((n + 255) / 256), dim3(256), 0, st, table, upd, n);
+  DORY_LAUNCH(k_apply_updates, dim3((n + 255) / 256), dim3(256), 0, st, table, upd, n, entries, flags);
   return hipGetLastError();
 }
 

@@ -48,18 +48,39 @@ hipError_t launch_loop_step(int dtype, float* h, const float* y, const float* al
                             float* hout, void* hb, int M, int d, int mode, hipStream_t st);
 constexpr int kArgmaxParts = 64;  // partial (max, index) pairs per row in the argmax scratch
 hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* ids, void* scratch, hipStream_t st);
-hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, hipStream_t st);
+// entries: size of the table (checked build: updates outside it are skipped and flagged in *flags)
+hipError_t launch_apply_updates(int32_t* table, const int32_t* upd, int n, int entries, int32_t* flags,
+                                hipStream_t st);
 hipError_t launch_rope_table(float2* tab, int max_len, int dh, double theta, hipStream_t st);
 hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t st);
+
+// Index guard of the kernels that follow a page table (k_attn.hip). The default build reads page
+// ids and RoPE rows as given: the host validates every sequence, position and page it hands to
+// the device. Built with DORY_CHECKED=1 (the debug library), every page-table read first checks
+// the sequence against max_seqs and the page index against the table width, then the page id it
+// read against the pages of the slot's cache region, and every RoPE row read checks its position
+// against max_pos; a violation sets a bit of *flags (kDevFlag*) and uses index 0 instead, so each
+// access stays inside its buffer (that call's outputs are then meaningless).
+struct PageGuard {
+  int32_t max_seqs;    // rows of the page table
+  int32_t pool_pages;  // pages of the cache region the table's ids index
+  int32_t max_pos;     // rows of the RoPE table
+  int32_t* flags;      // the context's device flag word
+};
+constexpr int32_t kDevFlagTokenId = 1, kDevFlagPageIndex = 2, kDevFlagPageId = 4, kDevFlagPosition = 8;
+#ifndef DORY_CHECKED
+#define DORY_CHECKED 0
+#endif
 
 // RoPE + per-head q/k norm + KV write of M rows. seq, pos0 >= 0: the rows are the consecutive
 // positions pos0 .. pos0+M-1 of sequence seq (a prefill chunk; page-tiled kernel for bf16 d_h 128).
 hipError_t launch_rope_qk_kv(int dtype, const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                              const float2* rope, void* q_out, void* kv_slot, int M, int H, int Hkv, int dh,
-                             size_t page_elems, int seq, int pos0, hipStream_t st);
+                             size_t page_elems, int seq, int pos0, const PageGuard& gd, hipStream_t st);
 hipError_t launch_attn_rows(int dtype, const void* q, const int32_t* rows, const int32_t* ptab, int max_pages,
                             const void* kv, size_t page_elems, int M, int H, int Hkv, int dh, int window,
-                            float scale, int splits, void* out, float* part_ml, float* part_o, hipStream_t st);
+                            float scale, int splits, void* out, float* part_ml, float* part_o, const PageGuard& gd,
+                            hipStream_t st);
 
 bool attn_decode_supported(int dtype, int H, int Hkv, int dh);
 constexpr int kDecodeMfmaRows = 16;  // split-key attention: MFMA kernel up to this many rows, VALU kernel above
@@ -68,12 +89,12 @@ constexpr int kDecodeMfmaRows = 16;  // split-key attention: MFMA kernel up to t
 hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32_t* ptab, int max_pages,
                               const float2* rope, void* kv, size_t page_elems, int M, int H, int Hkv, int window,
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
-                              const int32_t* order, int run_seq, int run_pos, hipStream_t st);
+                              const int32_t* order, int run_seq, int run_pos, const PageGuard& gd, hipStream_t st);
 // (run_seq >= 0: the M <= kDecodeMfmaRows rows are positions run_pos, run_pos + 1, ... of sequence
 // run_seq, so the kernel takes them from its arguments instead of loading the row list.)
 hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
-                               hipStream_t st);
+                               const PageGuard& gd, hipStream_t st);
 
 bool gemv_supported(int K);
 bool gemv_residual_supported(int K);

@@ -17,6 +17,10 @@ from . import synth
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdory.so")
+CHECKED_LIB_PATH = os.path.join(_HERE, "libdory_checked.so")
+# bytes past the KV pool that a checked-build context keeps unused, so that a page id one past the
+# pool (the guard tests' injected fault) stays inside the allocation even before the guard clamps it
+CHECKED_POOL_GUARD = 1 << 20
 
 DORY_OK, DORY_E_INVALID, DORY_E_STATE, DORY_E_NOMEM, DORY_E_HIP = 0, -1, -2, -3, -4
 KV_MODES = {"per_loop": 0, "last_loop": 1}
@@ -86,6 +90,8 @@ EXPORTS = {
     "dory_get_stats": (C.c_int, [C.c_void_p, C.POINTER(Stats)]),
     "dory_last_hidden": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
     "dory_device_flags": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32]),
+    "dory_checked_build": (C.c_int32, []),
+    "dory_debug_set_page": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     "dory_quantize_mxfp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dory_quantize_mxfp4": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dory_sample": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p, C.c_void_p,
@@ -102,22 +108,24 @@ EXPORTS = {
     "dory_status_string": (C.c_char_p, [C.c_int32]),
 }
 
-_lib = None
+_libs = {}
 
 
-def lib():
-    """Load libdory.so once; raise if it is missing (no fallback path exists)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run python -m looped_ngpt_language_amd.build")
-        L = C.CDLL(LIB_PATH)
+def lib(checked: bool = False):
+    """Load libdory.so (or, checked=True, its bounds-checked debug build libdory_checked.so) once;
+    raise if it is missing (no fallback path exists)."""
+    checked = bool(checked)
+    if checked not in _libs:
+        path = CHECKED_LIB_PATH if checked else LIB_PATH
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run python -m looped_ngpt_language_amd.build")
+        L = C.CDLL(path)
         for name, (res, args) in EXPORTS.items():
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
-        _lib = L
-    return _lib
+        _libs[checked] = L
+    return _libs[checked]
 
 
 def make_config(shape: synth.ModelShape, *, max_seqs=1, max_model_len=4096, max_loops=4, max_tokens=4096,
@@ -135,10 +143,10 @@ def make_config(shape: synth.ModelShape, *, max_seqs=1, max_model_len=4096, max_
                   rope_theta=shape.rope_theta, attn_scale=shape.scale)
 
 
-def query_sizes(cfg: Config, kv_mode: str, kv_tokens: int):
+def query_sizes(cfg: Config, kv_mode: str, kv_tokens: int, checked: bool = False):
     kv = C.c_size_t()
     ws = C.c_size_t()
-    st = lib().dory_query_sizes(C.byref(cfg), KV_MODES[kv_mode], int(kv_tokens), C.byref(kv), C.byref(ws))
+    st = lib(checked).dory_query_sizes(C.byref(cfg), KV_MODES[kv_mode], int(kv_tokens), C.byref(kv), C.byref(ws))
     if st != DORY_OK:
         raise DoryError(st, "dory_query_sizes rejected the configuration")
     return kv.value, ws.value
@@ -209,10 +217,13 @@ class Model:
 
     def __init__(self, shape: synth.ModelShape, weights=None, *, kv_mode="per_loop", max_loops=4, max_seqs=1,
                  max_model_len=4096, max_tokens=None, kv_tokens=None, device="cuda:0", dry_run=False, stream=None,
-                 share_weights_from=None, gemv_weights="bf16", swa_recycle=False):
+                 share_weights_from=None, gemv_weights="bf16", swa_recycle=False, checked=False):
         """gemv_weights="mxfp8" / "mxfp4": calls of at most 2 rows stream MXFP8 / MXFP4 copies of the weights.
         swa_recycle: sliding-window layers keep only the pages their window (plus a 64-token
-        rollback reserve) can reach; kv_tokens then sizes the full-attention pages."""
+        rollback reserve) can reach; kv_tokens then sizes the full-attention pages.
+        checked: run on the bounds-checked debug build (libdory_checked.so)."""
+        self._L = lib(checked)
+        self.checked = bool(checked)
         self.shape = shape
         self.dry = dry_run
         max_tokens = max_tokens or max_model_len
@@ -220,21 +231,22 @@ class Model:
                                max_tokens=max_tokens, dry_run=dry_run, gemv_weights=gemv_weights,
                                swa_recycle=swa_recycle)
         kv_tokens = kv_tokens if kv_tokens is not None else max_seqs * (max_model_len + 16)
-        kv_bytes, ws_bytes = query_sizes(self.cfg, kv_mode, kv_tokens)
+        kv_bytes, ws_bytes = query_sizes(self.cfg, kv_mode, kv_tokens, checked)
         self.kv_bytes, self.ws_bytes = kv_bytes, ws_bytes
         self._keep = []
         ctx = C.c_void_p()
         if dry_run:
-            st = lib().dory_create(C.byref(self.cfg), None, KV_MODES[kv_mode], None, kv_bytes, None, ws_bytes, None,
+            st = self._L.dory_create(C.byref(self.cfg), None, KV_MODES[kv_mode], None, kv_bytes, None, ws_bytes, None,
                                    C.byref(ctx))
         else:
             import torch
             self.device = torch.device(device)
             self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
             wc = self._share_weights(share_weights_from) if share_weights_from else self._upload_weights(weights)
-            self.pool = torch.empty(max(kv_bytes, 256), dtype=torch.uint8, device=self.device)
+            pad = CHECKED_POOL_GUARD if checked else 0
+            self.pool = torch.empty(max(kv_bytes, 256) + pad, dtype=torch.uint8, device=self.device)
             self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
-            st = lib().dory_create(C.byref(self.cfg), C.byref(wc), KV_MODES[kv_mode], _ptr(self.pool), kv_bytes,
+            st = self._L.dory_create(C.byref(self.cfg), C.byref(wc), KV_MODES[kv_mode], _ptr(self.pool), kv_bytes,
                                    _ptr(self.ws), ws_bytes, C.c_void_p(self.stream.cuda_stream), C.byref(ctx))
         if st != DORY_OK:
             raise DoryError(st, "dory_create failed")
@@ -278,7 +290,7 @@ class Model:
     # -- helpers ------------------------------------------------------------
     def _check(self, st, what):
         if st != DORY_OK:
-            msg = lib().dory_last_error(self.ctx)
+            msg = self._L.dory_last_error(self.ctx)
             raise DoryError(st, f"{what}: {msg.decode() if msg else ''}")
 
     def _tokens(self, tokens):
@@ -291,7 +303,7 @@ class Model:
 
     def close(self):
         if getattr(self, "ctx", None):
-            lib().dory_destroy(self.ctx)
+            self._L.dory_destroy(self.ctx)
             self.ctx = None
 
     def __del__(self):
@@ -302,21 +314,21 @@ class Model:
 
     # -- calls --------------------------------------------------------------
     def set_loops(self, k: int):
-        self._check(lib().dory_set_loops(self.ctx, int(k)), "dory_set_loops")
+        self._check(self._L.dory_set_loops(self.ctx, int(k)), "dory_set_loops")
 
     def loops(self) -> int:
         k = C.c_int32()
-        self._check(lib().dory_get_loops(self.ctx, C.byref(k)), "dory_get_loops")
+        self._check(self._L.dory_get_loops(self.ctx, C.byref(k)), "dory_get_loops")
         return k.value
 
     def set_kv_mode(self, mode: str):
-        self._check(lib().dory_kv_mode(self.ctx, KV_MODES[mode]), "dory_kv_mode")
+        self._check(self._L.dory_kv_mode(self.ctx, KV_MODES[mode]), "dory_kv_mode")
 
     def prefill(self, seq_id: int, tokens, logits_rows: int = 1, logits=None, ids=True):
         """Returns (logits [rows, V] fp32 device tensor, ids [rows] int32 device tensor or None)."""
         n = len(tokens)
         if self.dry:
-            st = lib().dory_prefill(self.ctx, seq_id, None, n, logits_rows, None, None)
+            st = self._L.dory_prefill(self.ctx, seq_id, None, n, logits_rows, None, None)
             self._check(st, "dory_prefill")
             return None, None
         import torch
@@ -324,7 +336,7 @@ class Model:
         if logits is None:
             logits = torch.empty((logits_rows, self.shape.vocab), dtype=torch.float32, device=self.device)
         out_ids = torch.empty(logits_rows, dtype=torch.int32, device=self.device) if ids else None
-        st = lib().dory_prefill(self.ctx, int(seq_id), _ptr(tok), n, int(logits_rows), _ptr(logits), _ptr(out_ids))
+        st = self._L.dory_prefill(self.ctx, int(seq_id), _ptr(tok), n, int(logits_rows), _ptr(logits), _ptr(out_ids))
         self._check(st, "dory_prefill")
         self._keep_call = tok
         return logits, out_ids
@@ -334,59 +346,67 @@ class Model:
         sids = (C.c_int32 * len(seq_ids))(*[int(s) for s in seq_ids])
         n = len(seq_ids)
         if self.dry:
-            self._check(lib().dory_decode(self.ctx, n, sids, None, None, None), "dory_decode")
+            self._check(self._L.dory_decode(self.ctx, n, sids, None, None, None), "dory_decode")
             return None, None
         import torch
         tok = self._tokens(tokens)
         lg = torch.empty((n, self.shape.vocab), dtype=torch.float32, device=self.device) if logits is True else logits
         if out_ids is None:
             out_ids = torch.empty(n, dtype=torch.int32, device=self.device)
-        st = lib().dory_decode(self.ctx, n, sids, _ptr(tok), _ptr(lg) if lg is not None else None, _ptr(out_ids))
+        st = self._L.dory_decode(self.ctx, n, sids, _ptr(tok), _ptr(lg) if lg is not None else None, _ptr(out_ids))
         self._check(st, "dory_decode")
         self._keep_call = tok
         return lg, out_ids
 
     def truncate(self, seq_id: int, new_len: int):
-        self._check(lib().dory_seq_truncate(self.ctx, int(seq_id), int(new_len)), "dory_seq_truncate")
+        self._check(self._L.dory_seq_truncate(self.ctx, int(seq_id), int(new_len)), "dory_seq_truncate")
 
     def release(self, seq_id: int):
-        self._check(lib().dory_seq_release(self.ctx, int(seq_id)), "dory_seq_release")
+        self._check(self._L.dory_seq_release(self.ctx, int(seq_id)), "dory_seq_release")
 
     def seq_len(self, seq_id: int) -> int:
         n = C.c_int32()
-        self._check(lib().dory_seq_len(self.ctx, int(seq_id), C.byref(n)), "dory_seq_len")
+        self._check(self._L.dory_seq_len(self.ctx, int(seq_id), C.byref(n)), "dory_seq_len")
         return n.value
 
     def kv_bytes_in_use(self) -> int:
         b = C.c_size_t()
-        self._check(lib().dory_kv_bytes_in_use(self.ctx, C.byref(b)), "dory_kv_bytes_in_use")
+        self._check(self._L.dory_kv_bytes_in_use(self.ctx, C.byref(b)), "dory_kv_bytes_in_use")
         return b.value
 
     def stats(self) -> dict:
         s = Stats()
-        self._check(lib().dory_get_stats(self.ctx, C.byref(s)), "dory_get_stats")
+        self._check(self._L.dory_get_stats(self.ctx, C.byref(s)), "dory_get_stats")
         return s.as_dict()
 
     def last_hidden(self, rows: int):
         import torch
         out = torch.empty((rows, self.shape.d_model), dtype=torch.float32, device=self.device)
-        self._check(lib().dory_last_hidden(self.ctx, _ptr(out), int(rows)), "dory_last_hidden")
+        self._check(self._L.dory_last_hidden(self.ctx, _ptr(out), int(rows)), "dory_last_hidden")
         return out
 
     def device_flags(self, reset=True) -> int:
-        """Device error flags (bit 0: an out-of-range token id was clamped)."""
+        """Device error flags (bit 0: an out-of-range token id was clamped; checked build also bit 1: a
+        page-table index, bit 2: a page id, bit 3: a RoPE position out of range)."""
         v = C.c_int32()
-        self._check(lib().dory_device_flags(self.ctx, C.byref(v), int(reset)), "dory_device_flags")
+        self._check(self._L.dory_device_flags(self.ctx, C.byref(v), int(reset)), "dory_device_flags")
         return v.value
 
+    def debug_set_page(self, seq_id: int, page_index: int, page_id: int) -> int:
+        """Checked build only: overwrite one device page-table entry; returns the previous entry."""
+        old = C.c_int32()
+        self._check(self._L.dory_debug_set_page(self.ctx, int(seq_id), int(page_index), int(page_id), C.byref(old)),
+                    "dory_debug_set_page")
+        return old.value
+
     def set_timing(self, enable: bool):
-        self._check(lib().dory_set_timing(self.ctx, 1 if enable else 0), "dory_set_timing")
+        self._check(self._L.dory_set_timing(self.ctx, 1 if enable else 0), "dory_set_timing")
 
     def timing(self, reset: bool = False) -> dict:
         """Per kernel role: launches, algorithmic bytes/flops, timed launches and milliseconds."""
         buf = (KernelTime * 32)()
         n = C.c_int32()
-        self._check(lib().dory_get_timing(self.ctx, buf, 32, C.byref(n), 1 if reset else 0), "dory_get_timing")
+        self._check(self._L.dory_get_timing(self.ctx, buf, 32, C.byref(n), 1 if reset else 0), "dory_get_timing")
         out = {}
         for i in range(min(n.value, 32)):
             e = buf[i]
@@ -398,7 +418,7 @@ class Model:
         """Counters of spec_decode since the last reset: rounds, drafted, accepted, produced,
         draft_ms and verify_ms (GPU time of the two phases)."""
         s = SpecStats()
-        self._check(lib().dory_get_spec_stats(self.ctx, C.byref(s), 1 if reset else 0), "dory_get_spec_stats")
+        self._check(self._L.dory_get_spec_stats(self.ctx, C.byref(s), 1 if reset else 0), "dory_get_spec_stats")
         return s.as_dict()
 
     def spec_decode(self, seq_id: int, last: int, n_new: int, gamma=4, k_draft=1, k_verify=4, reuse=False):
@@ -406,7 +426,7 @@ class Model:
         state and cache instead of recomputing them."""
         buf = (C.c_int32 * (n_new + gamma + 1))()
         n = C.c_int32()
-        st = lib().dory_spec_decode(self.ctx, int(seq_id), int(last), int(n_new), int(gamma), int(k_draft),
+        st = self._L.dory_spec_decode(self.ctx, int(seq_id), int(last), int(n_new), int(gamma), int(k_draft),
                                     int(k_verify), int(bool(reuse)), buf, C.byref(n))
         self._check(st, "dory_spec_decode")
         return np.array(buf[:n.value], dtype=np.int32)

@@ -22,13 +22,25 @@ def header_functions():
     return sorted(set(re.findall(r"\b(dory_[a-z_0-9]+)\s*\(", text)))
 
 
-def test_library_exports_every_declared_function():
-    lib = dory.lib()
+@pytest.mark.parametrize("checked", [False, True])
+def test_library_exports_every_declared_function(checked):
+    lib = dory.lib(checked)
     names = header_functions()
     assert len(names) >= 15
     for name in names:
         assert hasattr(lib, name), name
     assert set(dory.EXPORTS) == set(names)
+    assert lib.dory_checked_build() == (1 if checked else 0)
+
+
+@pytest.mark.parametrize("checked", [False, True])
+def test_debug_page_poke_refused_outside_a_checked_gpu_context(checked):
+    # the default build never writes the device page table on request; a dry-run context has none
+    m = dry(checked=checked)
+    with pytest.raises(dory.DoryError) as e:
+        m.debug_set_page(0, 0, 1)
+    assert e.value.status == dory.DORY_E_STATE
+    m.close()
 
 
 def dry(shape=synth.TINY, mode="per_loop", **kw):
