@@ -388,6 +388,40 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
   // 32-bit byte offsets inside the tile kernels
   if ((size_t)M * K * 2 > 0xFFFFFFFFull || (size_t)N * K * 2 > 0xFFFFFFFFull) return hipErrorNotSupported;
   if (M <= kGemvMaxRows && gemv_supported(K)) return launch_gemv(dual, A, B, nullptr, out, M, N, K, st);
+  if (M >= 64 && M <= 128 && split_ws && (dual || (N <= 4096 && K <= 4096))) {
+    // One row tile of 64..128 rows (batched decode): 128 x 64 tiles on 8 waves (two per SIMD, 32 x 32
+    // each), a 3-stage ring. gate/up runs unsplit with the SwiGLU epilogue in the tile (no partials,
+    // no reduce launch); the smaller plain products split K until the grid would pass 256
+    // workgroups. At 128 rows of the ~4B projections, timed after a 1 GB read that empties the
+    // memory-side cache, against the 128 x 128 four-wave split-K tiles: gate/up 33.2 vs 34.1 us
+    // (with its reduce), o 16.0 vs 17.5 (4 partial slices instead of 8); qkv (22.4 vs 21.2), down
+    // (26.2 vs 23.7) and the LM head (228 vs 185) stay on the other tiles.
+    if (dual) {
+      const int nt = (F + 31) / 32;
+      DORY_LAUNCH((k_gemm_tile<128, 64, 4, 2, true, 3>), dim3(nt), dim3(512), 0, st, (const bf16_t*)A,
+                  (const bf16_t*)B, out, M, N, K, F, 1, nt, K);
+      return hipGetLastError();
+    }
+    const int nt = (N + 63) / 64;
+    int S = 1;
+    while (nt * 2 * S <= 256 && (K / MF_BK) % (2 * S) == 0 && (size_t)(2 * S) * M * N * sizeof(float) <= split_ws_bytes)
+      S *= 2;
+    if (S == 1) {
+      DORY_LAUNCH((k_gemm_tile<128, 64, 4, 2, false, 3>), dim3(nt), dim3(512), 0, st, (const bf16_t*)A,
+                  (const bf16_t*)B, out, M, N, K, 0, 1, nt, K);
+      return hipGetLastError();
+    }
+    DORY_LAUNCH((k_gemm_tile<128, 64, 4, 2, false, 3>), dim3(nt, S), dim3(512), 0, st, (const bf16_t*)A,
+                (const bf16_t*)B, (void*)split_ws, M, N, K, 0, 1, nt, K / S);
+    if (parts) {
+      *parts = S;
+      return hipGetLastError();
+    }
+    const size_t outs = (size_t)M * N;
+    DORY_LAUNCH(k_splitk_reduce<false>, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st,
+                (const float*)split_ws, S, M, N, out);
+    return hipGetLastError();
+  }
   if (M <= 256 && split_ws) {
     const int S = choose_split(M, N, K, split_ws_bytes);
     if (S > 1) {
