@@ -604,6 +604,46 @@ def bench_long(m1, shape, args):
     mb.close()
     del mb
     torch.cuda.empty_cache()
+    out["context_262144_k1"] = bench_256k(m1, shape)
+    return out
+
+
+def bench_256k(m1, shape):
+    """The longest context the pages give (256K): a 262112-token prompt prefilled as one chunk at
+    k = 1 (the down projection's activation operand then passes 4 GiB and runs in row blocks),
+    then 16 decode steps at batch 1 from that context."""
+    import torch
+
+    from looped_ngpt_language_amd import dory, synth
+    T, n_dec = 262144 - 32, 16
+    mc = dory.Model(shape, None, kv_mode="last_loop", max_loops=1, max_seqs=1, max_model_len=262144, max_tokens=T,
+                    device="cuda:0", share_weights_from=m1, swa_recycle=True)
+    mc.set_loops(1)
+    st = mc.stream
+    prompt = torch.from_numpy(synth.prompt_tokens(shape, T, seed=1)).to("cuda:0")
+    e0, e1 = ev(), ev()
+    e0.record(st)
+    _, ids = mc.prefill(0, prompt, 1)
+    e1.record(st)
+    torch.cuda.synchronize()
+    pf_ms = e0.elapsed_time(e1)
+    cur = ids.clone()
+    nxt = [torch.empty(1, dtype=torch.int32, device="cuda:0") for _ in range(2)]
+    e0.record(st)
+    for i in range(n_dec):
+        mc.decode([0], cur, logits=None, out_ids=nxt[i % 2])
+        cur = nxt[i % 2]
+    e1.record(st)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / n_dec
+    out = {"prompt_tokens": T, "loops": 1, "prefill_s": round(pf_ms / 1e3, 3),
+           "prefill_tok_s": round(T / (pf_ms * 1e-3), 1), "decode_tok_s": round(1e3 / dec_ms, 2),
+           "kv_in_use_GB": round(mc.kv_bytes_in_use() / 1e9, 3)}
+    log(f"[bench] 256K context, k=1: one-chunk prefill of {T} tokens {pf_ms / 1e3:.2f} s, decode "
+        f"{1e3 / dec_ms:.1f} tok/s")
+    mc.close()
+    del mc
+    torch.cuda.empty_cache()
     return out
 
 

@@ -8,6 +8,8 @@
 //    and columns, LDS double-buffered, optional split-K; for the bf16 model at
 //    M > 2 (M <= 2 goes to the weight-streaming GEMV of k_gemv.hip).
 //  - k_gemm_f32: plain FMA tiles for the fp32 model.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -385,8 +387,23 @@ hipError_t launch_gemm(int dtype, bool dual, const void* A, const void* B, void*
     return hipGetLastError();
   }
   if (K % MF_BK != 0) return hipErrorNotSupported;
-  // 32-bit byte offsets inside the tile kernels
-  if ((size_t)M * K * 2 > 0xFFFFFFFFull || (size_t)N * K * 2 > 0xFFFFFFFFull) return hipErrorNotSupported;
+  // 32-bit byte offsets inside the tile kernels: a weight matrix must stay below 4 GiB; an
+  // activation operand that does not (a 262144-token chunk at K = 8192) goes in row blocks
+  if ((size_t)N * K * 2 > 0xFFFFFFFFull) return hipErrorNotSupported;
+  if ((size_t)M * K * 2 > 0xFFFFFFFFull) {
+    const int cap = (int)((0xFFFFFFFFull / ((size_t)K * 2)) / 256 * 256);
+    const int nblk = (M + cap - 1) / cap;
+    const int mb = ((M + nblk - 1) / nblk + 255) / 256 * 256;  // balanced row blocks
+    const size_t ocols = dual ? (size_t)F : (size_t)N;
+    const size_t oes = dual ? 2 : 4;  // bf16 z or fp32 out
+    for (int m0 = 0; m0 < M; m0 += mb) {
+      hipError_t e = launch_gemm(dtype, dual, static_cast<const bf16_t*>(A) + (size_t)m0 * K, B,
+                                 static_cast<char*>(out) + (size_t)m0 * ocols * oes, std::min(mb, M - m0), N, K,
+                                 split_ws, split_ws_bytes, st, nullptr);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (M <= kGemvMaxRows && gemv_supported(K)) return launch_gemv(dual, A, B, nullptr, out, M, N, K, st);
   if (M >= 64 && M <= 128 && split_ws && (dual || (N <= 4096 && K <= 4096))) {
     // One row tile of 64..128 rows (batched decode): 128 x 64 tiles on 8 waves (two per SIMD, 32 x 32

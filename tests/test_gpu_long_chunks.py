@@ -1,4 +1,4 @@
-"""Long prompts in one chunk: properties that hold at any size, at 32768 and 131072 tokens.
+"""Long prompts in one chunk: properties that hold at any size, at 32768, 131072 and 262144 tokens.
 
 Under the chunk semantics (a call's keys/values are written before its queries read them, in
 every block application), per-loop results do not depend on how a prompt is split into chunks,
@@ -9,7 +9,9 @@ values at these lengths, so the GPU is checked against these identities:
   * narrow bf16 model (128-wide heads, 3 query heads per KV head), 32768 tokens, k = 2:
     last-loop in one chunk == per-loop in one chunk == per-loop in 8192-token chunks;
   * the ~4B model, 131072 tokens, k = 4 (the long-context workload): last-loop in one chunk ==
-    per-loop in 8192-token chunks, on the last row's logits and final hidden state.
+    per-loop in 8192-token chunks, on the last row's logits and final hidden state;
+  * the ~4B model, 262144 tokens (the longest context the pages give), k = 1: one chunk == two
+    131072-token chunks.
 
 The GEMM tiles, split-K choices and flash row blocks differ between one chunk and several, so
 the results agree to bf16 rounding noise, not bitwise: 1e-3 on logits, 1e-3 on hidden rows.
@@ -87,3 +89,29 @@ def test_4b_131072_one_chunk_last_loop_equals_per_loop_chunks():
     compare("last-loop one chunk vs per-loop 8192-token chunks", one, chunked)
     m2.close()
     m1.close()
+
+
+def test_4b_262144_one_chunk_equals_two_chunks():
+    """The pages' longest context (256K = 262144 tokens) prefilled as one chunk, k = 1: the down
+    projection's activation operand (262144 x 8192 bf16) passes 4 GiB, so its GEMM runs in row
+    blocks. At k = 1 the result does not depend on the chunking (the last-loop cache is the
+    per-loop one), so the one-chunk last row equals that of two 131072-token chunks."""
+    T, k = 262144, 1
+    say(f"[4B] {T}-token prompt, k={k}: one chunk vs two {T // 2}-token chunks")
+    w = synth.make_weights(synth.DORY4B, seed=0)
+    prompt = torch.from_numpy(synth.prompt_tokens(synth.DORY4B, T, seed=1)).to("cuda:0")
+    m1 = dory.Model(synth.DORY4B, w, kv_mode="last_loop", max_loops=k, max_seqs=1, max_model_len=T,
+                    max_tokens=T)
+    del w
+    m1.set_loops(k)
+    one = prefill_chunks(m1, prompt, T)
+    say("  one-chunk prefill done")
+    m1.close()
+    m1.pool = m1.ws = None          # the weights stay, shared with the second context
+    torch.cuda.empty_cache()
+    m2 = dory.Model(synth.DORY4B, None, kv_mode="last_loop", max_loops=k, max_seqs=1, max_model_len=T,
+                    max_tokens=T // 2, share_weights_from=m1)
+    m2.set_loops(k)
+    chunked = prefill_chunks(m2, prompt, T // 2)
+    compare("one chunk vs two chunks", one, chunked)
+    m2.close()
