@@ -691,7 +691,8 @@ def cpu_baseline(shape, w, prompt, k, budget_s=12.0):
     that context in the oracle (a ~30 TFLOP fp64 prefill) does not fit the sample's budget, and
     a decode step's cost is dominated by the weights it reads (the context's keys add ~5% at
     2560 tokens), so the sample decodes after a 16-token prompt. Also the tiny fp32 model's
-    64-token prefill + 16 decode steps on all threads and on one thread."""
+    64-token prefill + 16 decode steps and the mid model's 64-token prefill + ~3 s of decode
+    steps (k = 2), each on all threads and on one thread."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from looped_ngpt_language_amd import synth
@@ -726,9 +727,29 @@ def cpu_baseline(shape, w, prompt, k, budget_s=12.0):
                 tk = int(ids[0])
             t2 = time.perf_counter()
         tiny[label] = {"prefill_tok_s": round(64 / (t1 - t0), 1), "decode_tok_s": round(16 / (t2 - t1), 1)}
+    # the mid-size model (cfg 1 shapes): a 64-token prompt, then decode steps for ~3 s, on all
+    # threads and on one thread
+    mid = {}
+    mw = synth.make_weights(synth.MID, seed=0)
+    mp = synth.prompt_tokens(synth.MID, 64)
+    for label, lim in (("all_threads", None), ("one_thread", 1)):
+        with threadpool_limits(limits=lim):
+            mo = OracleModel(synth.MID, mw, "last_loop", 2)
+            t0 = time.perf_counter()
+            _, ids = mo.prefill(0, mp, 1)
+            t1 = time.perf_counter()
+            tk, nd = int(ids[0]), 0
+            while nd < 2 or (time.perf_counter() - t1 < 3.0 and nd < 64):
+                _, ids = mo.decode([0], [tk])
+                tk = int(ids[0])
+                nd += 1
+            t2 = time.perf_counter()
+        mid[label] = {"prefill_tok_s": round(64 / (t1 - t0), 2), "decode_tok_s": round(nd / (t2 - t1), 2),
+                      "decode_steps": nd}
+    log(f"[bench] oracle mid model k=2: {mid}")
     return {"value": round(n / dt, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0)),
-            "prefill_tok_s": round(16 / t_pf, 3), "tiny_fp32_k2": tiny,
+            "prefill_tok_s": round(16 / t_pf, 3), "tiny_fp32_k2": tiny, "mid_bf16_k2_64_token_prompt": mid,
             "sample": f"{n} decode steps ({dt:.1f} s) at batch 1, k={k}, last-loop KV, after a 16-token prompt "
                       f"(fp64 numpy oracle, same ~4B weights; the GPU figure is at a 2560-token context); "
                       f"cores = BLAS threads used"}
