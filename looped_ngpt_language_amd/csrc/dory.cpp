@@ -531,7 +531,9 @@ void run_block(dory_ctx* c, int j, int t, int M, Flow& f, bool decode, const Geo
   const double resid_bytes = Md * d * (12 + es) + 4.0 * d;
   const int keys_max = full ? geo.max_ctx : std::min(geo.max_ctx, g.window);
   const bool paged = attn_decode_supported(dt, H, Hk, dh);
-  const bool fused_decode = decode && paged;
+  // the attention kernel writes the call's keys / values itself: decode rows, and short chunks of
+  // consecutive positions that one workgroup per split holds whole
+  const bool fused_decode = paged && (decode || (c->run_seq >= 0 && M <= kDecodeMfmaRows && M <= 32 / (H / Hk)));
   const bool flash = !decode && dt == DORY_BF16 && dh == 128 && M > c->L.part_rows;
   const int splits = flash ? 1 : choose_splits(c, M, keys_max, paged);
   c->stats.max_attn_splits = std::max(c->stats.max_attn_splits, splits);

@@ -53,6 +53,18 @@ DORY_DEV int rope_row(int pos, const PageGuard& gd) {
   return pos;
 }
 
+// RoPE of the dimension pair (x1, x2) = (x[i], x[i + dh/2]) with cs = (cos, sin) of the
+// position's angle, and the reciprocal L2 norm of the rotated head (summed over the wave). The
+// operations are fused in one fixed order, so every kernel that writes a position's k^ (prefill,
+// chunk, decode) rounds it to the same bits.
+DORY_DEV void rope_pair(float x1, float x2, float2 cs, float& a0, float& a1) {
+  a0 = __builtin_fmaf(x1, cs.x, -(x2 * cs.y));
+  a1 = __builtin_fmaf(x1, cs.y, x2 * cs.x);
+}
+DORY_DEV float rope_rnorm(float a0, float a1) {
+  return rsqrtf(fmaxf(wave_sum(__builtin_fmaf(a0, a0, a1 * a1)), DORY_TINY_SS));
+}
+
 // ---------------------------------------------------------------- rotary + norm + KV write
 
 // One wave per (row, head). Heads 0..H-1 are queries: q^ = N(RoPE(q)) -> q_out.
@@ -74,10 +86,9 @@ __global__ void __launch_bounds__(64) k_rope_qk_kv(const float* __restrict__ qkv
   if (act) {
     const float x1 = src[lane], x2 = src[lane + half];
     const float2 cs = rope[(size_t)rope_row(pos, gd) * half + lane];
-    a0 = x1 * cs.x - x2 * cs.y;
-    a1 = x1 * cs.y + x2 * cs.x;
+    rope_pair(x1, x2, cs, a0, a1);
   }
-  const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+  const float r = rope_rnorm(a0, a1);
   if (hd < H) {
     if (act) {
       T* q = q_out + (size_t)m * H * dh + (size_t)hd * dh;
@@ -136,8 +147,9 @@ __global__ void __launch_bounds__(1024) k_rope_page(const float* __restrict__ qk
     const float* x = src + (size_t)head * DH;
     const float x1 = x[lane], x2 = x[lane + 64];
     const float2 cs = rope[(size_t)rope_row(pos, gd) * 64 + lane];
-    const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
-    const float rn = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    float a0, a1;
+    rope_pair(x1, x2, cs, a0, a1);
+    const float rn = rope_rnorm(a0, a1);
     if (hu < G) {
       bf16_t* q = q_out + ((size_t)r * H + head) * DH;
       q[lane] = f32_to_bf16(a0 * rn);
@@ -360,10 +372,11 @@ DORY_DEV float bf16r(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 // workgroup (run.x >= 0: a short prefill chunk, a speculative verify), which then read each key
 // once for all their queries, column r * G + gi masking keys past its own row's position.
 // Each wave takes 32-key blocks round-robin with the next block's operands in flight. With
-// write_kv (decode, C = G) the split holding the row's own position first writes that
-// position's k^ and v (every row is the newest token of its sequence; splits never share a
-// page). With splits > 1 each workgroup stores a partial (max, sum, unnormalised output) per
-// column and k_attn_merge combines them.
+// write_kv the splits holding the rows' own positions first write those positions' k^ and v:
+// each decode row is the newest token of its sequence, and a chunk written this way has all its
+// rows in one workgroup (M <= 32 / G), so every key a workgroup reads that the call writes was
+// written by that workgroup (splits never share a page). With splits > 1 each workgroup stores
+// a partial (max, sum, unnormalised output) per column and k_attn_merge combines them.
 template <int G, int C>
 __global__ void __launch_bounds__(256) k_attn_decode(
     const float* __restrict__ qkv, const int32_t* __restrict__ rows, const int32_t* __restrict__ ptab, int max_pages,
@@ -395,7 +408,9 @@ __global__ void __launch_bounds__(256) k_attn_decode(
   const int sp_first = pf + sp * pps;
   const int sp_last = min(pl, sp_first + pps - 1);
   const size_t vbase = (size_t)Hkv * 16 * DH + (size_t)g * DH * 16;
-  const bool writer = C == G && write_kv && sp_first <= pl && pl <= sp_last;
+  // with write_kv, the splits holding the rows' own positions write those positions' k^ and v first
+  // (one decode row, or the consecutive positions of a short chunk; splits never share a page)
+  const bool writer = write_kv && sp_first <= pl && (pos_first >> 4) <= sp_last;
   const int npair = sp_last >= sp_first ? (sp_last - sp_first + 2) / 2 : 0;
   const int nw = npair > wv ? (npair - wv + 3) / 4 : 0;  // blocks of this wave: pairs wv, wv+4, ...
   bf16x8_t kA[8], vA[8], kB[8], vB[8];
@@ -421,30 +436,36 @@ __global__ void __launch_bounds__(256) k_attn_decode(
     const float2 cs = rope[(size_t)rope_row(pos_first + r, gd) * 64 + lane];
     const float* x = qkv + (size_t)(m0 + r) * (size_t)((H + 2 * Hkv) * DH) + (size_t)(g * G + gi) * DH;
     const float x1 = x[lane], x2 = x[lane + 64];
-    const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
-    const float rn = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    float a0, a1;
+    rope_pair(x1, x2, cs, a0, a1);
+    const float rn = rope_rnorm(a0, a1);
     qs[col][lane] = f32_to_bf16(a0 * rn);
     qs[col][lane + 64] = f32_to_bf16(a1 * rn);
   }
-  // the split holding the row's own position writes its key/value first
-  if (writer && wv < 2) {
-    const float* src = qkv + (size_t)m0 * (size_t)((H + 2 * Hkv) * DH);
-    const float2 cs = rope[(size_t)rope_row(pos, gd) * 64 + lane];
-    bf16_t* pg = kv_slot + (size_t)page_at(ptab, max_pages, seq, pl, gd) * page_elems;
-    const int tok = pos & 15;
-    if (wv == 0) {
-      const float* x = src + (size_t)(H + g) * DH;
-      const float x1 = x[lane], x2 = x[lane + 64];
-      const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
-      const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
-      bf16_t* kp = pg + ((size_t)g * 16 + tok) * DH;
-      kp[lane] = f32_to_bf16(a0 * r);
-      kp[lane + 64] = f32_to_bf16(a1 * r);
-    } else {
-      const float* v = src + (size_t)(H + Hkv + g) * DH;
-      bf16_t* vt = pg + vbase + vperm(tok);
-      vt[(size_t)lane * 16] = f32_to_bf16(v[lane]);
-      vt[(size_t)(lane + 64) * 16] = f32_to_bf16(v[lane + 64]);
+  // the writer splits write their rows' keys / values first: one wave per (row, key or value)
+  if (writer) {
+    for (int t = wv; t < 2 * RW; t += 4) {
+      const int r = t >> 1, p = pos_first + r, pg_i = p >> 4;
+      if (pg_i < sp_first || pg_i > sp_last) continue;  // another split's page
+      const float* src = qkv + (size_t)(m0 + r) * (size_t)((H + 2 * Hkv) * DH);
+      bf16_t* pg = kv_slot + (size_t)page_at(ptab, max_pages, seq, pg_i, gd) * page_elems;
+      const int tok = p & 15;
+      if ((t & 1) == 0) {
+        const float2 cs = rope[(size_t)rope_row(p, gd) * 64 + lane];
+        const float* x = src + (size_t)(H + g) * DH;
+        const float x1 = x[lane], x2 = x[lane + 64];
+        float a0, a1;
+        rope_pair(x1, x2, cs, a0, a1);
+        const float rn = rope_rnorm(a0, a1);
+        bf16_t* kp = pg + ((size_t)g * 16 + tok) * DH;
+        kp[lane] = f32_to_bf16(a0 * rn);
+        kp[lane + 64] = f32_to_bf16(a1 * rn);
+      } else {
+        const float* v = src + (size_t)(H + Hkv + g) * DH;
+        bf16_t* vt = pg + vbase + vperm(tok);
+        vt[(size_t)lane * 16] = f32_to_bf16(v[lane]);
+        vt[(size_t)(lane + 64) * 16] = f32_to_bf16(v[lane + 64]);
+      }
     }
   }
   __syncthreads();
@@ -595,8 +616,9 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
   for (int gi = wv; gi < G; gi += 4) {
     const float* x = src + (size_t)(g * G + gi) * DH;
     const float x1 = x[lane], x2 = x[lane + 64];
-    const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
-    const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    float a0, a1;
+    rope_pair(x1, x2, cs, a0, a1);
+    const float r = rope_rnorm(a0, a1);
     qs[gi][lane] = bf16r(a0 * r) * scale;
     qs[gi][lane + 64] = bf16r(a1 * r) * scale;
   }
@@ -610,8 +632,9 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu(
     if (wv == 0) {
       const float* x = src + (size_t)(H + g) * DH;
       const float x1 = x[lane], x2 = x[lane + 64];
-      const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
-      const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+      float a0, a1;
+      rope_pair(x1, x2, cs, a0, a1);
+      const float r = rope_rnorm(a0, a1);
       const bf16_t k0 = f32_to_bf16(a0 * r), k1 = f32_to_bf16(a1 * r);
       bf16_t* kp = pg + ((size_t)g * 16 + tok) * DH;
       kp[lane] = k0;
@@ -808,8 +831,9 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
   for (int gi = wv; gi < G; gi += 4) {
     const float* x = src + (size_t)(g * G + gi) * DH;
     const float x1 = x[lane], x2 = x[lane + 64];
-    const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
-    const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+    float a0, a1;
+    rope_pair(x1, x2, cs, a0, a1);
+    const float r = rope_rnorm(a0, a1);
     qh[gi][lane] = f32_to_bf16(a0 * r);
     qh[gi][lane + 64] = f32_to_bf16(a1 * r);
   }
@@ -823,8 +847,9 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
     if (wv == 0) {
       const float* x = src + (size_t)(H + g) * DH;
       const float x1 = x[lane], x2 = x[lane + 64];
-      const float a0 = x1 * cs.x - x2 * cs.y, a1 = x1 * cs.y + x2 * cs.x;
-      const float r = rsqrtf(fmaxf(wave_sum(a0 * a0 + a1 * a1), DORY_TINY_SS));
+      float a0, a1;
+      rope_pair(x1, x2, cs, a0, a1);
+      const float r = rope_rnorm(a0, a1);
       const bf16_t k0 = f32_to_bf16(a0 * r), k1 = f32_to_bf16(a1 * r);
       bf16_t* kp = pg + ((size_t)g * 16 + tok) * DH;
       kp[lane] = k0;
@@ -1331,9 +1356,9 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
                               const int32_t* order, int run_seq, int run_pos, const PageGuard& gd, hipStream_t st) {
   const int2 run = make_int2(M <= kDecodeMfmaRows ? run_seq : -1, run_pos);
-  // consecutive positions of one sequence whose keys are already in the cache (no key/value
-  // writes here): several rows per workgroup share every key load
-  const bool multi = run.x >= 0 && M > 1 && !write_kv;
+  // consecutive positions of one sequence (a short chunk, whose keys / values the kernel writes
+  // with write_kv): several rows per workgroup share every key load
+  const bool multi = run.x >= 0 && M > 1;
   dim3 grid(M, Hkv, splits);
 #define DORY_DEC(GV)                                                                                             \
   if (M > kDecodeMfmaRows && scale <= kFixedMaxScale)                                                          \

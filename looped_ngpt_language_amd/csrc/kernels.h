@@ -91,7 +91,9 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
                               float scale, int splits, int write_kv, void* out, float* part_ml, float* part_o,
                               const int32_t* order, int run_seq, int run_pos, const PageGuard& gd, hipStream_t st);
 // (run_seq >= 0: the M <= kDecodeMfmaRows rows are positions run_pos, run_pos + 1, ... of sequence
-// run_seq, so the kernel takes them from its arguments instead of loading the row list.)
+// run_seq, so the kernel takes them from its arguments instead of loading the row list.
+// write_kv: the kernel writes the rows' own keys / values first (decode rows; or such a chunk of
+// at most 32 / G rows, which one workgroup per split then holds whole).)
 hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
                                const PageGuard& gd, hipStream_t st);
