@@ -1010,9 +1010,9 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
 // worth of keys, so with `paired` a workgroup takes row blocks R-1-x and x (the
 // same total for every workgroup: no CU is left with two long blocks while
 // others idle); otherwise workgroup x takes row block R-1-x (longest first). Keys go through LDS in
-// blocks of 64 (4 pages), shared by the four waves and double-buffered: the
-// next block is loaded into registers while the current one is used, then
-// written to the idle buffer. Scores are computed transposed with
+// blocks of 64 (4 pages), shared by the four waves of a key group and double-buffered: the next
+// step's blocks go global -> LDS directly (no registers) into the idle buffer while the current
+// ones are used, each wave's page id read one step ahead. Scores are computed transposed with
 // v_mfma_f32_32x32x16_bf16, S^T = K . Q^T: lane l holds, for query l%32, the
 // keys 8j + 4(l/32) + i (v = 4j + i) of a 32-key half-block; its
 // probabilities for one page (j = 0,1 or 2,3) form the P^T operand of
@@ -1095,9 +1095,11 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
   const uint32_t lds_k = (uint32_t)(size_t)&Ks[0][kgu][wqu * 16 * DH];
   const uint32_t lds_v = (uint32_t)(size_t)&Vs[0][kgu][wqu * DH * 16];
   constexpr uint32_t kStageBytes = KSPLIT * PF_KB * 128 * 2;
-  auto kv_dma = [&](int step0, int st_) __attribute__((always_inline)) {
-    const int pidx = min(((step0 + kgu * KB) >> 4) + wqu, last_page);
-    const bf16_t* pg = kv_slot + (size_t)page_at(ptab, max_pages, seq, pidx, gd) * page_elems;
+  auto page_of = [&](int step0) __attribute__((always_inline)) {
+    return page_at(ptab, max_pages, seq, min(((step0 + kgu * KB) >> 4) + wqu, last_page), gd);
+  };
+  auto kv_dma = [&](int pid, int st_) __attribute__((always_inline)) {
+    const bf16_t* pg = kv_slot + (size_t)pid * page_elems;
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
       lds_dma16(pg, kofs[qt], lds_k + st_ * kStageBytes + qt * 4 * DH * 2);
@@ -1108,53 +1110,76 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
   const int klo = window > 0 ? max(0, wg_first - window + 1) : 0;
   const int wlo = window > 0 ? max(0, pos_first - window + 1) : 0;
   const int kstart = klo & ~(KB - 1);
-  kv_dma(kstart, 0);
+  kv_dma(page_of(kstart), 0);
+  int pid_next = page_of(kstart + STEP);  // the next step's page, read a step ahead
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
+  // the query operands are consumed here, before the loop: the compiler otherwise issues their
+  // loads after the barrier and waits for them inside the loop body, where (the key loads being
+  // inline assembly it does not count) those waits stall on the next step's key loads instead
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qb[ks]));
   int stage = 0;
   for (int kstep = kstart; kstep <= wg_last; kstep += STEP, stage ^= 1) {
     // the other stage was last read before the barrier that ended the previous step
-    if (kstep + STEP <= wg_last) kv_dma(kstep + STEP, stage ^ 1);
+    if (kstep + STEP <= wg_last) {
+      kv_dma(pid_next, stage ^ 1);
+      pid_next = page_of(kstep + 2 * STEP);
+    }
     const int kb = kstep + kg * KB;              // this key group's 64-key block
-    // every key of the block visible to every query of the wave (fixed offset only)
-    const bool whole = FIXED && nrow > 0 && kb + KB - 1 <= pos_first && (window <= 0 || kb > pos_last - window);
-    if (whole) {
-      // both 32-key halves in one straight run, so the second half's score MFMAs can overlap
-      // the first half's exponentials and the first half's P.V MFMAs the second's
-      const bf16_t* ks_ = Ks[stage][kg];
-      const bf16_t* vs_ = Vs[stage][kg];
-      f32x16_t st0, st1;
+    if constexpr (FIXED) {
+      // one code path for every block the wave sees: both 32-key halves' scores, the masked
+      // scores of an edge half set to -inf (exp2 -> 0), then exponentials and P.V, so the
+      // accumulators have a single update site in the loop (no register copies between paths)
+      if (nrow > 0 && kb <= pos_last && kb + KB > wlo) {
+        const bf16_t* ks_ = Ks[stage][kg];
+        const bf16_t* vs_ = Vs[stage][kg];
+        f32x16_t st2[2];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) st0[v] = st1[v] = 0.f;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        st0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(ks_ + koff[ks]), qb[ks],
-                                                      st0, 0, 0, 0);
-      }
+          for (int v = 0; v < 16; ++v) st2[t][v] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        st1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8_t*>(ks_ + 32 * DH + koff[ks]), qb[ks], st1, 0, 0, 0);
-      }
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x8_t pb[2];
+          for (int ks = 0; ks < 8; ++ks)
+            st2[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *reinterpret_cast<const bf16x8_t*>(ks_ + 32 * t * DH + koff[ks]), qb[ks], st2[t], 0, 0, 0);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f((t ? st1[v] : st0[v]) * k2 - k2);
-          lrun += p;
-          pb[v >> 3][v & 7] = (__bf16)p;
+        for (int t = 0; t < 2; ++t) {
+          const int k0 = kb + 32 * t;
+          // keys of this half-block that some query of the wave must not see (wave-uniform)
+          const bool edge = k0 + 31 > pos_first || (window > 0 && k0 <= pos_last - window);
+          if (edge) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int kp = k0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+              const bool ok = kp <= qpos && (window <= 0 || kp > qpos - window);
+              st2[t][v] = ok ? st2[t][v] : -INFINITY;
+            }
+          }
         }
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+        for (int t = 0; t < 2; ++t) {
+          bf16x8_t pb[2];
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const bf16x8_t va =
-                *reinterpret_cast<const bf16x8_t*>(vs_ + ((2 * t + pp) * DH + dt * 32) * 16 + voff);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[pp], acc[dt], 0, 0, 0);
+          for (int v = 0; v < 16; ++v) {
+            const float p = __builtin_amdgcn_exp2f(st2[t][v] * k2 - k2);
+            lrun += p;
+            pb[v >> 3][v & 7] = (__bf16)p;
           }
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const bf16x8_t va =
+                  *reinterpret_cast<const bf16x8_t*>(vs_ + ((2 * t + pp) * DH + dt * 32) * 16 + voff);
+              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[pp], acc[dt], 0, 0, 0);
+            }
+        }
       }
     } else if (nrow > 0 && kb <= pos_last && kb + KB > wlo) {
+      // running maximum: each visible 32-key half rescales the row sums and accumulators
       const bf16_t* ks_ = Ks[stage][kg];
       const bf16_t* vs_ = Vs[stage][kg];
 #pragma unroll
@@ -1173,50 +1198,33 @@ DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __rest
         // keys of this half-block that some query of the wave must not see (wave-uniform)
         const bool edge = k0 + 31 > pos_first || (window > 0 && k0 <= pos_last - window);
         bf16x8_t pb[2];
-        if (FIXED && !edge) {
-          // every score is visible: no mask, and the row sums stay lane-local until the end
+        float sv[16];
+        float mb = -INFINITY;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float p = __builtin_amdgcn_exp2f(st[v] * k2 - k2);
-            lrun += p;
-            pb[v >> 3][v & 7] = (__bf16)p;
-          }
-        } else {
-          float sv[16];
-          float mb = -INFINITY;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int kp = k0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            const bool ok = !edge || (kp <= qpos && (window <= 0 || kp > qpos - window));
-            sv[v] = ok ? st[v] : -INFINITY;
-            if (!FIXED) mb = fmaxf(mb, sv[v]);
-          }
-          float c = 1.f;
-          if (!FIXED) {
-            mb = fmaxf(mb * scale, __shfl_xor(mb * scale, 32, 64));
-            const float mn = fmaxf(mrun, mb);
-            c = safe_scale(mrun, mn);
-            mrun = mn;
-          }
-          const float off = mrun * LOG2E;
-          float psum = 0.f;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float p = sv[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] * k2 - off);
-            psum += p;
-            pb[v >> 3][v & 7] = (__bf16)p;
-          }
-          if (FIXED) {
-            lrun += psum;
-          } else {
-            psum += __shfl_xor(psum, 32, 64);
-            lrun = lrun * c + psum;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) acc[dt][v] *= c;
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int kp = k0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          const bool ok = !edge || (kp <= qpos && (window <= 0 || kp > qpos - window));
+          sv[v] = ok ? st[v] : -INFINITY;
+          mb = fmaxf(mb, sv[v]);
         }
+        mb = fmaxf(mb * scale, __shfl_xor(mb * scale, 32, 64));
+        const float mn = fmaxf(mrun, mb);
+        const float c = safe_scale(mrun, mn);
+        mrun = mn;
+        const float off = mrun * LOG2E;
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = sv[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] * k2 - off);
+          psum += p;
+          pb[v >> 3][v & 7] = (__bf16)p;
+        }
+        psum += __shfl_xor(psum, 32, 64);
+        lrun = lrun * c + psum;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[dt][v] *= c;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int page = 2 * t + pp;
