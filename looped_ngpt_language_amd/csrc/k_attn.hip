@@ -1004,12 +1004,11 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
 
 // ---------------------------------------------------------------- bf16 flash attention for prefill, d_h = 128
 
-// grid (row-block slots, H), 256 threads; a workgroup handles 128-query row
-// blocks of head blockIdx.y (one sequence: a prefill chunk), wave w owning
-// queries 32w .. +32 of the block. Causal row block i reads i + 1 key ranges'
-// worth of keys, so with `paired` a workgroup takes row blocks R-1-x and x (the
-// same total for every workgroup: no CU is left with two long blocks while
-// others idle); otherwise workgroup x takes row block R-1-x (longest first). Keys go through LDS in
+// grid (H, R) for R 128-query row blocks of one sequence (a prefill chunk); workgroup (h, y)
+// handles row block R-1-y of head h, wave w owning queries 32w .. +32 of the block. Causal row
+// block i reads i + 1 key ranges' worth of keys: with the head fastest in the dispatch order, the
+// whole grid runs longest first (every head's last row block, then every head's second last, ...),
+// so the short blocks dispatched last fill the CUs that the long ones left free. Keys go through LDS in
 // blocks of 64 (4 pages), shared by the four waves of a key group and double-buffered: the next
 // step's blocks go global -> LDS directly (no registers) into the idle buffer while the current
 // ones are used, each wave's page id read one step ahead. Scores are computed transposed with
@@ -1041,13 +1040,13 @@ template <bool FIXED, int KSPLIT>
 DORY_DEV void attn_row_block(const bf16_t* __restrict__ q, const int32_t* __restrict__ rows,
                              const int32_t* __restrict__ ptab, int max_pages, const bf16_t* __restrict__ kv_slot,
                              size_t page_elems, int M, int H, int Hkv, int window, float scale,
-                             bf16_t* __restrict__ out, int wrow0, bf16_t (*Ks)[KSPLIT][PF_KB * 128],
+                             bf16_t* __restrict__ out, int wrow0, int hq, bf16_t (*Ks)[KSPLIT][PF_KB * 128],
                              bf16_t (*Vs)[KSPLIT][PF_KB * 128], const PageGuard& gd) {
   constexpr int DH = 128, KB = PF_KB, STEP = KB * KSPLIT;
   constexpr float LOG2E = 1.4426950408889634f;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wq = wv & 3, kg = wv >> 2;             // query group, key group (wave-uniform)
-  const int hq = blockIdx.y, g = hq / (H / Hkv);
+  const int g = hq / (H / Hkv);
   const int row0 = wrow0 + wq * 32;
   const int nrow = max(0, min(32, M - row0));
   const int seq = rows[0];
@@ -1286,19 +1285,13 @@ __global__ void __launch_bounds__(256 * KSPLIT) k_attn_prefill(const bf16_t* __r
                                                                const int32_t* __restrict__ ptab, int max_pages,
                                                                const bf16_t* __restrict__ kv_slot, size_t page_elems,
                                                                int M, int H, int Hkv, int window, float scale,
-                                                               bf16_t* __restrict__ out, int paired,
+                                                               bf16_t* __restrict__ out,
                                                                const PageGuard gd) {
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][KSPLIT][PF_KB * 128];
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[2][KSPLIT][PF_KB * 128];
   const int nrb = (M + 127) / 128;
-  const int hi = nrb - 1 - (int)blockIdx.x, lo = (int)blockIdx.x;
   attn_row_block<FIXED, KSPLIT>(q, rows, ptab, max_pages, kv_slot, page_elems, M, H, Hkv, window, scale, out,
-                                hi * 128, Ks, Vs, gd);
-  if (paired && lo < hi) {
-    __syncthreads();  // the first block's merge read the LDS
-    attn_row_block<FIXED, KSPLIT>(q, rows, ptab, max_pages, kv_slot, page_elems, M, H, Hkv, window, scale, out,
-                                  lo * 128, Ks, Vs, gd);
-  }
+                                (nrb - 1 - (int)blockIdx.y) * 128, (int)blockIdx.x, Ks, Vs, gd);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1401,16 +1394,14 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* rows, const int32
 hipError_t launch_attn_prefill(const void* q, const int32_t* rows, const int32_t* ptab, int max_pages, const void* kv,
                                size_t page_elems, int M, int H, int Hkv, int window, float scale, void* out,
                                const PageGuard& gd, hipStream_t st) {
-  // pair row blocks when that still leaves at least 128 workgroups
   const int nrb = (M + 127) / 128;
-  const int paired = ((nrb + 1) / 2) * H >= 128 ? 1 : 0;
-  dim3 grid(paired ? (nrb + 1) / 2 : nrb, H);
+  const dim3 grid(H, nrb);  // head fastest: longest row blocks first over the whole grid
   if (scale <= kFixedMaxScale)
     DORY_LAUNCH((k_attn_prefill<true, 2>), grid, dim3(512), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
-                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, paired, gd);
+                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, gd);
   else
     DORY_LAUNCH((k_attn_prefill<false, 1>), grid, dim3(256), 0, st, (const bf16_t*)q, rows, ptab, max_pages,
-                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, paired, gd);
+                (const bf16_t*)kv, page_elems, M, H, Hkv, window, scale, (bf16_t*)out, gd);
   return hipGetLastError();
 }
 
