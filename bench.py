@@ -610,8 +610,10 @@ def bench_long(m1, shape, args):
 
 def bench_256k(m1, shape):
     """The longest context the pages give (256K): a 262112-token prompt prefilled as one chunk at
-    k = 1 (the down projection's activation operand then passes 4 GiB and runs in row blocks),
-    then 16 decode steps at batch 1 from that context."""
+    k = 1, then 16 decode steps at batch 1 from that context (32 positions are left for them
+    within the 262144-position limit; the down projection's activation operand, 262112 x 8192
+    bf16, stays just under 4 GiB here, so the row-blocked GEMM path is taken only by a
+    262144-token chunk)."""
     import torch
 
     from looped_ngpt_language_amd import dory, synth
