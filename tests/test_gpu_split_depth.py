@@ -165,3 +165,20 @@ def test_batched_decode_20_ragged_rows_deep_splits(narrow):
     for s in range(n_seq):
         del om.seqs[100 + s]
     m.close()
+
+
+def test_6000_token_prefill_all_rows(narrow):
+    """The whole 6000-token prompt prefilled as one chunk on the GPU, every row's final hidden
+    state and logits against the oracle's whole-prompt prefill (the module's fixture): 47 row
+    blocks of the flash prefill kernel on three query heads per KV head (the last block ragged,
+    112 rows), causal and 1000-token-window edges inside pages, k = 2 last-loop."""
+    w, prompt, om, hidden = narrow
+    m = dory.Model(NARROW3, w, kv_mode="last_loop", max_loops=K, max_seqs=1, max_model_len=LONG + 16,
+                   max_tokens=LONG)
+    m.set_loops(K)
+    say(f"[narrow3 bf16] {LONG}-token prefill in one chunk, all rows against the oracle")
+    lg, ids = m.prefill(0, torch.from_numpy(prompt).to(m.device), LONG)
+    g_h = m.last_hidden(LONG).cpu().numpy()
+    o_lg, o_ids = om.lm_head(hidden)
+    check_rows(f"{LONG} rows", lg.cpu().numpy(), ids.cpu().numpy(), o_lg, o_ids, g_h, hidden)
+    m.close()
