@@ -182,3 +182,32 @@ def test_6000_token_prefill_all_rows(narrow):
     o_lg, o_ids = om.lm_head(hidden)
     check_rows(f"{LONG} rows", lg.cpu().numpy(), ids.cpu().numpy(), o_lg, o_ids, g_h, hidden)
     m.close()
+
+
+def test_16384_token_prefill_and_decode():
+    """16384 positions in one chunk (128 flash row blocks per head; RoPE phases and
+    full-attention keys out to 16K): every row's final hidden state and the last 256 rows' logits
+    against the oracle's whole-prompt prefill, then 2 teacher-forced decode steps at that context
+    on the split MFMA kernel (32 splits, both merge groups), k = 2, last-loop."""
+    T = 16384
+    w = synth.make_weights(NARROW3, seed=0)
+    prompt = synth.prompt_tokens(NARROW3, T, seed=5)
+    say(f"[narrow3 bf16] oracle: {T}-token prefill, k={K}, last-loop")
+    om = OracleModel(NARROW3, w, "last_loop", K)
+    o_lg, o_ids = om.prefill(0, prompt, 256)
+    o_h = om.last_hidden.copy()
+    m = dory.Model(NARROW3, w, kv_mode="last_loop", max_loops=K, max_seqs=1, max_model_len=T + 16, max_tokens=T)
+    m.set_loops(K)
+    lg, ids = m.prefill(0, torch.from_numpy(prompt).to(m.device), 256)
+    g_h = m.last_hidden(T).cpu().numpy()
+    check_rows(f"{T}-token prefill (hidden: all rows; logits: last 256)", lg.cpu().numpy(), ids.cpu().numpy(),
+               o_lg, o_ids, g_h, o_h)
+    tok = int(o_ids[-1])
+    for step in range(2):
+        l1, i1 = m.decode([0], torch.tensor([tok], dtype=torch.int32, device=m.device))
+        ol, oi = om.decode([0], [tok])
+        check_rows(f"decode step {step} at {T + step + 1} keys", l1.cpu().numpy(), i1.cpu().numpy(), np.array(ol),
+                   np.array(oi), m.last_hidden(1).cpu().numpy(), om.last_hidden)
+        tok = int(oi[0])
+    assert m.stats()["max_attn_splits"] == 32
+    m.close()
