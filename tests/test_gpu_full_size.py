@@ -148,3 +148,43 @@ def test_4b_batched_decode_128_rows_vs_oracle(big):
         if int(ids[s]) != int(oi[0]):
             assert ol[0][int(oi[0])] - ol[0][int(ids[s])] < 2 * err
     mb.close()
+
+
+def test_4b_bench_config_2560_prompt_vs_oracle_golden(big):
+    """The benchmark's headline workload itself: the ~4B model on its seeded weights, the seeded
+    2560-token prompt prefilled in one chunk at k = 2 in last-loop mode, then two greedy decode
+    steps at 2561..2562 keys, whose split-key attention takes the benchmark's 21 splits (merge
+    groups 16 + 5). The oracle's outputs for these calls are stored, sampled, in
+    tests/golden/oracle_4b_bench_config.json (written by tests/golden/make_4b_bench_config.py,
+    which runs only the oracle): every final hidden value and, per row, the oracle's 64 largest
+    logits and every 64th vocabulary entry. Bars: bf16 (logits 5e-2, hidden rows 3e-2 max-abs);
+    ids equal, or the GPU's id among the sampled top entries within twice the row's error of
+    the oracle's maximum."""
+    import json
+    import os
+    w, m = big
+    gold = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                       "oracle_4b_bench_config.json")))
+    m.set_loops(2)
+    prompt = synth.prompt_tokens(synth.DORY4B, gold["prompt_tokens"])
+    say("[4B] benchmark workload: 2560-token prompt, k=2 last-loop, 2 decode steps vs the stored oracle outputs")
+    rows = gold["rows"]
+    lg, ids = m.prefill(0, prompt, 1)
+    outs = [(lg[0].cpu().numpy(), int(ids[0].item()), m.last_hidden(1)[0].cpu().numpy())]
+    for r in rows[:-1]:             # teacher-forced on the oracle's ids
+        l1, i1 = m.decode([0], torch.tensor([r["id"]], dtype=torch.int32, device=m.device))
+        outs.append((l1[0].cpu().numpy(), int(i1[0].item()), m.last_hidden(1)[0].cpu().numpy()))
+    for n, (r, (g_lg, g_id, g_h)) in enumerate(zip(rows, outs)):
+        idx = np.array(r["sample_idx"])
+        o_lg = np.array(r["logits"])
+        err = float(np.max(np.abs(g_lg[idx] - o_lg)))
+        err_h = float(np.max(np.abs(g_h - np.array(r["hidden"]))))
+        say(f"  row {n}: sampled logits max-abs {err:.2e}, hidden max-abs {err_h:.2e}, id {g_id} / oracle {r['id']}")
+        assert np.isfinite(g_lg).all()
+        assert err <= 5e-2 and err_h <= 3e-2
+        if g_id != r["id"]:
+            assert g_id in set(idx.tolist()), n
+            o_at = dict(zip(idx.tolist(), o_lg.tolist()))
+            assert o_at[r["id"]] - o_at[g_id] < 2 * err, n
+    assert m.stats()["max_attn_splits"] == 21
+    m.release(0)
