@@ -150,6 +150,29 @@ def test_4b_batched_decode_128_rows_vs_oracle(big):
     mb.close()
 
 
+def golden(name):
+    import json
+    import os
+    return json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)))
+
+
+def check_golden_row(tag, r, g_lg, g_id, g_h):
+    """One row against its stored oracle record: logits at the sampled entries, the whole final
+    hidden row, and the id (equal, or among the sampled top entries within twice the row's logit
+    error of the oracle's maximum)."""
+    idx = np.array(r["sample_idx"])
+    o_lg = np.array(r["logits"])
+    err = float(np.max(np.abs(g_lg[idx] - o_lg)))
+    err_h = float(np.max(np.abs(g_h - np.array(r["hidden"]))))
+    say(f"  {tag}: sampled logits max-abs {err:.2e}, hidden max-abs {err_h:.2e}, id {g_id} / oracle {r['id']}")
+    assert np.isfinite(g_lg).all()
+    assert err <= 5e-2 and err_h <= 3e-2
+    if g_id != r["id"]:
+        assert g_id in set(idx.tolist()), tag
+        o_at = dict(zip(idx.tolist(), o_lg.tolist()))
+        assert o_at[r["id"]] - o_at[g_id] < 2 * err, tag
+
+
 def test_4b_bench_config_2560_prompt_vs_oracle_golden(big):
     """The benchmark's headline workload itself: the ~4B model on its seeded weights, the seeded
     2560-token prompt prefilled in one chunk at k = 2 in last-loop mode, then two greedy decode
@@ -160,11 +183,8 @@ def test_4b_bench_config_2560_prompt_vs_oracle_golden(big):
     logits and every 64th vocabulary entry. Bars: bf16 (logits 5e-2, hidden rows 3e-2 max-abs);
     ids equal, or the GPU's id among the sampled top entries within twice the row's error of
     the oracle's maximum."""
-    import json
-    import os
     w, m = big
-    gold = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
-                                       "oracle_4b_bench_config.json")))
+    gold = golden("oracle_4b_bench_config.json")
     m.set_loops(2)
     prompt = synth.prompt_tokens(synth.DORY4B, gold["prompt_tokens"])
     say("[4B] benchmark workload: 2560-token prompt, k=2 last-loop, 2 decode steps vs the stored oracle outputs")
@@ -175,16 +195,54 @@ def test_4b_bench_config_2560_prompt_vs_oracle_golden(big):
         l1, i1 = m.decode([0], torch.tensor([r["id"]], dtype=torch.int32, device=m.device))
         outs.append((l1[0].cpu().numpy(), int(i1[0].item()), m.last_hidden(1)[0].cpu().numpy()))
     for n, (r, (g_lg, g_id, g_h)) in enumerate(zip(rows, outs)):
-        idx = np.array(r["sample_idx"])
-        o_lg = np.array(r["logits"])
-        err = float(np.max(np.abs(g_lg[idx] - o_lg)))
-        err_h = float(np.max(np.abs(g_h - np.array(r["hidden"]))))
-        say(f"  row {n}: sampled logits max-abs {err:.2e}, hidden max-abs {err_h:.2e}, id {g_id} / oracle {r['id']}")
-        assert np.isfinite(g_lg).all()
-        assert err <= 5e-2 and err_h <= 3e-2
-        if g_id != r["id"]:
-            assert g_id in set(idx.tolist()), n
-            o_at = dict(zip(idx.tolist(), o_lg.tolist()))
-            assert o_at[r["id"]] - o_at[g_id] < 2 * err, n
+        check_golden_row(f"row {n}", r, g_lg, g_id, g_h)
     assert m.stats()["max_attn_splits"] == 21
     m.release(0)
+
+
+def test_4b_batched_bench_config_vs_oracle_golden(big):
+    """The benchmark's batched-decode workload itself: 128 sequences of the ~4B model with seeded
+    prompt lengths uniform in [256, 4096] (the split-key VALU kernel, longest rows first, the
+    128-row projection tiles), k = 2, last-loop, every prompt prefilled, then two decode steps of
+    all 128 rows. Three sequences (the longest, the shortest, sequence 64) are checked against the
+    oracle outputs stored in tests/golden/oracle_4b_batched_config.json (written by
+    tests/golden/make_4b_batched_config.py, which runs only the oracle), teacher-forced on the
+    oracle's ids; the other rows decode their own greedy ids. Bars as for the bs1 workload."""
+    w, m = big
+    gold = golden("oracle_4b_batched_config.json")
+    n_seq = gold["n_seq"]
+    lens = synth.batch_prompt_lengths(n_seq, 256, 4096, seed=2)
+    prompts = synth.batch_prompts(synth.DORY4B, lens, seed=1)
+    picked = sorted(int(s) for s in gold["sequences"])
+    extra = 64
+    kv_tokens = int(sum(((int(n) + extra + 15) // 16) * 16 for n in lens))
+    mb = dory.Model(synth.DORY4B, None, kv_mode="last_loop", max_loops=2, max_seqs=n_seq,
+                    max_model_len=4096 + extra, max_tokens=4096, kv_tokens=kv_tokens, share_weights_from=m)
+    mb.set_loops(2)
+    say(f"[4B] batched workload: {n_seq} sequences ({int(sum(lens))} prompt tokens), k=2 last-loop, "
+        f"sequences {picked} vs the stored oracle outputs")
+    outs = {}
+    toks = []
+    for s, p in enumerate(prompts):
+        lg, ids = mb.prefill(s, torch.from_numpy(p).to(mb.device), 1)
+        if s in picked:
+            outs[s] = [(lg[0].cpu().numpy(), int(ids[0].item()), mb.last_hidden(1)[0].cpu().numpy())]
+        toks.append(int(ids[0].item()))
+    for step in range(2):
+        for s in picked:            # teacher-forced on the oracle's ids
+            toks[s] = gold["sequences"][str(s)]["rows"][step]["id"]
+        lg, ids = mb.decode(list(range(n_seq)), torch.tensor(toks, dtype=torch.int32, device=mb.device))
+        h = mb.last_hidden(n_seq).cpu().numpy()
+        lgn, idn = lg.cpu().numpy(), ids.cpu().numpy()
+        for s in picked:
+            outs[s].append((lgn[s], int(idn[s]), h[s]))
+        toks = [int(v) for v in idn]
+    for s in picked:
+        rows = gold["sequences"][str(s)]["rows"]
+        assert gold["sequences"][str(s)]["prompt_tokens"] == len(prompts[s])
+        for n, (r, (g_lg, g_id, g_h)) in enumerate(zip(rows, outs[s])):
+            check_golden_row(f"sequence {s} ({len(prompts[s])} tokens) row {n}", r, g_lg, g_id, g_h)
+    splits = mb.stats()["max_attn_splits"]
+    say(f"  largest split count: {splits}")
+    assert splits > 1
+    mb.close()
