@@ -38,12 +38,17 @@ def big():
     return w, m
 
 
-def test_4b_prefill_and_decode_vs_oracle(big):
-    w, m = big
-    say("[4B] k=2 last-loop: 40-token prompt + 2 decode steps vs oracle")
-    m.set_loops(2)
+@pytest.mark.parametrize("mode,k", [("last_loop", 2), ("last_loop", 4), ("per_loop", 1), ("per_loop", 4)])
+def test_4b_prefill_and_decode_vs_oracle(big, mode, k):
+    """40-token prompt (all rows' logits) and 2 greedy decode steps at the ~4B shapes, against the
+    oracle run live, for both KV modes and k = 1, 2, 4 (per-loop: 16 + 20 k cache slots)."""
+    w, m0 = big
+    say(f"[4B] k={k} {mode}: 40-token prompt + 2 decode steps vs oracle")
+    m = m0 if mode == "last_loop" else dory.Model(synth.DORY4B, None, kv_mode=mode, max_loops=k, max_seqs=1,
+                                                   max_model_len=64, max_tokens=40, share_weights_from=m0)
+    m.set_loops(k)
     prompt = synth.prompt_tokens(synth.DORY4B, 2560)
-    om = OracleModel(synth.DORY4B, w, "last_loop", 2)
+    om = OracleModel(synth.DORY4B, w, mode, k)
     olg, oids = om.prefill(0, prompt[:40], 40)
     o_h = [om.last_hidden[-1]]
     lg, ids = m.prefill(0, prompt[:40], 40)
@@ -69,6 +74,8 @@ def test_4b_prefill_and_decode_vs_oracle(big):
     assert max(errs) <= 5e-2
     assert err_h <= 3e-2
     m.release(0)
+    if m is not m0:
+        m.close()
 
 
 def test_4b_long_prefill_prefix_property(big):
