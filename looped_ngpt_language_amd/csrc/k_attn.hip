@@ -1005,7 +1005,7 @@ __global__ void __launch_bounds__(256) k_attn_decode_valu_fx(
 // ---------------------------------------------------------------- bf16 flash attention for prefill, d_h = 128
 
 // grid (H, R) for R 128-query row blocks of one sequence (a prefill chunk); workgroup (h, y)
-// handles row block R-1-y of head h, wave w owning queries 32w .. +32 of the block. Causal row
+// handles row block R-1-y of head h, wave w owning queries 32 (w % 4) .. +32 of the block. Causal row
 // block i reads i + 1 key ranges' worth of keys: with the head fastest in the dispatch order, the
 // whole grid runs longest first (every head's last row block, then every head's second last, ...),
 // so the short blocks dispatched last fill the CUs that the long ones left free. Keys go through LDS in
@@ -1032,7 +1032,7 @@ constexpr float kFixedMaxScale = 40.f;
 
 constexpr int PF_KB = 64;  // keys per LDS block of the prefill kernel
 
-// One 128-query row block of head blockIdx.y. KSPLIT = 2: the workgroup has 8
+// One 128-query row block (rows wrow0 ..) of query head hq. KSPLIT = 2: the workgroup has 8
 // waves; waves 4g .. 4g+3 (key group g) take the 64-key blocks 2s + g of each
 // 128-key step for their 32 queries each, and the two groups' partial sums are
 // merged through LDS at the end (two waves per SIMD, half the serial key loop).
