@@ -45,6 +45,105 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _clock_mhz(obj, prefix):
+    """Current clocks (MHz) of every clock domain whose name starts with `prefix` ("gfx", "mem")
+    in amd-smi's JSON clock report, whatever its nesting."""
+    vals = []
+
+    def num(v):
+        if isinstance(v, dict):
+            v = v.get("value")
+        if isinstance(v, (int, float)):
+            return float(v)
+        if isinstance(v, str):
+            try:
+                return float(v.split()[0])
+            except (ValueError, IndexError):
+                return None
+        return None
+
+    def walk(o):
+        if isinstance(o, dict):
+            for k, v in o.items():
+                if isinstance(k, str) and k.lower().startswith(prefix) and isinstance(v, dict):
+                    c = num(v.get("clk", v.get("cur_clk")))
+                    if c is not None:
+                        vals.append(c)
+                walk(v)
+        elif isinstance(o, list):
+            for v in o:
+                walk(v)
+
+    walk(obj)
+    return vals
+
+
+class ClockSampler:
+    """Reads the GPU's current graphics and memory clocks with `amd-smi metric --clock --json`
+    every few seconds from a background thread while the benchmark runs (amd-smi reads the
+    driver's metrics; it launches no GPU work). Reports the spread of the readings."""
+
+    def __init__(self, period_s=4.0):
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self.error = None
+        self.raw = None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import shutil
+        import subprocess
+        exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+        r = subprocess.run([exe, "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
+        if r.returncode != 0:
+            raise RuntimeError(f"amd-smi exit {r.returncode}: {r.stderr.strip()[-200:]}")
+        try:
+            data = json.loads(r.stdout)
+        except ValueError:  # warnings printed ahead of the JSON document
+            lines = r.stdout.splitlines()
+            first = next(i for i, ln in enumerate(lines) if ln.lstrip()[:1] in ("[", "{") and
+                         not ln.lstrip().startswith("[W") and not ln.lstrip().startswith("[I"))
+            data = json.loads("\n".join(lines[first:]))
+        gfx, mem = _clock_mhz(data, "gfx"), _clock_mhz(data, "mem")
+        if not gfx:
+            self.raw = r.stdout[:600]
+            raise RuntimeError("no gfx clock in amd-smi's report")
+        return {"t": time.time(), "gfx_mhz": float(np.mean(gfx)), "mem_mhz": float(np.mean(mem)) if mem else None}
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # a missing or changed tool must not end the benchmark
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join(timeout=40)
+        out = {"source": "amd-smi metric --clock --json", "samples": len(self.samples),
+               "period_s": self.period_s}
+        if self.samples:
+            g = [x["gfx_mhz"] for x in self.samples]
+            out.update({"gfx_mhz_min": round(min(g), 1), "gfx_mhz_median": round(float(np.median(g)), 1),
+                        "gfx_mhz_max": round(max(g), 1)})
+            mems = [x["mem_mhz"] for x in self.samples if x["mem_mhz"] is not None]
+            if mems:
+                out["mem_mhz_median"] = round(float(np.median(mems)), 1)
+        if self.error:
+            out["error"] = self.error
+        if self.raw:
+            out["raw_head"] = self.raw
+        return out
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -70,6 +169,7 @@ def parse():
     p.add_argument("--no-long", action="store_true", help="skip the 131072-token prompt at k=4 with decode and "
                    "self-speculative decoding at that context")
     p.add_argument("--no-long-chunked", action="store_true", help="skip the extra 8192-token-chunk long prefill")
+    p.add_argument("--no-clocks", action="store_true", help="do not sample the GPU clocks with amd-smi")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one device copy of 256 MiB first (counter calibration under rocprofv3)")
     return p.parse_args()
@@ -211,6 +311,7 @@ def main():
     from looped_ngpt_language_amd import dory, synth
 
     t_start = time.time()
+    clocks = ClockSampler().start() if not args.no_clocks else None
     loops = [int(x) for x in args.loops.split(",")]
     if args.calibrate_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
@@ -309,6 +410,9 @@ def main():
                      "what": "algorithmic bytes of a whole decode step (recurrent-core weights streamed k times, "
                              "KV reads and writes, LM head) over the step time"}
 
+    # the sampler stops before the host-side oracle timing, which it would disturb
+    gpu_clocks = clocks.stop() if clocks else None
+
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -351,6 +455,7 @@ def main():
         "roofline": roofline,
         "step_roofline": step_roofline,
         "cpu_baseline": cpu,
+        "gpu_clocks": gpu_clocks,
         "breakdown": bd,
     }
     print(json.dumps(out), flush=True)

@@ -192,11 +192,15 @@ def sample(logits, uniforms, temperature=1.0, top_p=0.95, stream=None, static_sc
     if ids is None:
         ids = torch.empty(rows, dtype=torch.int32, device=logits.device)
     st = stream if stream is not None else torch.cuda.current_stream(logits.device)
+    u = uniforms.contiguous()
     fn = lib().dory_sample_static if static_scratch else lib().dory_sample
-    r = fn(_ptr(logits), int(rows), int(vocab), float(temperature), float(top_p), _ptr(uniforms.contiguous()),
+    r = fn(_ptr(logits), int(rows), int(vocab), float(temperature), float(top_p), _ptr(u),
            _ptr(ids), C.c_void_p(st.cuda_stream))
     if r != DORY_OK:
         raise DoryError(r, "dory_sample rejected its arguments")
+    if st != torch.cuda.current_stream(logits.device):
+        for t in (logits, u, ids):  # allocated on the current stream, used on the sampler's
+            t.record_stream(st)
     return ids
 
 
@@ -301,6 +305,16 @@ class Model:
             t = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to(self.device)
         return t
 
+    def _hold(self, *tensors):
+        """Device tensors a call reads or writes were allocated on torch's current stream; when the
+        library runs on another stream, tell the caching allocator so their memory is not handed
+        out again before that stream's kernels are done with it."""
+        import torch
+        if self.stream != torch.cuda.current_stream(self.device):
+            for t in tensors:
+                if t is not None:
+                    t.record_stream(self.stream)
+
     def close(self):
         if getattr(self, "ctx", None):
             self._L.dory_destroy(self.ctx)
@@ -338,6 +352,7 @@ class Model:
         out_ids = torch.empty(logits_rows, dtype=torch.int32, device=self.device) if ids else None
         st = self._L.dory_prefill(self.ctx, int(seq_id), _ptr(tok), n, int(logits_rows), _ptr(logits), _ptr(out_ids))
         self._check(st, "dory_prefill")
+        self._hold(tok, logits, out_ids)
         self._keep_call = tok
         return logits, out_ids
 
@@ -355,6 +370,7 @@ class Model:
             out_ids = torch.empty(n, dtype=torch.int32, device=self.device)
         st = self._L.dory_decode(self.ctx, n, sids, _ptr(tok), _ptr(lg) if lg is not None else None, _ptr(out_ids))
         self._check(st, "dory_decode")
+        self._hold(tok, lg, out_ids)
         self._keep_call = tok
         return lg, out_ids
 
@@ -383,6 +399,7 @@ class Model:
         import torch
         out = torch.empty((rows, self.shape.d_model), dtype=torch.float32, device=self.device)
         self._check(self._L.dory_last_hidden(self.ctx, _ptr(out), int(rows)), "dory_last_hidden")
+        self._hold(out)
         return out
 
     def device_flags(self, reset=True) -> int:
