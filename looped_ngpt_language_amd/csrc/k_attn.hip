@@ -311,31 +311,51 @@ __global__ void __launch_bounds__(128) k_attn_merge(const float* __restrict__ pa
   const size_t rh = blockIdx.x;
   const int e = threadIdx.x;
   const bool own = e < dh;
+  const int lane = e & 63;
   const float* ml = part_ml + 2 * rh * splits;
   const float* po = part_o + rh * splits * dh + (own ? e : 0);
   float M = -INFINITY, L = 0.f, A = 0.f;
-  for (int s0 = 0; s0 < splits; s0 += 16) {
-    float mv[16], lv[16], ov[16];
+  // Splits in groups of 16, each folded in as: running maximum, rescale, weighted sums. All loads
+  // of 32 splits are issued together and unconditionally (one memory round trip): each wave takes
+  // the (max, sum) pairs with one coalesced load and reads them out with readlane; the partial
+  // outputs are loaded at clamped split indexes and the surplus ones dropped by select.
+  for (int s0 = 0; s0 < splits; s0 += 32) {
+    const int nml = 2 * min(32, splits - s0);
+    const float mlv = ml[2 * s0 + min(lane, nml - 1)];  // lanes past the group repeat its last word
+    float ov[32];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool ok = s0 + i < splits;
-      mv[i] = ok ? ml[2 * (s0 + i)] : -INFINITY;
-      lv[i] = ok ? ml[2 * (s0 + i) + 1] : 0.f;
-      ov[i] = ok ? po[(size_t)(s0 + i) * dh] : 0.f;
+    for (int i = 0; i < 32; ++i) ov[i] = po[(size_t)min(s0 + i, splits - 1) * dh];
+    // every value is taken here, so the compiler keeps the second group's loads ahead of the
+    // first group's arithmetic instead of moving them under that group's branch
+#pragma unroll
+    for (int i = 0; i < 32; ++i) asm volatile("" : : "v"(ov[i]));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      if (s0 + 16 * g >= splits) break;  // uniform
+      float mc = M;
+      float mv[16], lv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k = 16 * g + i;
+        const bool ok = s0 + k < splits;
+        const float m_k = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), 2 * k));
+        const float l_k = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv), 2 * k + 1));
+        mv[i] = ok ? m_k : -INFINITY;
+        lv[i] = ok ? l_k : 0.f;
+        mc = fmaxf(mc, mv[i]);
+      }
+      const float c = safe_scale(M, mc);
+      A *= c;
+      L *= c;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k = 16 * g + i;
+        const float w = safe_scale(mv[i], mc);
+        A += w * (s0 + k < splits ? ov[k] : 0.f);
+        L += w * lv[i];
+      }
+      M = mc;
     }
-    float mc = M;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mc = fmaxf(mc, mv[i]);
-    const float c = safe_scale(M, mc);
-    A *= c;
-    L *= c;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float w = safe_scale(mv[i], mc);
-      A += w * ov[i];
-      L += w * lv[i];
-    }
-    M = mc;
   }
   if (own) St<T>::st(out, rh * dh + e, L > 0.f ? A / L : 0.f);
 }
