@@ -21,7 +21,8 @@ Roofline fractions come from the library's algorithmic byte / flop accounting. T
 entry is the dominant decode kernel: its algorithmic bytes per launch over its average launch
 time, from HIP events the dispatches record on the library's stream in an instrumented pass of
 the same steps; it also carries the rocprofv3 average of the same kernel from the committed
-profile while that kernel's source is unchanged.
+profile while that kernel's source is unchanged. `gpu_clocks` holds the graphics and memory
+clocks amd-smi read every few seconds while the GPU part ran.
 """
 from __future__ import annotations
 
