@@ -330,3 +330,27 @@ def test_batched_decode_upload_fits():
     m.decode(list(range(n)), [1] * n)
     assert all(m.seq_len(q) == 16 * (1 + q % 5) + 1 for q in range(n))
     assert m.stats()["pages_in_use"] == sum(1 + q % 5 + 1 for q in range(n))
+
+
+def test_decode_step_launch_count_at_4b_shapes():
+    """Launches of one batch-1 decode step at the ~4B shapes (2560-token context, 21 key splits),
+    counted by the library in a dry run: six per block application (qkv GEMV with the pending
+    residual step in its prologue, attention, split merge, o GEMV, gate/up GEMV with the
+    residual prologue, down GEMV), so each recurrent loop adds 20 x 6 block launches plus one
+    loop-boundary launch; the rest of the step (embedding, entering the core, final step, LM head,
+    argmax) is the same at every k."""
+    counts = {}
+    for k in (1, 2, 4):
+        m = dory.Model(synth.DORY4B, kv_mode="last_loop", dry_run=True, max_model_len=2700, max_seqs=1,
+                       max_tokens=2560, max_loops=4)
+        m.set_loops(k)
+        m.prefill(0, list(range(2560)), 1)
+        before = m.stats()["kernel_launches"]
+        m.decode([0], [5])
+        st = m.stats()
+        counts[k] = st["kernel_launches"] - before
+        assert st["max_attn_splits"] == 21
+        m.close()
+    assert counts[2] - counts[1] == 20 * 6 + 1
+    assert counts[4] - counts[2] == 2 * (20 * 6 + 1)
+    assert counts[1] == 16 * 6 + 20 * 6 + 4
